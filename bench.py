@@ -1,0 +1,245 @@
+"""Benchmark: loop-query tokens/s of loop-aware attention on one MI355X.
+
+Default workload: Huginn-shaped RIPE decode (32 sequences, 4 core layers x 32
+loops, 55 heads x 96, bf16, context 1024, window 64, 16-token pages).  One step
+runs every core layer at every loop as its own attention call, loop-major, as a
+looped model's sequential loops require; it yields batch * q * loops
+loop-query tokens.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line with the throughput, the roofline of the attention kernel
+(algorithmic bytes per launch / mean launch time from HIP events recorded
+around each launch on the launch stream) and the fp64 oracle's throughput on a
+bounded sample of the same workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload huginn_ripe]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "loop-query tokens/s + achieved HBM GB/s (% of MI355X peak), looped-KV attention"
+KERNEL_SOURCES = ["verify_attention_loop_amd/csrc/decode.hip", "verify_attention_loop_amd/csrc/verify.hip",
+                  "verify_attention_loop_amd/csrc/cell.hip", "verify_attention_loop_amd/csrc/device.hpp",
+                  "verify_attention_loop_amd/csrc/params.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="huginn_ripe",
+                    choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "loopkv_cells"])
+    ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
+    ap.add_argument("--layers", type=int, default=0, help="distinct layers held in HBM (0: all)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def build_workload(w, args):
+    import harness
+    layers = list(range(w.n_layers if args.layers <= 0 else min(args.layers, w.n_layers)))
+    built = harness.build_plain(w, layers=layers)
+    return built, layers
+
+
+def cpu_baseline(w, seconds: float):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload: rows of (seq, layer 0, loop,
+    head) with their own and deepest planes regenerated on the host; the sample repeats until `seconds`
+    of oracle time accumulate.  Input generation is not timed."""
+    import numpy as np
+
+    import harness
+    import oracle
+    import synth
+
+    R = w.n_loops
+    pol = oracle.RIPE if w.policy == "ripe" else oracle.FULL
+    rng = np.random.default_rng(0)
+    n_rows = 24
+    L = w.length
+    q = np.empty((n_rows, w.head_dim))
+    ko = np.empty((n_rows, L, w.head_dim))
+    vo, kd, vd = np.empty_like(ko), np.empty_like(ko), np.empty_like(ko)
+    loops = np.empty(n_rows, dtype=np.int32)
+    for i in range(n_rows):
+        b, h, r = int(rng.integers(w.batch)), int(rng.integers(w.n_heads)), int(rng.integers(R))
+        loops[i] = r
+        ko[i] = harness.cpu_values(w, synth.T_K, b, 0, r, h, L)
+        vo[i] = harness.cpu_values(w, synth.T_V, b, 0, r, h, L)
+        if pol == oracle.RIPE and r != R - 1:
+            kd[i] = harness.cpu_values(w, synth.T_K, b, 0, R - 1, h, L)
+            vd[i] = harness.cpu_values(w, synth.T_V, b, 0, R - 1, h, L)
+        else:
+            kd[i], vd[i] = ko[i], vo[i]
+        q[i] = harness.cpu_query(w, b, 0, r, h, L - 1)
+    t = np.full(n_rows, L - 1, dtype=np.int32)
+    done, elapsed = 0, 0.0
+    while elapsed < seconds:
+        t1 = time.perf_counter()
+        oracle.attend_rows(q, ko, vo, kd, vd, t, t, loops, pol, R, w.window)
+        elapsed += time.perf_counter() - t1
+        done += n_rows
+    rows_per_s = done / elapsed
+    rows_per_token = w.n_layers * w.n_heads  # one loop-query token = every layer and head of one (seq, loop)
+    return {"value": rows_per_s / rows_per_token, "unit": "loop-query tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{done} rows ({n_rows} distinct (seq, layer 0, loop, head) rows of the {w.name} workload, "
+                      f"L={L}, d={w.head_dim}, repeated) in {elapsed:.1f} s of fp64 oracle time; "
+                      f"{rows_per_token} rows = 1 loop-query token"}
+
+
+def read_traffic(workload: str, khash: str):
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("kernel_hash") != khash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import harness
+    import synth
+    import verify_attention_loop_amd as vla
+
+    vla.load()
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    if args.workload not in ("huginn_ripe", "ouro_splitk", "huginn_verify"):
+        print(f"workload {args.workload}: not benchmarked by this script", file=sys.stderr)
+        sys.exit(2)
+    t_setup = time.perf_counter()
+    built, layers = build_workload(w, args)
+    cache = built.cache
+    R, B, q_len = w.n_loops, w.batch, w.q_len
+    mode = vla.MODE_VERIFY if q_len > 1 else vla.MODE_DECODE
+    split = w.split_k if args.split_k < 0 else args.split_k
+    n_layers_step = w.n_layers
+    # Queries and outputs of every (layer, loop) call of a step, resident in HBM.
+    qs, outs = {}, {}
+    for loop in range(R):
+        for layer in range(n_layers_step):
+            src_layer = layers[layer % len(layers)]
+            qs[(layer, loop)] = harness.gpu_queries(built, src_layer, loop, q_len)
+            outs[(layer, loop)] = torch.empty_like(qs[(layer, loop)])
+    ws_bytes = cache.lkv_workspace_bytes(0, 0, built.seqs, q_len=q_len, mode=mode, split_k=split)
+    ws = torch.empty(max(4, ws_bytes), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    calls = [(layer, loop) for loop in range(R) for layer in range(n_layers_step)]
+
+    def step(events=None):
+        for n, (layer, loop) in enumerate(calls):
+            kw = {}
+            if events is not None:
+                kw = {"ev_begin": events[2 * n].cuda_event, "ev_end": events[2 * n + 1].cuda_event}
+            cache.lkv_attend(layers[layer % len(layers)], loop, built.seqs, qs[(layer, loop)], outs[(layer, loop)],
+                             q_len=q_len, mode=mode, split_k=split, workspace=ws, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))] for _ in range(args.steps)]
+    for e in ev:
+        for x in e:
+            x.record()  # torch creates the underlying HIP event on its first record
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(args.steps):
+        step(ev[k])
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    kern_ms = np.array([[e[2 * n].elapsed_time(e[2 * n + 1]) for n in range(len(calls))] for e in ev])
+    mean_launch_ms = float(kern_ms.mean())
+    for o in outs.values():
+        assert torch.isfinite(o.float()).all(), "non-finite attention output"
+
+    tokens_per_step = B * q_len * R
+    value = tokens_per_step / (ms_per_step / 1e3)
+    alg_bytes = harness.algorithmic_bytes_per_call(w, built.lengths, q_len)
+    achieved = alg_bytes / (mean_launch_ms / 1e3) / 1e9
+    khash = kernel_hash()
+    traffic = read_traffic(args.workload, khash)
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "loop-query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == synth.DT_BF16 else "f32",
+        "data": "synthetic (seeded counter-hash generator; Huginn-shaped ripening planes)"
+        if w.mode == synth.MODE_RIPEN else "synthetic (seeded counter-hash generator)",
+        "config": {
+            "workload": w.name, "batch": B, "core_layers": w.n_layers, "loops": R, "heads": w.n_heads,
+            "head_dim": w.head_dim, "context": w.length, "q_len": q_len,
+            "policy": w.policy, "window": w.window, "page_tokens": 16, "split_k": split,
+            "calls_per_step": len(calls), "layers_resident": len(layers),
+            "kernel_ms_per_step": round(float(kern_ms.sum(axis=1).mean()), 4), "setup_s": round(setup_s, 1),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_kernel" if mode == vla.MODE_DECODE else "verify_kernel",
+            "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+            "kernel_hash": khash,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

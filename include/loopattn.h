@@ -1,0 +1,229 @@
+/*
+ * loopattn: loop-aware attention over a looped (recurrent-depth) language
+ * model's multi-plane KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * A looped model runs a block of core layers R times per token; loop r of each
+ * core layer writes its own keys and values, "plane r" ("Prefix Keys and Values
+ * Matter Late: RIPE Caching for Self-Speculative Decoding in Looped Language
+ * Models", Sec. 2).  At loop r each query token attends to its sequence's keys
+ * and values, read from the plane a cache policy names:
+ *
+ *   FULL  every position reads plane r                       (RIPE page, Sec. 2)
+ *   RIPE  plane r if t - j <= W, else the deepest plane R    (RIPE page, Eq. (9))
+ *         (W = 0 is the deepest-plane cache; positions of the query's own block
+ *          always read plane r, proof of Prop. 1)
+ *   cells LoopKV-style quantised (layer, loop) cells: INT4 or INT2 codes for the
+ *         history, or a pointer redirection to the final loop's codes; exact
+ *         sink and tail ("LoopKV: Loop-Aware KV Cache Compression for Serving
+ *         Looped Transformers", Sec. 3.1-3.4).
+ *
+ * Conventions used by every call:
+ *   - loops are 0-based: loop in [0, n_loops), deepest = n_loops - 1;
+ *   - a sequence of length L holds positions 0..L-1, including the query (or
+ *     the verify block) being attended; q_len rows sit at t0 = L - q_len .. L-1
+ *     and row t sees keys j <= t;
+ *   - the score scale is 1/sqrt(head_dim); lse outputs are natural logs;
+ *   - all device memory is caller-owned (e.g. PyTorch tensors); the library
+ *     never allocates device memory;
+ *   - `stream` arguments are hipStream_t handles (NULL = the null stream); all
+ *     device work is asynchronous on that stream; nothing synchronises;
+ *   - every call returns lkv_status; on error the handle is unchanged and stays
+ *     usable, and lkv_last_error() describes the failure;
+ *   - a handle is bound to one device and is not thread-safe.
+ */
+#ifndef LOOPATTN_H
+#define LOOPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LKV_OK = 0,
+  LKV_EINVAL = 1,       /* bad argument: shape, index, range, NULL pointer */
+  LKV_ENOMEM = 2,       /* an arena or the page pool is exhausted */
+  LKV_ESTATE = 3,       /* cache state does not allow the call (missing plane, gap, dead seq) */
+  LKV_EWINDOW = 4,      /* RIPE: a non-deepest plane written outside the window ring */
+  LKV_EDEVICE = 5,      /* a HIP call or kernel launch failed */
+  LKV_EUNSUPPORTED = 6  /* valid request that this build does not implement */
+} lkv_status;
+
+enum { LKV_DTYPE_F32 = 0, LKV_DTYPE_BF16 = 1 };
+enum { LKV_POLICY_FULL = 0, LKV_POLICY_RIPE = 1 };
+enum { LKV_MODE_DECODE = 0, LKV_MODE_VERIFY = 1, LKV_MODE_DRAFT = 2 };
+/* Cell kinds of a quantised cache (LoopKV page, Sec. 3.1-3.2).  BF16 is reserved. */
+enum { LKV_CELL_BF16 = 0, LKV_CELL_INT4 = 1, LKV_CELL_INT2 = 2, LKV_CELL_SHARED = 3 };
+
+/* Tokens per plain page and per code page. */
+#define LKV_PAGE_TOKENS 16
+#define LKV_CODE_PAGE_TOKENS 32
+
+typedef struct {
+  int32_t n_layers;     /* core (looped) layers */
+  int32_t n_loops;      /* R */
+  int32_t n_heads_q;    /* query heads */
+  int32_t n_heads_kv;   /* KV heads; n_heads_q % n_heads_kv == 0 */
+  int32_t head_dim;     /* 64, 96 or 128 */
+  int32_t page_size;    /* tokens per plain page: must be LKV_PAGE_TOKENS */
+  int32_t kv_dtype;     /* LKV_DTYPE_F32 or LKV_DTYPE_BF16 (also the q / out dtype) */
+  int32_t policy;       /* LKV_POLICY_FULL or LKV_POLICY_RIPE */
+  int32_t window;       /* RIPE window W >= 0 */
+  int32_t max_seqs;     /* sequence slots */
+  int32_t max_len;      /* longest sequence, positions */
+  int32_t max_block;    /* longest verify block (q_len), 1..16 */
+  int32_t quant;        /* 0: plain planes; 1: LoopKV-style cells (bf16, FULL) */
+  int32_t sink;         /* quant: exact sink positions [0, sink) */
+  int32_t tail;         /* quant: exact tail positions [L - tail, L) */
+  int32_t poison;       /* 1: fill pages with NaN when handed out (debug) */
+  uint64_t shuffle_seed;/* 0: free pages handed out in address order; else a seeded permutation */
+} lkv_config;
+
+/* Caller-owned device arenas.  Sizes come from lkv_sizes(). */
+typedef struct {
+  void* pages;  size_t pages_bytes;   /* plain pages */
+  void* codes4; size_t codes4_bytes;  /* INT4 code pages (quant only) */
+  void* codes2; size_t codes2_bytes;  /* INT2 code pages (quant only) */
+  void* meta;   size_t meta_bytes;    /* device block tables: exactly lkv_size_info.meta_bytes or more */
+} lkv_arenas;
+
+typedef struct {
+  size_t page_bytes;       /* one plain page: all KV heads, 16 tokens, K and V */
+  size_t code4_page_bytes; /* one INT4 code page: all KV heads, 32 tokens */
+  size_t code2_page_bytes; /* one INT2 code page */
+  size_t meta_bytes;       /* device tables */
+} lkv_size_info;
+
+typedef struct {
+  int32_t layer;             /* core layer */
+  int32_t loop;              /* r, 0-based */
+  int32_t n_seqs;            /* rows of q / out: 1..max_seqs */
+  const int32_t* seq_ids;    /* host array [n_seqs] */
+  int32_t q_len;             /* 1 for DECODE and DRAFT, k (<= max_block) for VERIFY */
+  int32_t mode;              /* LKV_MODE_* */
+  int32_t window;            /* RIPE window for this call; -1 = the cache's window */
+  int32_t split_k;           /* splits of each row's pages; 0 = chosen by the library */
+  float v_thresh_offset;     /* quant: far token hot iff s >= m0 - offset (m0 = max sink score) */
+  const void* q;             /* device [n_seqs][q_len][n_heads_q][head_dim], kv dtype */
+  void* out;                 /* device [n_seqs][q_len][n_heads_q][head_dim], kv dtype */
+  float* lse;                /* device [n_seqs][q_len][n_heads_q] natural log, or NULL */
+  void* workspace;           /* device scratch for split partials, lkv_workspace_bytes() */
+  size_t workspace_bytes;
+  /* DRAFT only: the draft block's own keys/values at this (layer, loop), for
+     positions len..len+draft_len-1 of each sequence; the query is the last of
+     them.  Device [n_seqs][draft_len][n_heads_kv][head_dim], kv dtype. */
+  const void* draft_k;
+  const void* draft_v;
+  int32_t draft_len;         /* 1..max_block */
+  /* Debug traces (NULL = off).  index_trace: device int32 [n_seqs][q_len][trace_len][2]
+     holding (plane read, physical token slot = phys_page * 16 + slot) for every key
+     position of query head 0, or (-1, -1) where the row does not read position j.
+     mask_trace (quant): device uint32 [n_seqs][n_heads_q][ceil(n_far / 32)] hot bits. */
+  int32_t* index_trace;
+  int32_t trace_len;
+  uint32_t* mask_trace;
+  /* Optional hipEvent_t pair recorded on `stream` around the main attention kernel
+     (not the merge), for timing. */
+  void* ev_begin;
+  void* ev_end;
+} lkv_attend_args;
+
+typedef struct {
+  int64_t logical_bytes;     /* K/V bytes the policy must hold: Eq. (3)/(10) core-layer terms */
+  int64_t pages_in_use;      /* plain pages handed out */
+  int64_t pages_total;
+  int64_t code4_in_use, code4_total;
+  int64_t code2_in_use, code2_total;
+} lkv_mem_info;
+
+typedef struct lkv_cache lkv_cache;
+
+/* Page and table sizes for a configuration.  Pure host computation. */
+lkv_status lkv_sizes(const lkv_config* cfg, lkv_size_info* out);
+
+/* Create a cache over caller-owned arenas (host bookkeeping only; no device
+   work).  Errors: EINVAL (config), ENOMEM (meta arena smaller than required). */
+lkv_status lkv_create(const lkv_config* cfg, const lkv_arenas* arenas, int device, lkv_cache** out);
+lkv_status lkv_destroy(lkv_cache* c);
+
+/* Sequence slots.  A new sequence has length 0. */
+lkv_status lkv_add_seq(lkv_cache* c, int32_t* seq_out);
+lkv_status lkv_free_seq(lkv_cache* c, int32_t seq);
+
+/* Allocate the pages that positions [pos0, pos0 + n_tok) of plane `plane` need,
+   without writing them (host bookkeeping; lkv_append_plane = reserve + copy).
+   Extends the sequence length to pos0 + n_tok.  Plain caches: positions must
+   not leave a gap after the plane's last position (ESTATE); RIPE non-deepest
+   planes accept only positions >= committed - W that fit the window ring
+   (EWINDOW); ENOMEM if the pool is empty. */
+lkv_status lkv_reserve(lkv_cache* c, int32_t seq, int32_t layer, int32_t plane, int32_t pos0,
+                       int32_t n_tok);
+
+/* Write positions [pos0, pos0 + n_tok) of (seq, layer, plane): k and v are device
+   [n_tok][n_heads_kv][head_dim] in kv dtype, caller-owned, read on `stream`.
+   Errors as lkv_reserve, plus EDEVICE. */
+lkv_status lkv_append_plane(lkv_cache* c, int32_t seq, int32_t layer, int32_t plane, int32_t pos0,
+                            int32_t n_tok, const void* k, const void* v, void* stream);
+
+/* Algorithm 1 step 7 of the RIPE page: positions < new_len are committed, and
+   the non-deepest planes of positions older than new_len - W are dropped
+   (their window-ring pages return to the pool).  new_len <= length. */
+lkv_status lkv_commit(lkv_cache* c, int32_t seq, int32_t new_len);
+
+/* Roll the sequence back to new_len positions (a rejected draft block): pages
+   holding only positions >= new_len return to the pool.  new_len >= committed. */
+lkv_status lkv_truncate(lkv_cache* c, int32_t seq, int32_t new_len);
+
+/* Quantised caches: the kind of every (layer, loop) cell, host int8
+   [n_layers][n_loops] of LKV_CELL_INT4 / INT2 / SHARED.  The deepest loop may not
+   be SHARED (EINVAL).  Must be set before any lkv_append_coded. */
+lkv_status lkv_set_plan(lkv_cache* c, const int8_t* kinds);
+
+/* Quantised caches: write far-history code pages [page0, page0 + n_pages) of
+   (seq, layer, loop).  Far page p holds positions sink + 32p .. sink + 32p + 31.
+   Inputs are device arrays in a plain logical layout (the library packs them):
+     k_codes [n_pages*32][n_heads_kv][head_dim] uint8, values 0..2^bits-1;
+     k_meta  [n_pages][n_heads_kv][head_dim][2] fp16 (scale, zero) per channel
+             over the page's 32 tokens;
+     v_codes [n_pages*32][n_heads_kv][head_dim] uint8;
+     v_meta  [n_pages*32][n_heads_kv][head_dim/32][2] fp16 (scale, zero) per token
+             and 32-channel group.
+   bits = 4 for INT4 cells, 2 for INT2; SHARED cells store nothing (EINVAL). */
+lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0,
+                            int32_t n_pages, const void* k_codes, const void* k_meta,
+                            const void* v_codes, const void* v_meta, void* stream);
+
+/* Workspace an attend call needs (0 when it runs unsplit). */
+lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, size_t* bytes);
+
+/* Attention of n_seqs rows at (layer, loop), on `stream`.
+   DECODE (q_len = 1) and VERIFY (q_len = k, causal inside [t0, L)) read the
+   cache; DRAFT reads cached positions < len through the policy with the given
+   window (0 = the deepest plane, the RIPE page's Alg. 1 draft) and the block's
+   positions from draft_k / draft_v.  Quantised caches serve DECODE.
+   Errors: EINVAL (arguments), ESTATE (a needed page is missing), ENOMEM
+   (workspace too small), EUNSUPPORTED, EDEVICE. */
+lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream);
+
+lkv_status lkv_mem_stats(const lkv_cache* c, lkv_mem_info* out);
+
+/* Host index function: the plane, physical page and slot that the row at
+   position t of a block starting at t0 reads for key j (window -1 = cache
+   default).  -1 for a page that is not resident. */
+lkv_status lkv_debug_resolve(const lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t t,
+                             int32_t t0, int32_t j, int32_t window, int32_t* plane,
+                             int32_t* phys_page, int32_t* slot);
+
+/* Length and committed length of a sequence. */
+lkv_status lkv_seq_info(const lkv_cache* c, int32_t seq, int32_t* len, int32_t* committed);
+
+const char* lkv_last_error(const lkv_cache* c);
+const char* lkv_status_str(lkv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOPATTN_H */

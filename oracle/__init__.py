@@ -76,6 +76,8 @@ def _lib():
         L.oracle_cell_row.argtypes = [i32, i32, i32, i32, i32, pd, pd, pd, pu8, pd, pd, pu8, pd, pd, dbl, pd, pd,
                                       pu8]
         L.oracle_cell_row.restype = i32
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = i32
         _LIB = L
     return _LIB
 
@@ -93,6 +95,11 @@ def _i(a):
 def _u8(a):
     a = np.ascontiguousarray(a, dtype=np.uint8)
     return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def threads() -> int:
+    """OpenMP threads the row-parallel oracle routines run on."""
+    return int(_lib().oracle_threads())
 
 
 def oracle_plane(policy: int, loop: int, n_loops: int, t: int, t0: int, j: int, window: int) -> int:

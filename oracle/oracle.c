@@ -26,6 +26,7 @@
  * sees keys j <= t; the score scale is 1/sqrt(d).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -256,4 +257,15 @@ int oracle_cell_row(int d, int L, int sink, int tail, int kind, const double* q,
   free(kh);
   free(s);
   return n_cold;
+}
+
+/* Threads the row-parallel routines use (OpenMP), for reporting. */
+int oracle_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
 }

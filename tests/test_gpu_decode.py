@@ -1,0 +1,197 @@
+"""GPU parity of q = 1 decode through the C-ABI against the fp64 oracle.
+
+Tolerances (max-abs on outputs): 1e-5 for fp32 caches, 2e-2 for bf16 caches
+(bf16 inputs, fp32 accumulation, bf16 output rounding).  Page indexing is
+compared exactly: the kernel's per-position trace of (plane, physical slot)
+against the oracle's plane map and the host block tables.
+"""
+import numpy as np
+import pytest
+
+import harness
+import oracle
+import synth
+import verify_attention_loop_amd as vla
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL_F32, TOL_BF16 = 1e-5, 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    vla.load()
+
+
+def _attend(built, layer, loop, q, split_k, window=-1, trace_len=0):
+    w = built.w
+    n = len(built.seqs)
+    out = torch.empty_like(q)
+    lse = torch.empty((n, q.shape[1], w.n_heads), dtype=torch.float32, device="cuda")
+    ws_bytes = built.cache.lkv_workspace_bytes(layer, loop, built.seqs, q_len=q.shape[1], split_k=split_k)
+    ws = torch.empty(max(4, ws_bytes), dtype=torch.uint8, device="cuda")
+    tr = torch.empty((n, q.shape[1], trace_len, 2), dtype=torch.int32, device="cuda") if trace_len else None
+    built.cache.lkv_attend(layer, loop, built.seqs, q, out, q_len=q.shape[1], split_k=split_k, lse=lse,
+                           workspace=ws, window=window, index_trace=tr, trace_len=trace_len)
+    torch.cuda.synchronize()
+    return out, lse, tr
+
+
+@pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 0), (vla.POLICY_RIPE, 16),
+                                      (vla.POLICY_RIPE, 128)])
+@pytest.mark.parametrize("split_k", [1, 3])
+def test_tiny_fp32_every_row_and_trace(policy, W, split_k):
+    """Tiny workload: fp32, 1 layer, 4 loops, 2 heads x 64, L = 128, seed 0: every output, lse and the
+    exact page-index trace, for the full cache and RIPE W in {0, 16, 128} on the same inputs."""
+    w = synth.WORKLOADS["tiny"]
+    built = harness.build_plain(w, policy=policy, window=W, poison=True)
+    L = w.length
+    for loop in range(w.n_loops):
+        q = harness.gpu_queries(built, 0, loop, 1)
+        out, lse, tr = _attend(built, 0, loop, q, split_k, trace_len=L)
+        rows = [(0, 0, h) for h in range(w.n_heads)]
+        want, want_lse = harness.oracle_rows(w, rows, 0, loop, built.lengths, 1, policy, W)
+        got = harness.out_f64(out)[0, 0]
+        assert np.abs(got - want).max() <= TOL_F32
+        assert np.abs(lse.cpu().numpy()[0, 0] - want_lse).max() <= TOL_F32
+        trace = tr.cpu().numpy()[0, 0]
+        pm = oracle.plane_map(policy, loop, w.n_loops, L - 1, L - 1, L, W)
+        np.testing.assert_array_equal(trace[:, 0], pm)
+        for j in range(L):
+            plane, phys, slot = built.cache.lkv_debug_resolve(built.seqs[0], 0, loop, L - 1, L - 1, j, W)
+            assert plane == pm[j] and trace[j, 1] == phys * 16 + slot
+    built.cache.close()
+
+
+def _ragged(D, mode=synth.MODE_RIPEN):
+    return synth.Workload("ragged", 6, 2, 5, 3, D, 257, synth.DT_BF16, "ripe", 20, 1, 16, mode, 1.0)
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("policy", [vla.POLICY_FULL, vla.POLICY_RIPE])
+def test_ragged_lengths_bf16(D, policy):
+    """Ragged batch (lengths 1, 15, 16, 17, 100, 257: empty window, page edges, partial pages), shuffled
+    pages poisoned with NaN, loops 0 / 2 / deepest, splits 1 / 2 / 5."""
+    w = _ragged(D)
+    lengths = [1, 15, 16, 17, 100, 257]
+    built = harness.build_plain(w, lengths=lengths, layers=(1,), policy=policy, window=20, shuffle=True,
+                                poison=True)
+    rows = [(b, 0, h) for b in range(len(lengths)) for h in range(w.n_heads)]
+    for loop in (0, 2, w.n_loops - 1):
+        want, want_lse = harness.oracle_rows(w, rows, 1, loop, lengths, 1, policy, 20)
+        q = harness.gpu_queries(built, 1, loop, 1)
+        for split_k in (1, 2, 5):
+            out, lse, _ = _attend(built, 1, loop, q, split_k)
+            got = harness.out_f64(out)[:, 0]
+            assert np.isfinite(got).all()
+            err = np.abs(got.reshape(-1, D) - want).max()
+            assert err <= TOL_BF16, (loop, split_k, err)
+            assert np.abs(lse.cpu().numpy()[:, 0].reshape(-1) - want_lse).max() <= 1e-3
+    built.cache.close()
+
+
+def test_shuffled_tables_are_bitwise_identical_to_identity_tables():
+    """Paging changes addresses, not values: identical outputs for shuffled and in-order page tables."""
+    w = _ragged(96)
+    lengths = [33, 100, 257]
+    outs = []
+    for shuffle in (False, True):
+        built = harness.build_plain(w, lengths=lengths, policy=vla.POLICY_RIPE, window=20, shuffle=shuffle)
+        q = harness.gpu_queries(built, 0, 1, 1)
+        outs.append([_attend(built, 0, 1, q, s)[0].cpu() for s in (1, 4)])
+        built.cache.close()
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_window_covering_context_is_bitwise_the_full_cache():
+    """RIPE with W >= L - 1 reads plane r everywhere, i.e. exactly the full cache."""
+    w = _ragged(128)
+    lengths = [40, 64, 90]
+    full = harness.build_plain(w, lengths=lengths, policy=vla.POLICY_FULL)
+    ripe = harness.build_plain(w, lengths=lengths, policy=vla.POLICY_RIPE, window=200, max_len=256)
+    for loop in (0, 3):
+        q = harness.gpu_queries(full, 0, loop, 1)
+        for s in (1, 3):
+            a = _attend(full, 0, loop, q, s)[0]
+            b = _attend(ripe, 0, loop, q, s)[0]
+            assert torch.equal(a, b)
+    full.cache.close()
+    ripe.cache.close()
+
+
+def test_window_zero_reads_the_deepest_plane():
+    """W = 0 is the deepest-plane cache: every cached position reads plane R (RIPE page, Sec. 2)."""
+    w = _ragged(64)
+    lengths = [50, 77]
+    built = harness.build_plain(w, lengths=lengths, policy=vla.POLICY_RIPE, window=0)
+    rows = [(b, 0, h) for b in range(2) for h in range(w.n_heads)]
+    for loop in (0, 1):
+        q = harness.gpu_queries(built, 0, loop, 1)
+        out, _, tr = _attend(built, 0, loop, q, 2, trace_len=80)
+        t = tr.cpu().numpy()
+        for b, L in enumerate(lengths):
+            assert (t[b, 0, :L - 1, 0] == w.n_loops - 1).all() and t[b, 0, L - 1, 0] == loop
+            assert (t[b, 0, L:, 0] == -1).all()
+        want, _ = harness.oracle_rows(w, rows, 0, loop, lengths, 1, vla.POLICY_RIPE, 0)
+        assert np.abs(harness.out_f64(out)[:, 0].reshape(-1, 64) - want).max() <= TOL_BF16
+    built.cache.close()
+
+
+def test_split_k_merge_matches_unsplit_fp32():
+    """LSE merge of split partials equals the unsplit softmax (fp32 cache: within 1e-6)."""
+    w = synth.Workload("f32", 3, 1, 3, 4, 128, 700, synth.DT_F32, "ripe", 33, 1, 16, synth.MODE_RIPEN, 0.25)
+    built = harness.build_plain(w, lengths=[700, 129, 16], policy=vla.POLICY_RIPE, window=33, shuffle=True)
+    q = harness.gpu_queries(built, 0, 1, 1)
+    base = harness.out_f64(_attend(built, 0, 1, q, 1)[0])
+    for s in (2, 7, 16, 64):
+        got = harness.out_f64(_attend(built, 0, 1, q, s)[0])
+        assert np.abs(got - base).max() <= 1e-6
+    built.cache.close()
+
+
+@pytest.mark.slow
+def test_huginn_ripe_full_size_sampled():
+    """Huginn-shaped RIPE decode at full size (32 sequences, 55 heads x 96, L = 1024, W = 64, page 16),
+    layer 0, loops 0 / 17 / 31, the launch configuration the benchmark times; sampled rows vs the oracle,
+    the whole index trace of head 0 vs the oracle's plane map."""
+    w = synth.WORKLOADS["huginn_ripe"]
+    built = harness.build_plain(w, layers=(0,))
+    L = w.length
+    rows = harness.sample_rows(w.batch, 1, w.n_heads, 20, seed=1)
+    for loop in (0, 17, 31):
+        q = harness.gpu_queries(built, 0, loop, 1)
+        out, lse, tr = _attend(built, 0, loop, q, 0, trace_len=L)
+        o = harness.out_f64(out)
+        assert np.isfinite(o).all()
+        want, want_lse = harness.oracle_rows(w, rows, 0, loop, built.lengths, 1, vla.POLICY_RIPE, w.window)
+        got = np.array([o[b, i, h] for (b, i, h) in rows])
+        assert np.abs(got - want).max() <= TOL_BF16
+        pm = oracle.plane_map(vla.POLICY_RIPE, loop, w.n_loops, L - 1, L - 1, L, w.window)
+        t = tr.cpu().numpy()
+        for b in range(w.batch):
+            np.testing.assert_array_equal(t[b, 0, :, 0], pm)
+    built.cache.close()
+
+
+@pytest.mark.slow
+def test_ouro_full_size_sampled():
+    """Ouro-shaped paged decode at full size for one layer (32 sequences, 16 heads x 128, L = 8192,
+    shuffled page tables, 8 splits merged by LSE): sampled rows vs the oracle."""
+    w = synth.WORKLOADS["ouro_splitk"]
+    built = harness.build_plain(w, layers=(0,), planes=[0, 3])
+    rows = harness.sample_rows(w.batch, 1, w.n_heads, 12, seed=2)
+    for loop in (0, 3):
+        q = harness.gpu_queries(built, 0, loop, 1)
+        out, lse, _ = _attend(built, 0, loop, q, 8)
+        o = harness.out_f64(out)
+        assert np.isfinite(o).all()
+        want, want_lse = harness.oracle_rows(w, rows, 0, loop, built.lengths, 1, vla.POLICY_FULL, 0)
+        got = np.array([o[b, i, h] for (b, i, h) in rows])
+        assert np.abs(got - want).max() <= TOL_BF16
+        got_lse = lse.cpu().numpy()
+        assert np.abs(np.array([got_lse[b, i, h] for (b, i, h) in rows]) - want_lse).max() <= 1e-3
+    built.cache.close()

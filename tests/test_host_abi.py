@@ -1,0 +1,230 @@
+"""Host-side tests of the C-ABI library: exports, allocator, tables, window ring,
+accounting and error paths.  No GPU: only calls that do host bookkeeping are made,
+on arenas whose addresses are never dereferenced."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import verify_attention_loop_amd as vla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vla.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return vla.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    hdr = open(os.path.join(ROOT, "include", "loopattn.h")).read()
+    declared = set(re.findall(r"^(?:lkv_status|const char\*)\s+(lkv_\w+)\(", hdr, flags=re.M))
+    assert declared, "no declarations parsed"
+    assert declared == set(vla.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+class HostArenas:
+    """Fake device arenas: host buffers whose addresses the host-only calls never read."""
+
+    def __init__(self, cfg, n_pages, n4=0, n2=0):
+        s = vla.LoopCache.sizes(cfg)
+        self.meta = np.zeros(max(256, s.meta_bytes), dtype=np.uint8)
+        base = 1 << 40  # never dereferenced
+        self.ar = vla.lkv_arenas(base, n_pages * s.page_bytes, base + (1 << 38), n4 * s.code4_page_bytes,
+                                 base + (1 << 39), n2 * s.code2_page_bytes, self.meta.ctypes.data, s.meta_bytes)
+        self.sizes = s
+
+
+def make(n_pages=64, **kw):
+    base = dict(n_layers=2, n_loops=4, n_heads_q=2, n_heads_kv=2, head_dim=64, kv_dtype=vla.DTYPE_BF16,
+                policy=vla.POLICY_RIPE, window=16, max_seqs=4, max_len=256, max_block=8)
+    base.update(kw)
+    cfg = vla.LoopCache.config(**base)
+    ha = HostArenas(cfg, n_pages)
+    c = vla.LoopCache(cfg, ha.ar, 0)
+    c._host_arenas = ha
+    return c
+
+
+def test_page_size_and_table_bytes(lib):
+    cfg = vla.LoopCache.config(n_layers=4, n_loops=32, n_heads_q=55, n_heads_kv=55, head_dim=96,
+                               kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_RIPE, window=64, max_seqs=32,
+                               max_len=1024, max_block=8)
+    s = vla.LoopCache.sizes(cfg)
+    assert s.page_bytes == 2 * 55 * 16 * 96 * 2
+    # deepest plane: 64 pages per sequence; window ring: ceil((64 + 8) / 16) + 1 = 6 pages
+    row = lambda n: (32 * n * 4 + 255) // 256 * 256
+    assert s.meta_bytes == 4 * (row(64) + 31 * row(6))
+
+
+def test_sequence_slots_and_errors_leave_handle_usable(lib):
+    c = make()
+    ids = [c.lkv_add_seq() for _ in range(4)]
+    assert ids == [0, 1, 2, 3]
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_add_seq()
+    assert e.value.status == vla.LKV_ENOMEM
+    c.lkv_free_seq(2)
+    assert c.lkv_add_seq() == 2
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_reserve(0, 5, 0, 0, 4)  # bad layer
+    assert e.value.status == vla.LKV_EINVAL
+    c.lkv_reserve(0, 0, 3, 0, 20)
+    assert c.lkv_seq_info(0) == (20, 0)
+
+
+def test_append_without_gap_and_pool_exhaustion(lib):
+    c = make(n_pages=5, policy=vla.POLICY_FULL)
+    s = c.lkv_add_seq()
+    c.lkv_reserve(s, 0, 1, 0, 40)  # 3 pages
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_reserve(s, 0, 1, 50, 4)  # gap after position 40
+    assert e.value.status == vla.LKV_ESTATE
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_reserve(s, 0, 2, 0, 48)  # 3 more pages, only 2 free
+    assert e.value.status == vla.LKV_ENOMEM
+    assert c.lkv_mem_stats()["pages_in_use"] == 3  # the failed call allocated nothing
+    c.lkv_reserve(s, 0, 2, 0, 32)
+    assert c.lkv_mem_stats()["pages_in_use"] == 5
+
+
+def test_window_ring_commit_and_ewindow(lib):
+    """RIPE page, Sec. 4 and Alg. 1 step 7: non-deepest planes are kept for the last W positions only;
+    committing drops the planes of positions older than W, and their pages return to the pool."""
+    W = 16
+    c = make(n_pages=200, window=W, max_block=8)
+    s = c.lkv_add_seq()
+    R = 4
+    # prefill 100 positions of the deepest plane, window planes only for the last W
+    c.lkv_reserve(s, 0, R - 1, 0, 100)
+    c.lkv_commit(s, 100)
+    for p in range(R - 1):
+        with pytest.raises(vla.LkvError) as e:
+            c.lkv_reserve(s, 0, p, 100 - W - 1, 5)
+        assert e.value.status == vla.LKV_EWINDOW
+        c.lkv_reserve(s, 0, p, 100 - W, W)
+    used = c.lkv_mem_stats()["pages_in_use"]
+    # decode 200 more tokens one at a time: ring pages are recycled, the deepest plane grows
+    for n in range(100, 250):
+        for p in range(R):
+            c.lkv_reserve(s, 0, p, n, 1)
+        c.lkv_commit(s, n + 1)
+    st = c.lkv_mem_stats()
+    deep_pages = (250 + 15) // 16
+    ring_pages = st["pages_in_use"] - deep_pages
+    assert ring_pages <= (R - 1) * ((W + 8 + 15) // 16 + 1)
+    assert st["pages_in_use"] > used
+    # a position older than the window can no longer be written in a non-deepest plane
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_reserve(s, 0, 0, 250 - W - 1, 1)
+    assert e.value.status == vla.LKV_EWINDOW
+
+
+def test_truncate_rolls_back_a_block(lib):
+    c = make(n_pages=100, window=16, max_block=8)
+    s = c.lkv_add_seq()
+    for p in range(4):
+        c.lkv_reserve(s, 0, p, 0 if p == 3 else 0, 40)
+    c.lkv_commit(s, 32)
+    for p in range(4):
+        c.lkv_reserve(s, 0, p, 40, 8)  # block of 8
+    assert c.lkv_seq_info(s) == (48, 32)
+    before = c.lkv_mem_stats()["pages_in_use"]
+    c.lkv_truncate(s, 41)  # accept 1 token of the block
+    assert c.lkv_seq_info(s) == (41, 32)
+    assert c.lkv_mem_stats()["pages_in_use"] <= before
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_truncate(s, 30)  # below committed
+    assert e.value.status == vla.LKV_EINVAL
+
+
+def test_logical_bytes_follow_eq3_and_eq10(lib):
+    """RIPE page, Eq. (3) and Eq. (10) for the core layers: the full cache holds R planes per position,
+    RIPE the deepest plane plus R-1 planes for min(W, L) positions."""
+    for policy in (vla.POLICY_FULL, vla.POLICY_RIPE):
+        c = make(n_pages=400, policy=policy, window=16, n_layers=2, n_loops=4, head_dim=64, n_heads_kv=2,
+                 n_heads_q=2)
+        b = oracle.kv_bytes_per_layer_token(2, 64)
+        for L in (5, 16, 100):
+            s = c.lkv_add_seq()
+            c.lkv_reserve(s, 0, 3, 0, L)
+            got = c.lkv_mem_stats()["logical_bytes"]
+            want = (oracle.mem_full(L, b, 0, 0, 2, 4) if policy == vla.POLICY_FULL
+                    else oracle.mem_ripe(L, b, 0, 0, 2, 4, 16))
+            assert got == want, (policy, L)
+            c.lkv_free_seq(s)
+
+
+def test_debug_resolve_matches_policy_and_tables(lib):
+    """The host index function names the plane of Eq. (9) (with the block rule) and the physical page
+    that the block table holds for it."""
+    R, W = 4, 16
+    c = make(n_pages=300, window=W, max_block=8, shuffle_seed=7)
+    s = c.lkv_add_seq()
+    L = 90
+    c.lkv_reserve(s, 0, R - 1, 0, L)
+    c.lkv_commit(s, L - 8)
+    for p in range(R - 1):
+        c.lkv_reserve(s, 0, p, L - 8 - W, W + 8)
+    t0 = L - 8
+    phys_seen = {}
+    for r in range(R):
+        for t in range(t0, L):
+            for j in range(t + 1):
+                plane, phys, slot = c.lkv_debug_resolve(s, 0, r, t, t0, j)
+                assert plane == oracle.oracle_plane(oracle.RIPE, r, R, t, t0, j, W)
+                assert slot == j % 16 and phys >= 0
+                key = (plane, j // 16)
+                assert phys_seen.setdefault(key, phys) == phys
+    # distinct (plane, page) pairs never share a physical page
+    assert len(set(phys_seen.values())) == len(phys_seen)
+
+
+def test_shuffled_pool_hands_out_a_permutation(lib):
+    c = make(n_pages=64, policy=vla.POLICY_FULL, shuffle_seed=123, max_len=1024)
+    s = c.lkv_add_seq()
+    c.lkv_reserve(s, 0, 0, 0, 1024)
+    phys = [c.lkv_debug_resolve(s, 0, 0, 1023, 1023, j * 16)[1] for j in range(64)]
+    assert sorted(phys) == list(range(64)) and phys != list(range(64))
+
+
+def test_config_validation(lib):
+    cfg = vla.LoopCache.config(n_layers=1, n_loops=4, n_heads_q=3, n_heads_kv=2, head_dim=64,
+                               kv_dtype=vla.DTYPE_BF16, policy=0, window=0, max_seqs=1, max_len=16, max_block=1)
+    with pytest.raises(vla.LkvError):
+        vla.LoopCache.sizes(cfg)  # heads not divisible
+    cfg.n_heads_q = 2
+    cfg.head_dim = 80
+    with pytest.raises(vla.LkvError):
+        vla.LoopCache.sizes(cfg)
+    cfg.head_dim = 64
+    cfg.max_block = 17
+    with pytest.raises(vla.LkvError):
+        vla.LoopCache.sizes(cfg)
+
+
+def test_plan_rules(lib):
+    cfg = vla.LoopCache.config(n_layers=2, n_loops=4, n_heads_q=16, n_heads_kv=16, head_dim=128,
+                               kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=2,
+                               max_len=400, max_block=1, quant=1, sink=4, tail=128)
+    ha = HostArenas(cfg, 10, 10, 10)
+    c = vla.LoopCache(cfg, ha.ar, 0)
+    plan = np.full((2, 4), vla.CELL_INT4, dtype=np.int8)
+    plan[0, 3] = vla.CELL_SHARED
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_set_plan(plan)  # the final loop is the source of shared cells
+    assert e.value.status == vla.LKV_EINVAL
+    plan[0, 3] = vla.CELL_INT4
+    plan[0, 1] = vla.CELL_SHARED
+    plan[1, 0] = vla.CELL_INT2
+    c.lkv_set_plan(plan)
+    assert ha.sizes.code4_page_bytes == 16 * 160 * 32  # LoopKV page App. C: 2.5 KiB per token and layer
+    assert ha.sizes.code2_page_bytes == 16 * 96 * 32   # 1.5 KiB

@@ -1,0 +1,267 @@
+"""Python binding of libloopattn (loop-aware attention over a looped model's
+multi-plane KV cache, MI355X / gfx950).
+
+Argument marshalling only: every call goes through the C-ABI declared in
+``include/loopattn.h``; every step of the attention path runs in the library's
+HIP kernels.  PyTorch provides device memory (the arenas, inputs, outputs) and
+the stream.  If the library is not built this module raises on first use; it
+has no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libloopattn.so")
+
+LKV_OK, LKV_EINVAL, LKV_ENOMEM, LKV_ESTATE, LKV_EWINDOW, LKV_EDEVICE, LKV_EUNSUPPORTED = range(7)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+POLICY_FULL, POLICY_RIPE = 0, 1
+MODE_DECODE, MODE_VERIFY, MODE_DRAFT = 0, 1, 2
+CELL_BF16, CELL_INT4, CELL_INT2, CELL_SHARED = 0, 1, 2, 3
+PAGE_TOKENS, CODE_PAGE_TOKENS = 16, 32
+
+EXPORTS = [
+    "lkv_sizes", "lkv_create", "lkv_destroy", "lkv_add_seq", "lkv_free_seq", "lkv_reserve", "lkv_append_plane",
+    "lkv_commit", "lkv_truncate", "lkv_set_plan", "lkv_append_coded", "lkv_workspace_bytes", "lkv_attend",
+    "lkv_mem_stats", "lkv_debug_resolve", "lkv_seq_info", "lkv_last_error", "lkv_status_str",
+]
+
+
+class lkv_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "n_loops", "n_heads_q", "n_heads_kv", "head_dim", "page_size", "kv_dtype", "policy", "window",
+        "max_seqs", "max_len", "max_block", "quant", "sink", "tail", "poison")] + [("shuffle_seed", ctypes.c_uint64)]
+
+
+class lkv_arenas(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("pages_bytes", ctypes.c_size_t),
+                ("codes4", ctypes.c_void_p), ("codes4_bytes", ctypes.c_size_t),
+                ("codes2", ctypes.c_void_p), ("codes2_bytes", ctypes.c_size_t),
+                ("meta", ctypes.c_void_p), ("meta_bytes", ctypes.c_size_t)]
+
+
+class lkv_size_info(ctypes.Structure):
+    _fields_ = [("page_bytes", ctypes.c_size_t), ("code4_page_bytes", ctypes.c_size_t),
+                ("code2_page_bytes", ctypes.c_size_t), ("meta_bytes", ctypes.c_size_t)]
+
+
+class lkv_attend_args(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_int32), ("loop", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+                ("seq_ids", ctypes.POINTER(ctypes.c_int32)), ("q_len", ctypes.c_int32), ("mode", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("split_k", ctypes.c_int32), ("v_thresh_offset", ctypes.c_float),
+                ("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("draft_k", ctypes.c_void_p), ("draft_v", ctypes.c_void_p), ("draft_len", ctypes.c_int32),
+                ("index_trace", ctypes.c_void_p), ("trace_len", ctypes.c_int32), ("mask_trace", ctypes.c_void_p),
+                ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p)]
+
+
+class lkv_mem_info(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("logical_bytes", "pages_in_use", "pages_total", "code4_in_use",
+                                               "code4_total", "code2_in_use", "code2_total")]
+
+
+class LkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+_LIB = None
+
+
+def load():
+    """Load libloopattn.so (raises if it is not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, vp, st = ctypes.c_int32, ctypes.c_void_p, ctypes.c_int
+    P = ctypes.POINTER
+    sig = {
+        "lkv_sizes": [P(lkv_config), P(lkv_size_info)],
+        "lkv_create": [P(lkv_config), P(lkv_arenas), ctypes.c_int, P(vp)],
+        "lkv_destroy": [vp],
+        "lkv_add_seq": [vp, P(i32)],
+        "lkv_free_seq": [vp, i32],
+        "lkv_reserve": [vp, i32, i32, i32, i32, i32],
+        "lkv_append_plane": [vp, i32, i32, i32, i32, i32, vp, vp, vp],
+        "lkv_commit": [vp, i32, i32],
+        "lkv_truncate": [vp, i32, i32],
+        "lkv_set_plan": [vp, P(ctypes.c_int8)],
+        "lkv_append_coded": [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp],
+        "lkv_workspace_bytes": [vp, P(lkv_attend_args), P(ctypes.c_size_t)],
+        "lkv_attend": [vp, P(lkv_attend_args), vp],
+        "lkv_mem_stats": [vp, P(lkv_mem_info)],
+        "lkv_debug_resolve": [vp, i32, i32, i32, i32, i32, i32, i32, P(i32), P(i32), P(i32)],
+        "lkv_seq_info": [vp, i32, P(i32), P(i32)],
+    }
+    for name, args in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = st
+    L.lkv_last_error.argtypes = [vp]
+    L.lkv_last_error.restype = ctypes.c_char_p
+    L.lkv_status_str.argtypes = [st]
+    L.lkv_status_str.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def _ptr(x) -> int:
+    """Device address of a tensor (or an int address, or None -> 0)."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+class LoopCache:
+    """A handle over caller-owned arenas.  Method names follow the C-ABI (lkv_*)."""
+
+    def __init__(self, cfg: lkv_config, arenas: lkv_arenas, device: int = 0, keep=()):
+        self.lib = load()
+        self.cfg = cfg
+        self.arenas = arenas
+        self._keep = list(keep)  # tensors backing the arenas
+        h = ctypes.c_void_p()
+        rc = self.lib.lkv_create(ctypes.byref(cfg), ctypes.byref(arenas), device, ctypes.byref(h))
+        if rc != LKV_OK:
+            raise LkvError(rc, "lkv_create: " + self.lib.lkv_status_str(rc).decode())
+        self.h = h
+
+    # -- construction helpers
+    @staticmethod
+    def config(**kw) -> lkv_config:
+        c = lkv_config()
+        c.page_size = PAGE_TOKENS
+        c.max_block = 1
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return c
+
+    @staticmethod
+    def sizes(cfg: lkv_config) -> lkv_size_info:
+        s = lkv_size_info()
+        rc = load().lkv_sizes(ctypes.byref(cfg), ctypes.byref(s))
+        if rc != LKV_OK:
+            raise LkvError(rc, "lkv_sizes: invalid configuration")
+        return s
+
+    @classmethod
+    def on_device(cls, cfg: lkv_config, n_pages: int, n_code4: int = 0, n_code2: int = 0, device: int = 0):
+        """Allocate the arenas as torch uint8 tensors on cuda:device and create the cache."""
+        import torch
+        s = cls.sizes(cfg)
+        dev = torch.device("cuda", device)
+        pages = torch.empty(max(1, n_pages * s.page_bytes), dtype=torch.uint8, device=dev)
+        c4 = torch.empty(max(1, n_code4 * s.code4_page_bytes), dtype=torch.uint8, device=dev) if n_code4 else None
+        c2 = torch.empty(max(1, n_code2 * s.code2_page_bytes), dtype=torch.uint8, device=dev) if n_code2 else None
+        meta = torch.empty(max(256, s.meta_bytes), dtype=torch.uint8, device=dev)
+        ar = lkv_arenas(pages.data_ptr(), n_pages * s.page_bytes,
+                        c4.data_ptr() if c4 is not None else 0, n_code4 * s.code4_page_bytes,
+                        c2.data_ptr() if c2 is not None else 0, n_code2 * s.code2_page_bytes,
+                        meta.data_ptr(), s.meta_bytes)
+        return cls(cfg, ar, device, keep=[t for t in (pages, c4, c2, meta) if t is not None])
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.lkv_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, rc: int, what: str):
+        if rc != LKV_OK:
+            raise LkvError(rc, f"{what}: {self.lib.lkv_last_error(self.h).decode()}")
+
+    # -- C-ABI calls
+    def lkv_add_seq(self) -> int:
+        s = ctypes.c_int32()
+        self._check(self.lib.lkv_add_seq(self.h, ctypes.byref(s)), "lkv_add_seq")
+        return s.value
+
+    def lkv_free_seq(self, seq: int):
+        self._check(self.lib.lkv_free_seq(self.h, seq), "lkv_free_seq")
+
+    def lkv_reserve(self, seq: int, layer: int, plane: int, pos0: int, n_tok: int):
+        self._check(self.lib.lkv_reserve(self.h, seq, layer, plane, pos0, n_tok), "lkv_reserve")
+
+    def lkv_append_plane(self, seq: int, layer: int, plane: int, pos0: int, k, v, stream=None):
+        n_tok = k.shape[0]
+        self._check(self.lib.lkv_append_plane(self.h, seq, layer, plane, pos0, n_tok, _ptr(k), _ptr(v),
+                                              _stream(stream)), "lkv_append_plane")
+
+    def lkv_commit(self, seq: int, new_len: int):
+        self._check(self.lib.lkv_commit(self.h, seq, new_len), "lkv_commit")
+
+    def lkv_truncate(self, seq: int, new_len: int):
+        self._check(self.lib.lkv_truncate(self.h, seq, new_len), "lkv_truncate")
+
+    def lkv_set_plan(self, kinds):
+        import numpy as np
+        a = np.ascontiguousarray(kinds, dtype=np.int8)
+        self._check(self.lib.lkv_set_plan(self.h, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int8))), "lkv_set_plan")
+
+    def lkv_append_coded(self, seq: int, layer: int, loop: int, page0: int, n_pages: int, k_codes, k_meta, v_codes,
+                         v_meta, stream=None):
+        self._check(self.lib.lkv_append_coded(self.h, seq, layer, loop, page0, n_pages, _ptr(k_codes), _ptr(k_meta),
+                                              _ptr(v_codes), _ptr(v_meta), _stream(stream)), "lkv_append_coded")
+
+    def _args(self, layer, loop, seq_ids, q, out, q_len=1, mode=MODE_DECODE, window=-1, split_k=0,
+              v_thresh_offset=4.0, lse=None, workspace=None, draft_k=None, draft_v=None, draft_len=0,
+              index_trace=None, trace_len=0, mask_trace=None, ev_begin=None, ev_end=None):
+        ids = (ctypes.c_int32 * len(seq_ids))(*seq_ids)
+        a = lkv_attend_args()
+        a.layer, a.loop, a.n_seqs, a.seq_ids = layer, loop, len(seq_ids), ids
+        a.q_len, a.mode, a.window, a.split_k, a.v_thresh_offset = q_len, mode, window, split_k, v_thresh_offset
+        a.q, a.out, a.lse = _ptr(q), _ptr(out), _ptr(lse)
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        a.draft_k, a.draft_v, a.draft_len = _ptr(draft_k), _ptr(draft_v), draft_len
+        a.index_trace, a.trace_len, a.mask_trace = _ptr(index_trace), trace_len, _ptr(mask_trace)
+        a.ev_begin = ev_begin or 0
+        a.ev_end = ev_end or 0
+        return a, ids
+
+    def lkv_workspace_bytes(self, layer, loop, seq_ids, q_len=1, mode=MODE_DECODE, split_k=0) -> int:
+        a, _ids = self._args(layer, loop, seq_ids, None, None, q_len=q_len, mode=mode, split_k=split_k)
+        n = ctypes.c_size_t()
+        self._check(self.lib.lkv_workspace_bytes(self.h, ctypes.byref(a), ctypes.byref(n)), "lkv_workspace_bytes")
+        return n.value
+
+    def lkv_attend(self, layer, loop, seq_ids, q, out, stream=None, **kw):
+        a, _ids = self._args(layer, loop, seq_ids, q, out, **kw)
+        self._check(self.lib.lkv_attend(self.h, ctypes.byref(a), _stream(stream)), "lkv_attend")
+
+    def lkv_mem_stats(self) -> dict:
+        m = lkv_mem_info()
+        self._check(self.lib.lkv_mem_stats(self.h, ctypes.byref(m)), "lkv_mem_stats")
+        return {n: getattr(m, n) for n, _ in lkv_mem_info._fields_}
+
+    def lkv_debug_resolve(self, seq, layer, loop, t, t0, j, window=-1):
+        p, ph, sl = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._check(self.lib.lkv_debug_resolve(self.h, seq, layer, loop, t, t0, j, window, ctypes.byref(p),
+                                               ctypes.byref(ph), ctypes.byref(sl)), "lkv_debug_resolve")
+        return p.value, ph.value, sl.value
+
+    def lkv_seq_info(self, seq):
+        n, c = ctypes.c_int32(), ctypes.c_int32()
+        self._check(self.lib.lkv_seq_info(self.h, seq, ctypes.byref(n), ctypes.byref(c)), "lkv_seq_info")
+        return n.value, c.value

@@ -1,0 +1,102 @@
+// Kernel parameter blocks shared by the host library and the HIP kernels.
+// Passed by value as kernel arguments (well under the 4 KB limit).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lkv {
+
+constexpr int kPage = 16;       // tokens per plain page
+constexpr int kQuad = 4;        // tokens interleaved per channel in a V block
+constexpr int kCodePage = 32;   // tokens per code page
+constexpr int kMaxRows = 64;    // sequences per launch
+constexpr int kMaxBlock = 16;   // verify rows per sequence (one MFMA tile)
+
+enum : int32_t { kFull = 0, kRipe = 1 };
+enum : int32_t { kDecode = 0, kVerify = 1, kDraft = 2 };
+
+// Plain page layout (one page = one (seq, layer, plane), all KV heads, 16 tokens):
+//   K block: [head][token 0..15][channel 0..D-1]
+//   V block: [head][quad 0..3][channel 0..D-1][token-in-quad 0..3]
+// so each (page, head) K slice and V slice is one contiguous run of 16*D elements;
+// V interleaves four tokens per channel so that a lane reads four tokens of its
+// channels in one 16-byte load, and the verify tile gets V^T operands directly.
+
+// Attention over plain pages (DECODE, VERIFY, DRAFT).
+struct PlainParams {
+  const uint8_t* pool;        // plain page arena
+  uint64_t page_bytes;
+  const int32_t* tab_own;     // table of the loop's own plane: [seq slot][ring_own]
+  const int32_t* tab_deep;    // table of the deepest plane:    [seq slot][ring_deep]
+  int32_t ring_own;
+  int32_t ring_deep;
+  const void* q;              // [n_rows][q_len][hq][D]
+  void* out;                  // [n_rows][q_len][hq][D]
+  float* lse;                 // [n_rows][q_len][hq] or null
+  float* ws;                  // split partials [n_rows][q_len][hq][n_splits][D + 1]
+  const void* draft_k;        // DRAFT: [n_rows][draft_len][hkv][D]
+  const void* draft_v;
+  int32_t* trace;             // [n_rows][q_len][trace_len][2] or null
+  int32_t trace_len;
+  int32_t draft_len;
+  int32_t n_rows, q_len, hq, hkv;
+  int32_t window;             // effective RIPE window
+  int32_t ripe;               // 1: RIPE with loop < deepest; 0: every position reads tab_own
+  int32_t loop;
+  int32_t deepest;
+  int32_t n_splits;
+  float scale_log2;           // log2(e) / sqrt(D)
+  int32_t slot[kMaxRows];     // sequence slot (row of the tables)
+  int32_t len[kMaxRows];      // cached positions of the sequence
+};
+
+// Quantised LoopKV-style cells (DECODE).
+struct CellParams {
+  const uint8_t* pool;        // plain (bf16) pages: sink and tail of the cell's own loop
+  uint64_t page_bytes;
+  const int32_t* tab_near;    // [seq slot][ring_near]
+  int32_t ring_near;
+  const uint8_t* codes;       // code page arena of the cell's source (own, or the final loop's)
+  uint64_t code_page_bytes;
+  const int32_t* tab_code;    // [seq slot][code_ring]
+  int32_t code_ring;
+  int32_t bits;               // 4 or 2
+  int32_t masked;             // 1: V lo plane read only for hot tokens (INT4 / shared cells)
+  float thr_offset;           // hot iff s >= m0 - thr_offset (natural-log units)
+  const void* q;
+  void* out;
+  float* lse;
+  float* ws;                  // partials [n_rows][hq][n_splits + 1][D + 1]
+  uint32_t* mask_trace;       // [n_rows][hq][mask_words] or null
+  int32_t mask_words;
+  int32_t n_rows, hq, hkv;
+  int32_t sink, tail;
+  int32_t n_splits;           // far splits; block x == n_splits is the near (sink + tail) block
+  float scale_log2;
+  float scale;                // 1 / sqrt(D)
+  int32_t slot[kMaxRows];
+  int32_t len[kMaxRows];
+};
+
+// Merge of split partials.
+struct MergeParams {
+  const float* ws;            // [rows][n_parts][D + 1], entry D = base-2 lse (-inf if empty)
+  void* out;                  // [rows][D]
+  float* lse;                 // [rows] or null
+  int32_t n_rows;
+  int32_t n_parts;
+};
+
+// Append rows into plain pages.
+struct CopyParams {
+  uint8_t* pool;
+  uint64_t page_bytes;
+  const void* k;              // [n_tok][hkv][D]
+  const void* v;
+  int32_t pos0, n_tok, hkv;
+  int32_t page0;              // logical page of pos0
+  int32_t n_pages;
+  int32_t phys[64];           // physical page of logical page page0 + i
+};
+
+}  // namespace lkv

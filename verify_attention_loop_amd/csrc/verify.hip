@@ -1,0 +1,266 @@
+// q = k verification attention over plain pages (self-speculative verify).
+//
+// One pass runs a block of k tokens [t0, t0 + k) through loop r; query t reads
+// key j <= t from the plane the policy names (RIPE page, Eq. (9); block tokens
+// j >= t0 read plane r, proof of Prop. 1).  Under RIPE the rule depends on the
+// query, so a page that straddles the window edge is attended twice, once per
+// plane, each pass masking the (query, key) pairs the other plane owns.
+//
+// This is a dense k x 16 x D contraction per page and head, so it runs on MFMA:
+//   S^T[16 keys x 16 queries]  = K[16 x D] * Q^T         (16x16x32 bf16 / 16x16x4 f32)
+//   O^T[D x 16 queries]       += V^T[D x 16 keys] * P^T   (16x16x16 bf16 / 16x16x4 f32)
+// Lane l = (g = l / 16, n = l % 16): n is its query column; its S^T values are
+// keys 4g..4g+3 of the page for query n, which is exactly the P^T operand layout
+// of the PV product, and the V block's [quad][channel][4 keys] layout is exactly
+// the V^T operand (4 keys of one channel per lane).  Rows k..15 of the tile are
+// padding (k <= 16).
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "params.hpp"
+
+namespace lkv {
+
+__device__ __forceinline__ float xmax4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float xsum4(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <typename T, int D, int WAVES, bool TRACE>
+__global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p) {
+  constexpr bool F32 = sizeof(T) == 4;
+  constexpr int ES = F32 ? 4 : 2;
+  constexpr int HEAD = kPage * D * ES;
+  // bf16: D/32 QK steps of 32 channels and D/32 PV loads of two 16-channel blocks.
+  // f32:  D/16 loads of 4 channels, 4 QK MFMAs each; D/16 PV loads of 4 keys, 4 MFMAs each.
+  constexpr int NB = F32 ? D / 16 : D / 32;
+  constexpr int NACC = F32 ? D / 16 : D / 16;  // 16-channel output blocks
+
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int g = lane >> 4, n = lane & 15;
+  const int hk = h / (p.hq / p.hkv);
+  const int slot = p.slot[b];
+  const int L = p.len[b];
+  const int k = p.q_len;
+  const int t0 = L - k;
+  const bool qv = n < k;
+  const int tq = t0 + n;
+  const int own_n = p.ripe ? max(0, min(t0, tq - p.window)) : 0;
+  const int own_min = p.ripe ? max(0, min(t0, t0 - p.window)) : 0;
+  const int own_max = p.ripe ? max(0, min(t0, t0 + k - 1 - p.window)) : 0;
+
+  // Q^T operand (query n), zero for padding columns.
+  uint32_t qb[NB][4];
+  {
+    const int64_t qrow = (((int64_t)b * k + (qv ? n : 0)) * p.hq + h) * D;
+    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + qrow * ES;
+#pragma unroll
+    for (int s = 0; s < NB; ++s) {
+      Raw<16> r;
+      if constexpr (F32) load_raw<16>(r, qp + (16 * s + 4 * g) * 4);
+      else load_raw<16>(r, qp + (32 * s + 8 * g) * 2);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) qb[s][x] = qv ? r.w[x] : 0u;
+    }
+  }
+
+  f32x4_t acc[NACC];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) acc[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, lsum = 0.f;
+
+  const int n_pages = (L + kPage - 1) / kPage;
+  const int p0 = (int)((int64_t)split * n_pages / p.n_splits);
+  const int p1 = (int)((int64_t)(split + 1) * n_pages / p.n_splits);
+  const int32_t* tab_own = p.tab_own + (int64_t)slot * p.ring_own;
+  const int32_t* tab_deep = p.tab_deep + (int64_t)slot * p.ring_deep;
+
+  for (int pg = p0 + w; pg < p1; pg += WAVES) {
+    const int pos = pg * kPage;
+    const int vend = min(pos + kPage, L);
+    const bool any_own = vend - 1 >= own_min;
+    const bool any_deep = pos < own_max;
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool own = pass == 0;
+      if (own ? !any_own : !any_deep) continue;
+      const int phys = own ? tab_own[pg % p.ring_own] : tab_deep[pg];
+      const uint8_t* base = p.pool + (uint64_t)phys * p.page_bytes;
+      const uint8_t* kbase = base + (uint64_t)hk * HEAD + (uint64_t)n * D * ES;
+      const uint8_t* vbase = base + (uint64_t)p.hkv * HEAD + (uint64_t)hk * HEAD + (uint64_t)g * (kQuad * D * ES);
+
+      // ---- S^T = K Q^T
+      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (F32) {
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+          Raw<16> kr;
+          load_raw<16>(kr, kbase + (16 * s + 4 * g) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kr.w[e]), __uint_as_float(qb[s][e]), sc, 0, 0,
+                                                      0);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+          Raw<16> kr;
+          load_raw<16>(kr, kbase + (32 * s + 8 * g) * 2);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr.w),
+                                                       __builtin_bit_cast(bf16x8_t, qb[s]), sc, 0, 0, 0);
+        }
+      }
+
+      // ---- mask, online softmax for query n
+      float x[4];
+      bool keep[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = pos + 4 * g + i;
+        const bool plane_ok = own ? (j >= own_n) : (j < own_n);
+        const bool vis = qv && j <= tq && plane_ok;
+        x[i] = vis ? sc[i] * p.scale_log2 : -INFINITY;
+        keep[i] = j < L && (own ? j >= own_min : j < own_max);
+        if constexpr (TRACE) {
+          if (h == 0 && vis && j < p.trace_len) {
+            int32_t* tr = p.trace + (((int64_t)b * k + n) * p.trace_len + j) * 2;
+            tr[0] = own ? p.loop : p.deepest;
+            tr[1] = phys * kPage + (j % kPage);
+          }
+        }
+      }
+      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      mx = xmax4(mx);
+      const float mn = fmaxf(m, mx);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(m - mu);
+      m = mn;
+      float pe[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pe[i] = fast_exp2(x[i] - mu);
+#pragma unroll
+      for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+
+      // ---- O^T += V^T P^T
+      if constexpr (F32) {
+        lsum = fmaf(lsum, alpha, (pe[0] + pe[1]) + (pe[2] + pe[3]));
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+          Raw<16> vr;
+          load_raw<16>(vr, vbase + (uint64_t)(16 * s + n) * kQuad * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = keep[e] ? __uint_as_float(vr.w[e]) : 0.f;
+            acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pe[e], acc[s], 0, 0, 0);
+          }
+        }
+      } else {
+        // P in bf16 for the MFMA; the row sum uses the same rounded weights.
+        const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
+        lsum = fmaf(lsum, alpha, (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23)));
+        const uint32_t pw[2] = {p01, p23};
+        const bool need_mask = !(keep[0] && keep[1] && keep[2] && keep[3]);
+        const uint32_t k01 = (keep[0] ? 0x0000FFFFu : 0u) | (keep[1] ? 0xFFFF0000u : 0u);
+        const uint32_t k23 = (keep[2] ? 0x0000FFFFu : 0u) | (keep[3] ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+          Raw<16> vr;
+          load_raw<16>(vr, vbase + (uint64_t)(32 * s + 2 * n) * kQuad * 2);
+          if (need_mask) {
+            vr.w[0] &= k01;
+            vr.w[1] &= k23;
+            vr.w[2] &= k01;
+            vr.w[3] &= k23;
+          }
+          const uint32_t a0[2] = {vr.w[0], vr.w[1]};
+          const uint32_t a1[2] = {vr.w[2], vr.w[3]};
+          acc[2 * s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a0),
+                                                                 __builtin_bit_cast(bf16x4_t, pw), acc[2 * s], 0, 0, 0);
+          acc[2 * s + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(bf16x4_t, a1), __builtin_bit_cast(bf16x4_t, pw), acc[2 * s + 1], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  lsum = xsum4(lsum);
+
+  // ---- merge the waves of this workgroup through LDS
+  __shared__ float sm_o[WAVES][kMaxBlock][D + 1];
+  __shared__ float sm_m[WAVES][kMaxBlock], sm_l[WAVES][kMaxBlock];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int ch;
+      if constexpr (F32) ch = 16 * a + 4 * g + i;
+      else ch = 32 * (a >> 1) + 2 * (4 * g + i) + (a & 1);
+      sm_o[w][n][ch] = acc[a][i];
+    }
+  if (g == 0) {
+    sm_m[w][n] = m;
+    sm_l[w][n] = lsum;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < k * D; idx += WAVES * 64) {
+    const int qi = idx / D, c = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sm_m[v][qi]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) {
+      const float f = fast_exp2(sm_m[v][qi] - Mu);
+      Ls = fmaf(sm_l[v][qi], f, Ls);
+      O = fmaf(sm_o[v][qi][c], f, O);
+    }
+    const float val = Ls > 0.f ? O / Ls : 0.f;
+    const int64_t row = ((int64_t)b * k + qi) * p.hq + h;
+    if (p.n_splits == 1) {
+      store_out<T>(p.out, row * D + c, val);
+      if (c == 0 && p.lse) p.lse[row] = (Ls > 0.f ? M + fast_log2(Ls) : -INFINITY) * 0.69314718055994531f;
+    } else {
+      float* wsr = p.ws + (row * p.n_splits + split) * (D + 1);
+      wsr[c] = val;
+      if (c == 0) wsr[D] = Ls > 0.f ? M + fast_log2(Ls) : -INFINITY;
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_verify_t(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+  dim3 grid(p.n_splits, p.hq, p.n_rows);
+  if (waves == 2) {
+    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 2, true>), grid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((verify_kernel<T, D, 2, false>), grid, dim3(128), 0, s, p);
+  } else {
+    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 4, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((verify_kernel<T, D, 4, false>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s) {
+  if (p.q_len < 1 || p.q_len > kMaxBlock) return hipErrorInvalidValue;
+  if (waves != 2) waves = 4;
+  if (dtype == 0) {
+    if (head_dim == 64) return launch_verify_t<float, 64>(p, waves, trace, s);
+    if (head_dim == 96) return launch_verify_t<float, 96>(p, waves, trace, s);
+    if (head_dim == 128) return launch_verify_t<float, 128>(p, waves, trace, s);
+  } else {
+    if (head_dim == 64) return launch_verify_t<bf16, 64>(p, waves, trace, s);
+    if (head_dim == 96) return launch_verify_t<bf16, 96>(p, waves, trace, s);
+    if (head_dim == 128) return launch_verify_t<bf16, 128>(p, waves, trace, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lkv

@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "loop-query tokens/s + achieved HBM GB/s (% of MI355X peak), looped-KV attention"
-KERNEL_SOURCES = ["verify_attention_loop_amd/csrc/decode.hip", "verify_attention_loop_amd/csrc/verify.hip",
+KERNEL_SOURCES = ["verify_attention_loop_amd/csrc/decode.hip", "verify_attention_loop_amd/csrc/attn_common.hpp", "verify_attention_loop_amd/csrc/verify.hip",
                   "verify_attention_loop_amd/csrc/cell.hip", "verify_attention_loop_amd/csrc/device.hpp",
                   "verify_attention_loop_amd/csrc/params.hpp"]
 

@@ -56,7 +56,7 @@ def pages_needed(w: synth.Workload, lengths, layers, planes, policy: int, W: int
 
 def build_plain(w: synth.Workload, *, lengths=None, layers=(0,), planes=None, policy=None, window=None,
                 q_len=None, shuffle=None, poison=False, seed=None, extra_pages=0, max_len=None,
-                chunk_tokens=4096, rows=None) -> Built:
+                chunk_tokens=4096, rows=None, max_block=None) -> Built:
     """Cache of a plain (fp32/bf16) workload holding the given layers and planes."""
     import torch
     R = w.n_loops
@@ -73,7 +73,8 @@ def build_plain(w: synth.Workload, *, lengths=None, layers=(0,), planes=None, po
     n_pages = pages_needed(w, lengths, layers, planes, policy, W, q_len) + extra_pages
     cfg = vla.LoopCache.config(n_layers=w.n_layers, n_loops=R, n_heads_q=w.n_heads, n_heads_kv=w.n_heads,
                                head_dim=w.head_dim, kv_dtype=w.dtype, policy=policy, window=W,
-                               max_seqs=len(lengths), max_len=max_len or max(lengths), max_block=max(1, q_len),
+                               max_seqs=len(lengths), max_len=max_len or max(lengths),
+                               max_block=max_block or max(1, q_len),
                                poison=1 if poison else 0, shuffle_seed=(0x5EED + seed) if shuffle else 0)
     cache = vla.LoopCache.on_device(cfg, n_pages)
     dt = torch_dtype(w.dtype)
@@ -114,7 +115,8 @@ def gpu_queries(built: Built, layer: int, loop: int, q_len: int, t0s=None, seed=
     out = torch.empty((len(built.seqs), q_len, w.n_heads, w.head_dim), dtype=torch_dtype(w.dtype), device="cuda")
     for b0 in range(0, len(built.seqs), 64):
         b1 = min(len(built.seqs), b0 + 64)
-        synth.gpu_q(out[b0:b1].data_ptr(), w.dtype, w.seed if seed is None else seed, built.rows[b0:b1],
+        rows = getattr(built, "rows", None) or list(range(len(built.seqs)))
+        synth.gpu_q(out[b0:b1].data_ptr(), w.dtype, w.seed if seed is None else seed, rows[b0:b1],
                     t0s[b0:b1], layer, loop, q_len, w.n_heads, w.head_dim, w.scale,
                     torch.cuda.current_stream().cuda_stream)
     return out
@@ -195,3 +197,123 @@ def algorithmic_bytes_per_call(w: synth.Workload, lengths, q_len: int = 1) -> in
     kv = sum(2 * L * w.n_heads * w.head_dim * es for L in lengths)
     qo = 2 * len(lengths) * q_len * w.n_heads * w.head_dim * es
     return kv + qo
+
+
+# ----------------------------------------------------------------------------- quantised cells
+
+@dataclass
+class BuiltCells:
+    cache: vla.LoopCache
+    w: synth.Workload
+    seqs: list
+    lengths: list
+    layers: list
+    plan: np.ndarray
+
+
+def cell_src_loop(plan, layer: int, loop: int) -> int:
+    """A shared cell reads the final loop's codes (LoopKV page, Sec. 3.2)."""
+    return plan.shape[1] - 1 if plan[layer, loop] == synth.CELL_SHARED else loop
+
+
+def cell_bits(plan, layer: int, loop: int) -> int:
+    return 2 if plan[layer, cell_src_loop(plan, layer, loop)] == synth.CELL_INT2 else 4
+
+
+def build_cells(w: synth.Workload, *, lengths=None, layers=(0,), loops=None, plan=None, seed=None) -> BuiltCells:
+    """LoopKV-style cache: bf16 sink and tail of every cell, and far-history code pages of every
+    non-shared cell, written through lkv_append_plane / lkv_append_coded."""
+    import torch
+    R, H, D = w.n_loops, w.n_heads, w.head_dim
+    seed = w.seed if seed is None else seed
+    lengths = list(lengths) if lengths is not None else [w.length] * w.batch
+    loops = list(loops) if loops is not None else list(range(R))
+    plan = np.array(plan if plan is not None else synth.cell_plan(seed, w.n_layers, R), dtype=np.int8)
+    needed = set()
+    for layer in layers:
+        for r in loops:
+            needed.add((layer, r))
+            needed.add((layer, cell_src_loop(plan, layer, r)))
+    n_near = n4 = n2 = 0
+    for L in lengths:
+        n_far = L - w.sink - w.tail
+        n_cp = (n_far + 31) // 32
+        near_pages = len({0} | set(range((L - w.tail) // 16, (L - 1) // 16 + 1)))
+        for (layer, r) in needed:
+            n_near += near_pages
+            if plan[layer, r] == synth.CELL_INT4:
+                n4 += n_cp
+            elif plan[layer, r] == synth.CELL_INT2:
+                n2 += n_cp
+    cfg = vla.LoopCache.config(n_layers=w.n_layers, n_loops=R, n_heads_q=H, n_heads_kv=H, head_dim=D,
+                               kv_dtype=synth.DT_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=len(lengths),
+                               max_len=max(lengths), max_block=1, quant=1, sink=w.sink, tail=w.tail)
+    cache = vla.LoopCache.on_device(cfg, n_near, n4, n2)
+    cache.lkv_set_plan(plan)
+    st = torch.cuda.current_stream().cuda_stream
+    seqs = []
+    for b, L in enumerate(lengths):
+        s = cache.lkv_add_seq()
+        seqs.append(s)
+        n_far = L - w.sink - w.tail
+        n_cp = (n_far + 31) // 32
+        for (layer, r) in sorted(needed):
+            for (p0, n) in ((0, w.sink), (L - w.tail, w.tail)):
+                if n <= 0:
+                    continue
+                k = torch.empty((n, H, D), dtype=torch.bfloat16, device="cuda")
+                v = torch.empty_like(k)
+                synth.gpu_kv(k.data_ptr(), synth.DT_BF16, seed, synth.T_K, b, layer, r, H, D, p0, n, synth.MODE_PLAIN,
+                             R, w.scale, st)
+                synth.gpu_kv(v.data_ptr(), synth.DT_BF16, seed, synth.T_V, b, layer, r, H, D, p0, n, synth.MODE_PLAIN,
+                             R, w.scale, st)
+                cache.lkv_append_plane(s, layer, r, p0, k, v)
+            if plan[layer, r] == synth.CELL_SHARED:
+                continue
+            bits = 2 if plan[layer, r] == synth.CELL_INT2 else 4
+            kc = torch.empty((n_cp * 32, H, D), dtype=torch.uint8, device="cuda")
+            vc = torch.empty_like(kc)
+            km = torch.empty((n_cp, H, D, 2), dtype=torch.int16, device="cuda")
+            vm = torch.empty((n_cp * 32, H, D // 32, 2), dtype=torch.int16, device="cuda")
+            synth.gpu_codes(kc.data_ptr(), seed, synth.T_KCODE, b, layer, r, H, D, w.sink, n_cp * 32, bits, st)
+            synth.gpu_codes(vc.data_ptr(), seed, synth.T_VCODE, b, layer, r, H, D, w.sink, n_cp * 32, bits, st)
+            synth.gpu_meta(km.data_ptr(), seed, 0, b, layer, r, H, D, 0, n_cp, bits, st)
+            synth.gpu_meta(vm.data_ptr(), seed, 1, b, layer, r, H, D // 32, 0, n_cp * 32, bits, st)
+            cache.lkv_append_coded(s, layer, r, 0, n_cp, kc, km, vc, vm)
+        torch.cuda.synchronize()
+    return BuiltCells(cache, w, seqs, lengths, list(layers), plan)
+
+
+def cell_oracle_row(bc: BuiltCells, b: int, layer: int, loop: int, h: int, thr_offset: float, seed=None):
+    """Oracle inputs of one cell row from the generator, and the oracle's (out, lse, hot bits, scores)."""
+    import oracle
+    w = bc.w
+    seed = w.seed if seed is None else seed
+    L = bc.lengths[b]
+    D = w.head_dim
+    n_far = L - w.sink - w.tail
+    n_cp = (n_far + 31) // 32
+    src = cell_src_loop(bc.plan, layer, loop)
+    bits = cell_bits(bc.plan, layer, loop)
+    kind = {synth.CELL_INT4: oracle.CELL_INT4, synth.CELL_INT2: oracle.CELL_INT2,
+            synth.CELL_SHARED: oracle.CELL_SHARED}[int(bc.plan[layer, loop])]
+    kn = np.zeros((L, D))
+    vn = np.zeros((L, D))
+    for (p0, n) in ((0, w.sink), (L - w.tail, w.tail)):
+        kn[p0:p0 + n] = to_f64(synth.kv(synth.DT_BF16, seed, synth.T_K, b, layer, loop, w.n_heads, D, p0, n,
+                                        heads=[h])[:, 0], synth.DT_BF16)
+        vn[p0:p0 + n] = to_f64(synth.kv(synth.DT_BF16, seed, synth.T_V, b, layer, loop, w.n_heads, D, p0, n,
+                                        heads=[h])[:, 0], synth.DT_BF16)
+    kc = synth.codes(seed, synth.T_KCODE, b, layer, src, w.n_heads, D, w.sink, n_far, bits, heads=[h])[:, 0]
+    vc = synth.codes(seed, synth.T_VCODE, b, layer, src, w.n_heads, D, w.sink, n_far, bits, heads=[h])[:, 0]
+    km = synth.f64_from_f16(synth.meta(seed, 0, b, layer, src, w.n_heads, D, 0, n_cp, bits, heads=[h])[:, 0])
+    vm = synth.f64_from_f16(synth.meta(seed, 1, b, layer, src, w.n_heads, D // 32, 0, n_far, bits, heads=[h])[:, 0])
+    q = cpu_query(w, b, layer, loop, h, L - 1, seed=seed)
+    out, lse, hot, n_cold = oracle.cell_row(q, kn, vn, kc, km[..., 0], km[..., 1], vc, vm[..., 0], vm[..., 1],
+                                            w.sink, w.tail, kind, thr_offset)
+    # scores of far tokens and the threshold (only to place the rounding band of the mask comparison)
+    g = np.arange(n_far) // 32
+    kh = km[g, :, 1] + km[g, :, 0] * kc
+    s_far = kh @ q / np.sqrt(D)
+    m0 = (kn[:w.sink] @ q / np.sqrt(D)).max()
+    return out, lse, hot, s_far, m0 - thr_offset

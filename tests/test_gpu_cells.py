@@ -1,0 +1,119 @@
+"""GPU parity of LoopKV-style quantised cells (INT4 / INT2 / shared; bit-plane V with the
+fixed hot rule s >= m0 - offset) through the C-ABI against the fp64 oracle.
+
+Outputs: max-abs 2e-2 (bf16 out).  Hot masks: bit-exact for every far token whose score
+lies outside a 1e-4 band around the threshold (both sides compute the score in a
+different rounding order; inside the band either bit is accepted and counted)."""
+import math
+
+import numpy as np
+import pytest
+
+import harness
+import synth
+import verify_attention_loop_amd as vla
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+BAND = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    vla.load()
+
+
+def _cells_wl(batch=3):
+    return synth.Workload("cells", batch, 2, 4, 2, 128, 1000, synth.DT_BF16, "full", 0, 1, 16, synth.MODE_PLAIN,
+                          1.0, quant=True, sink=4, tail=128)
+
+
+def _attend_cells(bc, layer, loop, offset, split_k=0):
+    w = bc.w
+    n = len(bc.seqs)
+    q = harness.gpu_queries(bc, layer, loop, 1)
+    out = torch.empty_like(q)
+    lse = torch.empty((n, 1, w.n_heads), dtype=torch.float32, device="cuda")
+    max_far = max(bc.lengths) - w.sink - w.tail
+    words = (max_far + 31) // 32
+    mask = torch.empty((n, w.n_heads, words), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(4, bc.cache.lkv_workspace_bytes(layer, loop, bc.seqs, split_k=split_k)) + (1 << 20),
+                     dtype=torch.uint8, device="cuda")
+    bc.cache.lkv_attend(layer, loop, bc.seqs, q, out, split_k=split_k, v_thresh_offset=offset, lse=lse,
+                        workspace=ws, mask_trace=mask)
+    torch.cuda.synchronize()
+    return harness.out_f64(out), lse.cpu().numpy(), mask.cpu().numpy().view(np.uint32)
+
+
+def _bits(words, n_far):
+    b = np.unpackbits(words.view(np.uint8), bitorder="little")
+    return b[:n_far]
+
+
+PLAN = np.array([[synth.CELL_INT4, synth.CELL_INT2, synth.CELL_SHARED, synth.CELL_INT4],
+                 [synth.CELL_SHARED, synth.CELL_INT4, synth.CELL_INT2, synth.CELL_INT4]], dtype=np.int8)
+
+
+@pytest.mark.parametrize("offset", [4.0, 1.0, math.inf, -math.inf])
+def test_cells_every_kind(offset):
+    """Ragged lengths (133 = sink + tail + 1: one far token; a partial last code page; 1000), every cell kind,
+    offsets 4 (the workload's rule), 1 (many cold tokens), +inf (all hot), -inf (all cold)."""
+    w = _cells_wl()
+    lengths = [133, 300, 1000]
+    bc = harness.build_cells(w, lengths=lengths, layers=(0, 1), plan=PLAN)
+    band_hits = 0
+    for layer in (0, 1):
+        for loop in range(4):
+            for split_k in (1, 3):
+                out, lse, mask = _attend_cells(bc, layer, loop, offset, split_k)
+                assert np.isfinite(out).all()
+                for b, L in enumerate(lengths):
+                    n_far = L - w.sink - w.tail
+                    for h in range(w.n_heads):
+                        want, want_lse, hot, s_far, thr = harness.cell_oracle_row(bc, b, layer, loop, h, offset)
+                        err = np.abs(out[b, 0, h] - want).max()
+                        assert err <= TOL, (layer, loop, split_k, b, h, err)
+                        assert abs(lse[b, 0, h] - want_lse) <= 1e-2
+                        got = _bits(mask[b, h], n_far)
+                        near = np.abs(s_far - thr) <= BAND if np.isfinite(thr) else np.zeros(n_far, bool)
+                        assert np.array_equal(got[~near], hot[~near]), (layer, loop, b, h)
+                        band_hits += int(near.sum())
+    assert band_hits < 5
+    bc.cache.close()
+
+
+def test_all_hot_cell_reads_full_int4_codes_bitwise_equal_to_negative_infinite_threshold():
+    """LoopKV page, App. I: with the threshold at -inf (every token hot) the reader equals the plain reader
+    of both V planes; the same kernel with any offset >= the whole score range gives the same bits."""
+    w = _cells_wl(2)
+    bc = harness.build_cells(w, lengths=[500, 700], layers=(0,), plan=PLAN)
+    a, _, ma = _attend_cells(bc, 0, 0, math.inf, 2)
+    b, _, mb = _attend_cells(bc, 0, 0, 1e9, 2)
+    assert np.array_equal(a, b) and np.array_equal(ma, mb)
+    bc.cache.close()
+
+
+@pytest.mark.slow
+def test_loopkv_full_shape_sampled():
+    """The LoopKV-shaped workload at full length: 16 sequences, L = 16384 (sink 4, far 16252, tail 128),
+    16 heads x 128, seeded plan over layer 0's four loops; sampled rows and their masks."""
+    w = synth.WORKLOADS["loopkv_cells"]
+    plan = synth.cell_plan(w.seed, w.n_layers, w.n_loops)
+    bc = harness.build_cells(w, layers=(0,), plan=plan)
+    rng = np.random.default_rng(4)
+    n_far = w.length - w.sink - w.tail
+    for loop in range(w.n_loops):
+        out, lse, mask = _attend_cells(bc, 0, loop, 4.0)
+        assert np.isfinite(out).all()
+        for _ in range(4):
+            b, h = int(rng.integers(w.batch)), int(rng.integers(w.n_heads))
+            want, want_lse, hot, s_far, thr = harness.cell_oracle_row(bc, b, 0, loop, h, 4.0)
+            assert np.abs(out[b, 0, h] - want).max() <= TOL
+            got = _bits(mask[b, h], n_far)
+            near = np.abs(s_far - thr) <= BAND
+            assert np.array_equal(got[~near], hot[~near])
+    bc.cache.close()

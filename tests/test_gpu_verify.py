@@ -151,7 +151,8 @@ def test_draft_step(policy, W, D):
     w = _wl(D)
     n_cached = [30, 64, 200]
     dl = 4
-    built = harness.build_plain(w, lengths=n_cached, policy=policy, window=W, q_len=1, shuffle=True, poison=True)
+    built = harness.build_plain(w, lengths=n_cached, policy=policy, window=W, q_len=1, shuffle=True, poison=True,
+                                max_block=8)
     for loop in (0, 3):
         dk, dv = _draft_inputs(w, 3, 0, loop, n_cached, dl, built.rows)
         q = harness.gpu_queries(built, 0, loop, 1, t0s=[n + dl - 1 for n in n_cached])

@@ -15,6 +15,7 @@
 // row (one token-head) is never requested at all (LoopKV page, Sec. 3.3).
 #include <hip/hip_runtime.h>
 
+#include "attn_common.hpp"
 #include "device.hpp"
 #include "params.hpp"
 
@@ -86,12 +87,273 @@ hipError_t launch_pack_codes(uint8_t* page, const void* k_codes, const void* k_m
   return hipGetLastError();
 }
 
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ float crumb(uint32_t w, int c) { return (float)((w >> (2 * c)) & 3u); }
+__device__ __forceinline__ float nibble(uint32_t w, int c) { return (float)((w >> (4 * c)) & 15u); }
+
+__device__ __forceinline__ uint32_t or4(uint32_t v) {
+  v |= (uint32_t)__shfl_xor((int)v, 16);
+  v |= (uint32_t)__shfl_xor((int)v, 32);
+  return v;
+}
+
+// One launch per cell: grid.x = n_splits far blocks + 1 near block.
+//   near block: exact bf16 attention over the sink [0, sink) and the tail
+//     [L - tail, L) of the cell's own loop (LoopKV page, Sec. 3.2: sink and window
+//     stay the cell's own and exact);
+//   far block c: its share of the code pages of the cell's source (own codes, or
+//     the final loop's for a shared cell).  Per page the K scale is folded into q
+//     and q.z into a bias (LoopKV page, App. E), so a score is bias + sum q'_c c_jc.
+//     The seed m0 is the largest sink score, recomputed by every far block from
+//     the 4 sink keys (no wait on another block); a far token is hot iff
+//     s_j >= m0 - offset.  V: hot tokens read both bit planes (4 hi + lo), cold
+//     tokens only hi and take the bucket midpoint 4 hi + 1.5; the per-token V
+//     scale and zero fold into the weight p_j (LoopKV page, Sec. 3.3, App. E Alg. 1).
+// Each DPP row keeps its own online softmax; partials go to the workspace and
+// the LSE merge kernel combines them.
+template <int WAVES, bool TRACE>
+__global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
+  constexpr int D = 128, E = 8;
+  constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
+  const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int g = lane >> 4, li = lane & 15;
+  const int hk = h / (p.hq / p.hkv);
+  const int slot = p.slot[b];
+  const int L = p.len[b];
+  const int n_far = L - p.sink - p.tail;
+  const int tail_lo = L - p.tail;
+
+  float qf[E];
+  uint32_t qw[E / 2];
+  {
+    Raw<16> r;
+    load_raw<16>(r, reinterpret_cast<const uint8_t*>(p.q) + (((int64_t)b * p.hq + h) * D + li * E) * 2);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      qw[x] = r.w[x];
+      qf[2 * x] = bf_lo(r.w[x]);
+      qf[2 * x + 1] = bf_hi(r.w[x]);
+    }
+  }
+  const int32_t* tab_near = p.tab_near + (int64_t)slot * p.ring_near;
+  const uint64_t koff = (uint64_t)hk * HEADB + (uint64_t)li * 16;
+  const uint64_t voff = (uint64_t)p.hkv * HEADB + (uint64_t)hk * HEADB + (uint64_t)g * (kQuad * D * 2) + li * 64;
+
+  Softmax st{-INFINITY, 0.f};
+  float o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  float zacc = 0.f;
+
+  if (part == p.n_splits) {
+    // ---------------- near block: sink and tail, bf16, own loop
+    const int np_sink = (p.sink + kPage - 1) / kPage;
+    const int tp0 = max(np_sink, tail_lo / kPage), tp1 = (L - 1) / kPage;
+    const int count = np_sink + (p.tail > 0 ? max(0, tp1 - tp0 + 1) : 0);
+    for (int k = w; k < count; k += WAVES) {
+      const int pg = k < np_sink ? k : tp0 + (k - np_sink);
+      const uint8_t* base = p.pool + (uint64_t)tab_near[pg] * p.page_bytes;
+      Raw<16> kr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_raw<16>(kr[i], base + koff + (uint64_t)(4 * g + i) * (D * 2));
+      Raw<64> vr;
+      load_raw<64>(vr, base + voff);
+      bool zero[4], none[4] = {false, false, false, false};
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = pg * kPage + 4 * g + i;
+        const bool valid = j < p.sink || (j >= tail_lo && j < L);
+        zero[i] = !valid;
+        float s = 0.f;
+#pragma unroll
+        for (int x2 = 0; x2 < 4; ++x2) s = dot2_bf16(qw[x2], kr[i].w[x2], s);
+        s = row_sum16(s) * p.scale_log2;
+        x[i] = valid ? s : -INFINITY;
+      }
+      blend_quad<bf16, D>(vr, vr, none, zero);
+      softmax_step<E, 4>(st, o, x);
+      accum_quad<bf16, D>(o, vr, x);
+    }
+  } else {
+    // ---------------- far block
+    // seed m0: largest exact sink score (natural-log units)
+    float m0 = -INFINITY;
+    {
+      const uint8_t* base = p.pool + (uint64_t)tab_near[0] * p.page_bytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * g + i;
+        if (j < p.sink) {  // uniform per DPP row
+          Raw<16> kr;
+          load_raw<16>(kr, base + koff + (uint64_t)j * (D * 2));
+          float s = 0.f;
+#pragma unroll
+          for (int x2 = 0; x2 < 4; ++x2) s = dot2_bf16(qw[x2], kr.w[x2], s);
+          m0 = fmaxf(m0, row_sum16(s) * p.scale);
+        }
+      }
+      m0 = fmaxf(m0, __shfl_xor(m0, 16));
+      m0 = fmaxf(m0, __shfl_xor(m0, 32));
+    }
+    const float thr = m0 - p.thr_offset;
+    const bool masked = p.masked != 0;
+    const int n_cp = (n_far + kCodePage - 1) / kCodePage;
+    const int c0 = (int)((int64_t)part * n_cp / p.n_splits);
+    const int c1 = (int)((int64_t)(part + 1) * n_cp / p.n_splits);
+    const int32_t* tab_code = p.tab_code + (int64_t)slot * p.code_ring;
+    const uint64_t head_bytes = (uint64_t)(p.bits == 4 ? 40 : 24) * D;
+    const uint64_t vcode_off = p.bits == 4 ? 20 * D : 12 * D;
+    const uint64_t vmeta_off = p.bits == 4 ? 36 * D : 20 * D;
+    for (int cp = c0 + w; cp < c1; cp += WAVES) {
+      const uint8_t* hb = p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes;
+      // K meta of this lane's 8 channels -> q' = q * scale, bias = q . zero
+      Raw<32> km;
+      load_raw<32>(km, hb + li * 32);
+      float qs[E], bias = 0.f;
+#pragma unroll
+      for (int c = 0; c < E; ++c) {
+        qs[c] = qf[c] * f16_to_f32(km.w[c] & 0xFFFFu);
+        bias = fmaf(qf[c], f16_to_f32(km.w[c] >> 16), bias);
+      }
+      // K codes -> scores of tokens g + 4i
+      float ps[8];
+      if (p.bits == 4) {
+        Raw<16> k0, k1;
+        load_raw<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
+        load_raw<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t wd = i < 4 ? k0.w[i] : k1.w[i - 4];
+          float s = bias;
+#pragma unroll
+          for (int c = 0; c < E; ++c) s = fmaf(qs[c], nibble(wd, c), s);
+          ps[i] = s;
+        }
+      } else {
+        Raw<16> kk;
+        load_raw<16>(kk, hb + 4 * D + (g * 16 + li) * 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t hw = (kk.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+          float s = bias;
+#pragma unroll
+          for (int c = 0; c < E; ++c) s = fmaf(qs[c], crumb(hw, c), s);
+          ps[i] = s;
+        }
+      }
+      float x[8];
+      bool hot[8], valid[8];
+      uint32_t hotbits = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float ssum = row_sum16(ps[i]);
+        valid[i] = cp * kCodePage + g + 4 * i < n_far;
+        hot[i] = valid[i] && (!masked || ssum * p.scale >= thr);
+        x[i] = valid[i] ? ssum * p.scale_log2 : -INFINITY;
+        if (hot[i]) hotbits |= 1u << (g + 4 * i);
+      }
+      // online softmax of this row (x[] becomes p_j)
+      float mn = st.m;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mn = fmaxf(mn, x[i]);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(st.m - mu);
+      float add = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = fast_exp2(x[i] - mu);
+        add += x[i];
+      }
+      st.l = fmaf(st.l, alpha, add);
+      st.m = mn;
+#pragma unroll
+      for (int c = 0; c < E; ++c) o[c] *= alpha;
+      zacc *= alpha;
+      // V meta of the lane's group for its 8 tokens; fold scale and zero into the weights
+      Raw<32> vm;
+      load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
+      float wgt[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float sg = f16_to_f32(vm.w[i] & 0xFFFFu), zz = f16_to_f32(vm.w[i] >> 16);
+        wgt[i] = valid[i] ? x[i] * sg : 0.f;
+        const float zc = valid[i] ? x[i] * zz : 0.f;
+        zacc += (masked && valid[i] && !hot[i]) ? fmaf(1.5f, wgt[i], zc) : zc;
+      }
+      // V hi plane (INT4) or V codes (INT2)
+      Raw<16> vh;
+      load_raw<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t hw = (vh.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        const float coef = masked ? 4.f * wgt[i] : wgt[i];
+#pragma unroll
+        for (int c = 0; c < E; ++c) o[c] = fmaf(coef, crumb(hw, c), o[c]);
+      }
+      // V lo plane: fetched for hot tokens only
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (hot[i]) {
+            const uint32_t lo = *reinterpret_cast<const uint16_t*>(hb + 28 * D + (g + 4 * i) * 32 + li * 2);
+#pragma unroll
+            for (int c = 0; c < E; ++c) o[c] = fmaf(wgt[i], crumb(lo, c), o[c]);
+          }
+        }
+      }
+      if constexpr (TRACE) {
+        const uint32_t word = or4(hotbits);
+        if (lane == 0 && p.mask_trace) p.mask_trace[((int64_t)b * p.hq + h) * p.mask_words + cp] = word;
+      }
+    }
+  }
+
+  // merge the 4 * WAVES row states
+  __shared__ float sm_o[WAVES * 4][D];
+  __shared__ float sm_m[WAVES * 4], sm_l[WAVES * 4];
+  const int r = w * 4 + g;
+#pragma unroll
+  for (int e = 0; e < E; ++e) sm_o[r][li * E + e] = o[e] + zacc;
+  if (li == 0) {
+    sm_m[r] = st.m;
+    sm_l[r] = st.l;
+  }
+  __syncthreads();
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < WAVES * 4; ++k) M = fmaxf(M, sm_m[k]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float Lsum = 0.f;
+#pragma unroll
+  for (int k = 0; k < WAVES * 4; ++k) Lsum += sm_l[k] * fast_exp2(sm_m[k] - Mu);
+  const int64_t row = (int64_t)b * p.hq + h;
+  float* wsr = p.ws + (row * (p.n_splits + 1) + part) * (D + 1);
+  for (int c = threadIdx.x; c < D; c += WAVES * 64) {
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < WAVES * 4; ++k) acc += sm_o[k][c] * fast_exp2(sm_m[k] - Mu);
+    wsr[c] = Lsum > 0.f ? acc / Lsum : 0.f;
+  }
+  if (threadIdx.x == 0) wsr[D] = Lsum > 0.f ? M + fast_log2(Lsum) : -INFINITY;
+}
+
 hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s) {
-  (void)p;
-  (void)head_dim;
-  (void)waves;
-  (void)s;
-  return hipErrorNotSupported;
+  if (head_dim != 128 || p.sink > kPage) return hipErrorInvalidValue;
+  dim3 grid(p.n_splits + 1, p.hq, p.n_rows);
+  const bool trace = p.mask_trace != nullptr;
+  if (waves == 2) {
+    if (trace) hipLaunchKernelGGL((cell_kernel<2, true>), grid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((cell_kernel<2, false>), grid, dim3(128), 0, s, p);
+  } else {
+    if (trace) hipLaunchKernelGGL((cell_kernel<4, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((cell_kernel<4, false>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace lkv

@@ -18,114 +18,11 @@
 // page costs one extra V quad load on that page only.
 #include <hip/hip_runtime.h>
 
+#include "attn_common.hpp"
 #include "device.hpp"
 #include "params.hpp"
 
 namespace lkv {
-
-template <typename T, int D>
-struct DecodeTile {
-  static constexpr int ES = sizeof(T) == 4 ? 4 : 2;
-  static constexpr int E = D / 16;
-  static constexpr int KB = E * ES;          // K bytes per lane per token
-  static constexpr int VB = kQuad * E * ES;  // V bytes per lane per quad
-  static constexpr int HEAD = kPage * D * ES;
-};
-
-// Partial score of one token: this lane's channels.
-template <typename T, int D>
-__device__ __forceinline__ float partial_dot(const Raw<DecodeTile<T, D>::KB>& k, const float* qf,
-                                             const uint32_t* qw) {
-  constexpr int E = D / 16;
-  float s = 0.f;
-  if constexpr (sizeof(T) == 4) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) s = fmaf(qf[e], __uint_as_float(k.w[e]), s);
-  } else {
-#pragma unroll
-    for (int w = 0; w < E / 2; ++w) s = dot2_bf16(qw[w], k.w[w], s);
-  }
-  return s;
-}
-
-// o[e] += sum_k p[k] * v(channel e, token k) for this lane's quad block.
-template <typename T, int D>
-__device__ __forceinline__ void accum_quad(float* o, const Raw<DecodeTile<T, D>::VB>& v, const float* p) {
-  constexpr int E = D / 16;
-  if constexpr (sizeof(T) == 4) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float a = o[e];
-      a = fmaf(p[0], __uint_as_float(v.w[4 * e + 0]), a);
-      a = fmaf(p[1], __uint_as_float(v.w[4 * e + 1]), a);
-      a = fmaf(p[2], __uint_as_float(v.w[4 * e + 2]), a);
-      a = fmaf(p[3], __uint_as_float(v.w[4 * e + 3]), a);
-      o[e] = a;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      float a = o[e];
-      a = fmaf(p[0], bf_lo(v.w[2 * e + 0]), a);
-      a = fmaf(p[1], bf_hi(v.w[2 * e + 0]), a);
-      a = fmaf(p[2], bf_lo(v.w[2 * e + 1]), a);
-      a = fmaf(p[3], bf_hi(v.w[2 * e + 1]), a);
-      o[e] = a;
-    }
-  }
-}
-
-// Per-token select between two quad blocks: token k taken from `b` where take_b[k].
-// Tokens with zero[k] are cleared (keys beyond the sequence: their slots may hold NaN).
-template <typename T, int D>
-__device__ __forceinline__ void blend_quad(Raw<DecodeTile<T, D>::VB>& a, const Raw<DecodeTile<T, D>::VB>& b,
-                                           const bool* take_b, const bool* zero) {
-  constexpr int E = D / 16;
-  if constexpr (sizeof(T) == 4) {
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t x = take_b[k] ? b.w[4 * e + k] : a.w[4 * e + k];
-        a.w[4 * e + k] = zero[k] ? 0u : x;
-      }
-  } else {
-    const uint32_t sel01 = (take_b[0] ? 0x0000FFFFu : 0u) | (take_b[1] ? 0xFFFF0000u : 0u);
-    const uint32_t sel23 = (take_b[2] ? 0x0000FFFFu : 0u) | (take_b[3] ? 0xFFFF0000u : 0u);
-    const uint32_t keep01 = (zero[0] ? 0u : 0x0000FFFFu) | (zero[1] ? 0u : 0xFFFF0000u);
-    const uint32_t keep23 = (zero[2] ? 0u : 0x0000FFFFu) | (zero[3] ? 0u : 0xFFFF0000u);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      a.w[2 * e + 0] = ((b.w[2 * e + 0] & sel01) | (a.w[2 * e + 0] & ~sel01)) & keep01;
-      a.w[2 * e + 1] = ((b.w[2 * e + 1] & sel23) | (a.w[2 * e + 1] & ~sel23)) & keep23;
-    }
-  }
-}
-
-struct Softmax {
-  float m;  // running max, base-2 units
-  float l;
-};
-
-// Online softmax update of one DPP row with NT new base-2 logits x[].
-template <int E, int NT>
-__device__ __forceinline__ void softmax_step(Softmax& st, float* o, float* x) {
-  float mn = st.m;
-#pragma unroll
-  for (int i = 0; i < NT; ++i) mn = fmaxf(mn, x[i]);
-  const float mu = (mn == -INFINITY) ? 0.f : mn;
-  const float alpha = fast_exp2(st.m - mu);
-  float add = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    x[i] = fast_exp2(x[i] - mu);
-    add += x[i];
-  }
-  st.l = fmaf(st.l, alpha, add);
-  st.m = mn;
-#pragma unroll
-  for (int e = 0; e < E; ++e) o[e] *= alpha;
-}
 
 template <typename T, int D, int WAVES, bool TRACE>
 __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p) {

@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -110,14 +111,21 @@ def cpu_baseline(w, seconds: float):
 
 
 def read_traffic(workload: str, khash: str):
-    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """HBM bytes per launch of the attention kernel from the rocprofv3 counter summary of this workload
+    (profiles/traffic_<workload>.txt: FETCH_SIZE + WRITE_SIZE per dispatch, scaled by the same counters
+    read on a plain device copy of known size).  None when absent or taken on other kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(p):
         return None
+    kv = {}
     with open(p) as fh:
-        t = json.load(fh)
-    if t.get("kernel_hash") != khash:
+        for line in fh:
+            m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_hash") != khash or "bytes_per_launch" not in kv:
         return None
-    return t.get("bytes_per_launch")
+    return int(float(kv["bytes_per_launch"]))
 
 
 def main():
@@ -200,7 +208,10 @@ def main():
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
         for _ in range(3):
-            b.copy_(a)
+            b.copy_(a)  # device-to-device blit: reads 1 GiB, writes 1 GiB
+        af, bf = a.view(torch.float32), b.view(torch.float32)
+        for _ in range(3):
+            torch.mul(af, 1.0, out=bf)  # elementwise kernel: reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
 
     cpu = None

@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "loop-query tokens/s + achieved HBM GB/s (% of MI355X peak), looped-KV attention"
-KERNEL_SOURCES = ["verify_attention_loop_amd/csrc/decode.hip", "verify_attention_loop_amd/csrc/attn_common.hpp", "verify_attention_loop_amd/csrc/verify.hip",
+KERNEL_SOURCES = ["verify_attention_loop_amd/csrc/decode.hip", "verify_attention_loop_amd/csrc/attn_common.hpp",
+                  "verify_attention_loop_amd/csrc/verify.hip", "verify_attention_loop_amd/csrc/copy.hip",
                   "verify_attention_loop_amd/csrc/cell.hip", "verify_attention_loop_amd/csrc/device.hpp",
                   "verify_attention_loop_amd/csrc/params.hpp"]
 
@@ -128,6 +129,36 @@ def read_traffic(workload: str, khash: str):
     return int(float(kv["bytes_per_launch"]))
 
 
+def cpu_baseline_cells(bc, seconds: float):
+    """The fp64 oracle's cell routine, as it stands, on a bounded sample of the quantised-cell workload:
+    rows (seq, layer 0, loop, head) of every loop with inputs regenerated on the host (not timed), repeated
+    until `seconds` of oracle time accumulate."""
+    import numpy as np
+
+    import harness
+    import oracle
+
+    w = bc.w
+    rng = np.random.default_rng(0)
+    rows = []
+    for i in range(8):
+        b, h, r = int(rng.integers(w.batch)), int(rng.integers(w.n_heads)), i % w.n_loops
+        rows.append(harness.cell_inputs(bc, b, 0, r, h))
+    done, elapsed = 0, 0.0
+    while elapsed < seconds:
+        for a in rows:
+            t1 = time.perf_counter()
+            oracle.cell_row(a["q"], a["k_near"], a["v_near"], a["kc"], a["ks"], a["kz"], a["vc"], a["vs"], a["vz"],
+                            a["sink"], a["tail"], a["kind"], 4.0)
+            elapsed += time.perf_counter() - t1
+            done += 1
+    rows_per_token = w.n_layers * w.n_heads
+    return {"value": done / elapsed / rows_per_token, "unit": "loop-query tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} cell rows ({len(rows)} distinct (seq, layer 0, loop, head) rows of the {w.name} "
+                      f"workload, L={w.length}, repeated) in {elapsed:.1f} s of fp64 oracle time on one thread; "
+                      f"{rows_per_token} rows = 1 loop-query token"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -144,35 +175,59 @@ def main():
     vla.load()
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
-    if args.workload not in ("huginn_ripe", "ouro_splitk", "huginn_verify"):
-        print(f"workload {args.workload}: not benchmarked by this script", file=sys.stderr)
-        sys.exit(2)
     t_setup = time.perf_counter()
-    built, layers = build_workload(w, args)
-    cache = built.cache
     R, B, q_len = w.n_loops, w.batch, w.q_len
-    mode = vla.MODE_VERIFY if q_len > 1 else vla.MODE_DECODE
     split = w.split_k if args.split_k < 0 else args.split_k
+    layers = list(range(w.n_layers if args.layers <= 0 else min(args.layers, w.n_layers)))
+    if w.quant:
+        built = harness.build_cells(w, layers=layers)
+        mode = vla.MODE_DECODE
+        kernel = "cell_kernel"
+    else:
+        built, layers = build_workload(w, args)
+        mode = vla.MODE_VERIFY if q_len > 1 else vla.MODE_DECODE
+        kernel = "decode_kernel" if mode == vla.MODE_DECODE else "verify_kernel"
+    cache = built.cache
     n_layers_step = w.n_layers
     # Queries and outputs of every (layer, loop) call of a step, resident in HBM.
+    calls = [(layer, loop) for loop in range(R) for layer in range(n_layers_step)]
     qs, outs = {}, {}
-    for loop in range(R):
-        for layer in range(n_layers_step):
-            src_layer = layers[layer % len(layers)]
-            qs[(layer, loop)] = harness.gpu_queries(built, src_layer, loop, q_len)
-            outs[(layer, loop)] = torch.empty_like(qs[(layer, loop)])
+    for (layer, loop) in calls:
+        src_layer = layers[layer % len(layers)]
+        qs[(layer, loop)] = harness.gpu_queries(built, src_layer, loop, q_len)
+        outs[(layer, loop)] = torch.empty_like(qs[(layer, loop)])
     ws_bytes = cache.lkv_workspace_bytes(0, 0, built.seqs, q_len=q_len, mode=mode, split_k=split)
     ws = torch.empty(max(4, ws_bytes), dtype=torch.uint8, device="cuda")
+    extra = {"v_thresh_offset": 4.0} if w.quant else {}
+
+    # Algorithmic bytes of each call.  Quantised cells skip the V lo plane of cold tokens, so one untimed
+    # pass with the hot-mask trace counts them first.
+    if w.quant:
+        n_far = [L - w.sink - w.tail for L in built.lengths]
+        words = (max(n_far) + 31) // 32
+        mask = torch.empty((len(built.seqs), w.n_heads, words), dtype=torch.int32, device="cuda")
+        valid = torch.zeros((len(built.seqs), 1, words * 32), dtype=torch.bool)
+        for b, nf in enumerate(n_far):
+            valid[b, 0, :nf] = True
+        call_bytes = []
+        for (layer, loop) in calls:
+            src_layer = layers[layer % len(layers)]
+            cache.lkv_attend(src_layer, loop, built.seqs, qs[(layer, loop)], outs[(layer, loop)], split_k=split,
+                             workspace=ws, mask_trace=mask, **extra)
+            bits = np.unpackbits(mask.cpu().numpy().view(np.uint8), bitorder="little").reshape(
+                len(built.seqs), w.n_heads, words * 32).astype(bool)
+            n_cold = int((~bits & valid.numpy()).sum())
+            call_bytes.append(harness.cell_bytes_per_call(built, src_layer, loop, n_cold))
+    else:
+        call_bytes = [harness.algorithmic_bytes_per_call(w, built.lengths, q_len)] * len(calls)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    calls = [(layer, loop) for loop in range(R) for layer in range(n_layers_step)]
-
     def step(events=None):
         for n, (layer, loop) in enumerate(calls):
-            kw = {}
+            kw = dict(extra)
             if events is not None:
-                kw = {"ev_begin": events[2 * n].cuda_event, "ev_end": events[2 * n + 1].cuda_event}
+                kw.update(ev_begin=events[2 * n].cuda_event, ev_end=events[2 * n + 1].cuda_event)
             cache.lkv_attend(layers[layer % len(layers)], loop, built.seqs, qs[(layer, loop)], outs[(layer, loop)],
                              q_len=q_len, mode=mode, split_k=split, workspace=ws, **kw)
 
@@ -199,8 +254,9 @@ def main():
 
     tokens_per_step = B * q_len * R
     value = tokens_per_step / (ms_per_step / 1e3)
-    alg_bytes = harness.algorithmic_bytes_per_call(w, built.lengths, q_len)
-    achieved = alg_bytes / (mean_launch_ms / 1e3) / 1e9
+    alg_bytes = float(np.mean(call_bytes))
+    # achieved = algorithmic bytes of all timed launches / their summed duration
+    achieved = float(np.sum(call_bytes)) * args.steps / (kern_ms.sum() / 1e3) / 1e9
     khash = kernel_hash()
     traffic = read_traffic(args.workload, khash)
 
@@ -216,8 +272,25 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline_cells(built, args.cpu_seconds) if w.quant else cpu_baseline(w, args.cpu_seconds)
 
+    if w.quant:
+        dtype = "int4/int2 codes + bf16 near, fp32 accumulate"
+        data = "synthetic (seeded counter-hash generator: binomial codes, fp16 metadata, seeded cell plan)"
+    else:
+        dtype = "bf16" if w.dtype == synth.DT_BF16 else "f32"
+        data = ("synthetic (seeded counter-hash generator; Huginn-shaped ripening planes)"
+                if w.mode == synth.MODE_RIPEN else "synthetic (seeded counter-hash generator)")
+    cfg = {"workload": w.name, "batch": B, "core_layers": w.n_layers, "loops": R, "heads": w.n_heads,
+           "head_dim": w.head_dim, "context": w.length, "q_len": q_len, "policy": w.policy, "window": w.window,
+           "page_tokens": 32 if w.quant else 16, "split_k": split, "calls_per_step": len(calls),
+           "layers_resident": len(layers), "kernel_ms_per_step": round(float(kern_ms.sum(axis=1).mean()), 4),
+           "setup_s": round(setup_s, 1)}
+    if w.quant:
+        cfg.update(sink=w.sink, tail=w.tail, v_thresh="m0 - 4.0",
+                   plan={k: int((built.plan == v).sum()) for k, v in (("int4", synth.CELL_INT4),
+                                                                      ("int2", synth.CELL_INT2),
+                                                                      ("shared", synth.CELL_SHARED))})
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -229,22 +302,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == synth.DT_BF16 else "f32",
-        "data": "synthetic (seeded counter-hash generator; Huginn-shaped ripening planes)"
-        if w.mode == synth.MODE_RIPEN else "synthetic (seeded counter-hash generator)",
-        "config": {
-            "workload": w.name, "batch": B, "core_layers": w.n_layers, "loops": R, "heads": w.n_heads,
-            "head_dim": w.head_dim, "context": w.length, "q_len": q_len,
-            "policy": w.policy, "window": w.window, "page_tokens": 16, "split_k": split,
-            "calls_per_step": len(calls), "layers_resident": len(layers),
-            "kernel_ms_per_step": round(float(kern_ms.sum(axis=1).mean()), 4), "setup_s": round(setup_s, 1),
-        },
+        "dtype": dtype,
+        "data": data,
+        "config": cfg,
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_kernel" if mode == vla.MODE_DECODE else "verify_kernel",
-            "algorithmic_bytes_per_launch": alg_bytes, "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+            "kernel": kernel,
+            "algorithmic_bytes_per_launch": int(alg_bytes), "mean_launch_us": round(mean_launch_ms * 1e3, 2),
             "kernel_hash": khash,
         },
         "cpu_baseline": cpu,

@@ -36,7 +36,7 @@ class Built:
 
 def ripe_window_start(L: int, q_len: int, W: int) -> int:
     """First position whose non-deepest planes a RIPE cache still holds for a call whose block
-    starts at t0 = L - q_len (RIPE page, Alg. 1 step 7: planes of positions older than W are dropped)."""
+    starts at t0 = L - q_len (RIPE page, Sec. 4 and Algorithm 1: once a position leaves the window its non-deepest planes are dropped)."""
     return max(0, L - q_len - W)
 
 
@@ -284,8 +284,9 @@ def build_cells(w: synth.Workload, *, lengths=None, layers=(0,), loops=None, pla
     return BuiltCells(cache, w, seqs, lengths, list(layers), plan)
 
 
-def cell_oracle_row(bc: BuiltCells, b: int, layer: int, loop: int, h: int, thr_offset: float, seed=None):
-    """Oracle inputs of one cell row from the generator, and the oracle's (out, lse, hot bits, scores)."""
+def cell_inputs(bc: BuiltCells, b: int, layer: int, loop: int, h: int, seed=None):
+    """The oracle's inputs for one cell row, regenerated on the host from the generator (same bits as the
+    device cache): query, exact near keys/values, far codes and fp64 metadata, the oracle cell kind."""
     import oracle
     w = bc.w
     seed = w.seed if seed is None else seed
@@ -309,11 +310,36 @@ def cell_oracle_row(bc: BuiltCells, b: int, layer: int, loop: int, h: int, thr_o
     km = synth.f64_from_f16(synth.meta(seed, 0, b, layer, src, w.n_heads, D, 0, n_cp, bits, heads=[h])[:, 0])
     vm = synth.f64_from_f16(synth.meta(seed, 1, b, layer, src, w.n_heads, D // 32, 0, n_far, bits, heads=[h])[:, 0])
     q = cpu_query(w, b, layer, loop, h, L - 1, seed=seed)
-    out, lse, hot, n_cold = oracle.cell_row(q, kn, vn, kc, km[..., 0], km[..., 1], vc, vm[..., 0], vm[..., 1],
-                                            w.sink, w.tail, kind, thr_offset)
+    return dict(q=q, k_near=kn, v_near=vn, kc=kc, ks=km[..., 0], kz=km[..., 1], vc=vc, vs=vm[..., 0],
+                vz=vm[..., 1], sink=w.sink, tail=w.tail, kind=kind)
+
+
+def cell_oracle_row(bc: BuiltCells, b: int, layer: int, loop: int, h: int, thr_offset: float, seed=None):
+    """Oracle inputs of one cell row from the generator, and the oracle's (out, lse, hot bits, scores)."""
+    import oracle
+    w = bc.w
+    D = w.head_dim
+    a = cell_inputs(bc, b, layer, loop, h, seed)
+    out, lse, hot, n_cold = oracle.cell_row(a["q"], a["k_near"], a["v_near"], a["kc"], a["ks"], a["kz"], a["vc"],
+                                            a["vs"], a["vz"], a["sink"], a["tail"], a["kind"], thr_offset)
     # scores of far tokens and the threshold (only to place the rounding band of the mask comparison)
+    n_far = a["kc"].shape[0]
     g = np.arange(n_far) // 32
-    kh = km[g, :, 1] + km[g, :, 0] * kc
-    s_far = kh @ q / np.sqrt(D)
-    m0 = (kn[:w.sink] @ q / np.sqrt(D)).max()
+    kh = a["kz"][g] + a["ks"][g] * a["kc"]
+    s_far = kh @ a["q"] / np.sqrt(D)
+    m0 = (a["k_near"][:w.sink] @ a["q"] / np.sqrt(D)).max()
     return out, lse, hot, s_far, m0 - thr_offset
+
+
+def cell_bytes_per_call(bc: BuiltCells, layer: int, loop: int, n_cold: int = 0) -> int:
+    """Algorithmic bytes of one cell call: every far token-head's codes and metadata once (INT4 and shared
+    cells: K codes 64 B + K metadata 16 B + V hi 32 B + V lo 32 B + V metadata 16 B = 160 B, the lo 32 B
+    only for hot tokens; INT2: 96 B), the exact sink and tail keys and values, and Q and O."""
+    w = bc.w
+    H, D = w.n_heads, w.head_dim
+    per_tok = (40 if cell_bits(bc.plan, layer, loop) == 4 else 24) * D // 32  # bytes per token-head
+    far = sum(L - w.sink - w.tail for L in bc.lengths) * H * per_tok
+    near = len(bc.lengths) * (w.sink + w.tail) * H * 2 * D * 2
+    qo = 2 * len(bc.lengths) * H * D * 2
+    lo_skipped = 32 * n_cold if cell_bits(bc.plan, layer, loop) == 4 else 0
+    return far + near + qo - lo_skipped

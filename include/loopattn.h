@@ -167,7 +167,7 @@ lkv_status lkv_reserve(lkv_cache* c, int32_t seq, int32_t layer, int32_t plane, 
 lkv_status lkv_append_plane(lkv_cache* c, int32_t seq, int32_t layer, int32_t plane, int32_t pos0,
                             int32_t n_tok, const void* k, const void* v, void* stream);
 
-/* Algorithm 1 step 7 of the RIPE page: positions < new_len are committed, and
+/* The window slide of the RIPE page (Sec. 4, Algorithm 1): positions < new_len are committed, and
    the non-deepest planes of positions older than new_len - W are dropped
    (their window-ring pages return to the pool).  new_len <= length. */
 lkv_status lkv_commit(lkv_cache* c, int32_t seq, int32_t new_len);

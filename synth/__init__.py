@@ -299,8 +299,9 @@ WORKLOADS = {
     "ouro_splitk": Workload("ouro_splitk", 32, 24, 4, 16, 128, 8192, DT_BF16, "full", 0, 1, 16,
                             MODE_PLAIN, 1.0, split_k=8, shuffle=True),
     # LoopKV-style cells on the Ouro shape at L=16384, batch 16; sink 4, tail 128.
+    # split_k 0: the library chooses the number of far splits.
     "loopkv_cells": Workload("loopkv_cells", 16, 24, 4, 16, 128, 16384, DT_BF16, "full", 0, 1, 16,
-                             MODE_PLAIN, 1.0, quant=True, sink=4, tail=128),
+                             MODE_PLAIN, 1.0, split_k=0, quant=True, sink=4, tail=128),
 }
 
 

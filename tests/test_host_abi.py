@@ -97,7 +97,7 @@ def test_append_without_gap_and_pool_exhaustion(lib):
 
 
 def test_window_ring_commit_and_ewindow(lib):
-    """RIPE page, Sec. 4 and Alg. 1 step 7: non-deepest planes are kept for the last W positions only;
+    """RIPE page, Sec. 4 and Algorithm 1 (window slide): non-deepest planes are kept for the last W positions only;
     committing drops the planes of positions older than W, and their pages return to the pool."""
     W = 16
     c = make(n_pages=200, window=W, max_block=8)

@@ -25,8 +25,7 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream
 hipError_t launch_append(const CopyParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_fill(void* dst, uint64_t n_bytes, uint32_t value, hipStream_t s);
 hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s);
-hipError_t launch_pack_codes(uint8_t* page, const void* k_codes, const void* k_meta, const void* v_codes,
-                             const void* v_meta, int hkv, int head_dim, int bits, int n_valid, hipStream_t s);
+hipError_t launch_pack_codes(const PackParams& p, int head_dim, hipStream_t s);
 uint64_t code_page_bytes(int hkv, int head_dim, int bits);
 }  // namespace lkv
 
@@ -526,11 +525,21 @@ lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t lo
       T.owner[i] = p;
       T.dirty[(size_t)seq] = 1;
     }
-    const int64_t k = p - page0;
-    hipError_t e = launch_pack_codes(
-        arena + (uint64_t)T.phys[i] * cpb, (const uint8_t*)k_codes + k * kCodePage * hkv * d,
-        (const uint8_t*)k_meta + k * hkv * d * 4, (const uint8_t*)v_codes + k * kCodePage * hkv * d,
-        (const uint8_t*)v_meta + k * kCodePage * hkv * (d / 32) * 4, hkv, d, bits, kCodePage, s);
+  }
+  for (int q0 = page0; q0 < page0 + n_pages; q0 += 64) {
+    PackParams P{};
+    P.arena = arena;
+    P.page_bytes = cpb;
+    const int64_t k = q0 - page0;
+    P.k_codes = (const uint8_t*)k_codes + k * kCodePage * hkv * d;
+    P.k_meta = (const uint16_t*)((const uint8_t*)k_meta + k * hkv * d * 4);
+    P.v_codes = (const uint8_t*)v_codes + k * kCodePage * hkv * d;
+    P.v_meta = (const uint16_t*)((const uint8_t*)v_meta + k * kCodePage * hkv * (d / 32) * 4);
+    P.hkv = hkv;
+    P.bits = bits;
+    P.n_pages = std::min(64, page0 + n_pages - q0);
+    for (int x = 0; x < P.n_pages; ++x) P.phys[x] = T.phys[(size_t)seq * T.ring + q0 + x];
+    hipError_t e = launch_pack_codes(P, d, s);
     if (e != hipSuccess) return hip_fail(c, e, "pack kernel");
   }
   T.hi[(size_t)seq] = std::max(T.hi[(size_t)seq], page0 + n_pages);
@@ -689,7 +698,9 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
     hipError_t e = hipMemsetAsync(a->index_trace, 0xFF, (size_t)a->n_seqs * a->q_len * a->trace_len * 8, s);
     if (e != hipSuccess) return hip_fail(c, e, "trace clear");
   }
-  const int waves = env_int("LKV_WAVES", 4);
+  // Waves per workgroup: 4 for q = 1 rows, 2 for verify tiles (measured best on MI355X
+  // at the workloads' shapes; the environment can override for experiments).
+  const int waves = a->mode == LKV_MODE_VERIFY ? env_int("LKV_VERIFY_WAVES", 2) : env_int("LKV_WAVES", 4);
   const int64_t qrow = (int64_t)a->q_len * hq * D;
   for (int b0 = 0; b0 < a->n_seqs; b0 += kMaxRows) {
     const int nb = std::min(kMaxRows, a->n_seqs - b0);

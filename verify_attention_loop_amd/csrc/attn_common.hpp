@@ -12,11 +12,27 @@ namespace lkv {
 template <typename T, int D>
 struct DecodeTile {
   static constexpr int ES = sizeof(T) == 4 ? 4 : 2;
-  static constexpr int E = D / 16;
-  static constexpr int KB = E * ES;          // K bytes per lane per token
-  static constexpr int VB = kQuad * E * ES;  // V bytes per lane per quad
+  static constexpr int E = D / 16;           // K channels and V channels per lane
+  static constexpr int KB = E * ES;          // K bytes per lane per token: channels [li E, li E + E)
+  static constexpr int VL = D * ES / 64;     // 16-byte V loads per lane per page
+  static constexpr int VB = 16 * VL;         // V bytes per lane per page
   static constexpr int HEAD = kPage * D * ES;
 };
+
+// Channel of a lane's V element e.  Load j of lane li reads the 16 bytes at offset
+// 256 j + 16 li of its quad: bf16 channels 32 j + 2 li and 32 j + 2 li + 1, fp32
+// channel 16 j + li (four tokens each).
+template <typename T>
+__device__ __forceinline__ int vchan(int e, int li) {
+  if constexpr (sizeof(T) == 4) return 16 * e + li;
+  else return 32 * (e >> 1) + 2 * li + (e & 1);
+}
+
+// The lane's V block of one quad (quad_lane = quad base + 16 li).
+template <typename T, int D>
+__device__ __forceinline__ void load_vquad(Raw<DecodeTile<T, D>::VB>& v, const uint8_t* quad_lane) {
+  load_stream_strided<DecodeTile<T, D>::VL>(v, quad_lane, 256);
+}
 
 // Partial score of one token: this lane's channels.
 template <typename T, int D>

@@ -25,16 +25,23 @@ uint64_t code_page_bytes(int hkv, int head_dim, int bits) {
   return (uint64_t)hkv * (bits == 4 ? 40 : 24) * head_dim;
 }
 
-// One thread per (head, token, lane li): packs that lane's 8 channels of one token.
-__global__ __launch_bounds__(256) void pack_codes_kernel(uint8_t* page, const uint8_t* kc, const uint16_t* km,
-                                                         const uint8_t* vc, const uint16_t* vm, int hkv, int bits) {
+// One thread per (head, token, lane li) of one page (blockIdx.y = page of the batch):
+// packs that lane's 8 channels of one token into the page's lane-major layout.
+__global__ __launch_bounds__(256) void pack_codes_kernel(const PackParams p) {
   constexpr int D = 128;
+  const int pi = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= hkv * kCodePage * 16) return;
+  const int hkv = p.hkv, bits = p.bits;
+  if (idx >= hkv * kCodePage * 16 || pi >= p.n_pages) return;
   const int li = idx & 15;
   const int tok = (idx >> 4) & 31;
   const int h = idx >> 9;
   const int g = tok & 3, i = tok >> 2;
+  uint8_t* page = p.arena + (uint64_t)p.phys[pi] * p.page_bytes;
+  const uint8_t* kc = p.k_codes + (int64_t)pi * kCodePage * hkv * D;
+  const uint8_t* vc = p.v_codes + (int64_t)pi * kCodePage * hkv * D;
+  const uint16_t* km = p.k_meta + (int64_t)pi * hkv * D * 2;
+  const uint16_t* vm = p.v_meta + (int64_t)pi * kCodePage * hkv * (D / 32) * 2;
   uint8_t* hb = page + (uint64_t)h * (bits == 4 ? 40 : 24) * D;
   const uint8_t* kin = kc + ((int64_t)tok * hkv + h) * D + 8 * li;
   const uint8_t* vin = vc + ((int64_t)tok * hkv + h) * D + 8 * li;
@@ -76,14 +83,10 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(uint8_t* page, const ui
   }
 }
 
-hipError_t launch_pack_codes(uint8_t* page, const void* k_codes, const void* k_meta, const void* v_codes,
-                             const void* v_meta, int hkv, int head_dim, int bits, int n_valid, hipStream_t s) {
-  (void)n_valid;
-  if (head_dim != 128) return hipErrorInvalidValue;
-  const int n = hkv * kCodePage * 16;
-  hipLaunchKernelGGL(pack_codes_kernel, dim3((n + 255) / 256), dim3(256), 0, s, page,
-                     reinterpret_cast<const uint8_t*>(k_codes), reinterpret_cast<const uint16_t*>(k_meta),
-                     reinterpret_cast<const uint8_t*>(v_codes), reinterpret_cast<const uint16_t*>(v_meta), hkv, bits);
+hipError_t launch_pack_codes(const PackParams& p, int head_dim, hipStream_t s) {
+  if (head_dim != 128 || p.n_pages < 1 || p.n_pages > 64) return hipErrorInvalidValue;
+  const int n = p.hkv * kCodePage * 16;
+  hipLaunchKernelGGL(pack_codes_kernel, dim3((n + 255) / 256, p.n_pages), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
   }
   const int32_t* tab_near = p.tab_near + (int64_t)slot * p.ring_near;
   const uint64_t koff = (uint64_t)hk * HEADB + (uint64_t)li * 16;
-  const uint64_t voff = (uint64_t)p.hkv * HEADB + (uint64_t)hk * HEADB + (uint64_t)g * (kQuad * D * 2) + li * 64;
+  const uint64_t voff = (uint64_t)p.hkv * HEADB + (uint64_t)hk * HEADB + (uint64_t)g * (kQuad * D * 2) + li * 16;
 
   Softmax st{-INFINITY, 0.f};
   float o[E];
@@ -159,14 +162,14 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
       const uint8_t* base = p.pool + (uint64_t)tab_near[pg] * p.page_bytes;
       Raw<16> kr[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) load_raw<16>(kr[i], base + koff + (uint64_t)(4 * g + i) * (D * 2));
+      for (int i = 0; i < 4; ++i) load_stream<16>(kr[i], base + koff + (uint64_t)(4 * i + g) * (D * 2));
       Raw<64> vr;
-      load_raw<64>(vr, base + voff);
+      load_vquad<bf16, D>(vr, base + voff);
       bool zero[4], none[4] = {false, false, false, false};
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = pg * kPage + 4 * g + i;
+        const int j = pg * kPage + 4 * i + g;
         const bool valid = j < p.sink || (j >= tail_lo && j < L);
         zero[i] = !valid;
         float s = 0.f;
@@ -224,8 +227,8 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
       float ps[8];
       if (p.bits == 4) {
         Raw<16> k0, k1;
-        load_raw<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
-        load_raw<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
+        load_stream<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
+        load_stream<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint32_t wd = i < 4 ? k0.w[i] : k1.w[i - 4];
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
         }
       } else {
         Raw<16> kk;
-        load_raw<16>(kk, hb + 4 * D + (g * 16 + li) * 16);
+        load_stream<16>(kk, hb + 4 * D + (g * 16 + li) * 16);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint32_t hw = (kk.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
       }
       // V hi plane (INT4) or V codes (INT2)
       Raw<16> vh;
-      load_raw<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
+      load_stream<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t hw = (vh.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
   __shared__ float sm_m[WAVES * 4], sm_l[WAVES * 4];
   const int r = w * 4 + g;
 #pragma unroll
-  for (int e = 0; e < E; ++e) sm_o[r][li * E + e] = o[e] + zacc;
+  for (int e = 0; e < E; ++e) sm_o[r][part == p.n_splits ? vchan<bf16>(e, li) : li * E + e] = o[e] + zacc;
   if (li == 0) {
     sm_m[r] = st.m;
     sm_l[r] = st.l;

@@ -1,7 +1,7 @@
 // Writing planes into pages: the append path of the paged plane allocator.
 // A page of plane p holds 16 consecutive positions of one (sequence, layer)
-// for all KV heads: K token-major, V with four tokens interleaved per channel
-// (layout in params.hpp).
+// for all KV heads: K token-major, V in four quads, quad g holding the tokens
+// g, g + 4, g + 8, g + 12 interleaved per channel (layout in params.hpp).
 #include <hip/hip_runtime.h>
 
 #include "params.hpp"
@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void append_kernel(const CopyParams p, int D) 
     uint8_t* page = p.pool + (uint64_t)p.phys[lp] * p.page_bytes;
     uint8_t* kd = page + (uint64_t)h * head + ((uint64_t)s * D + c) * ES;
     uint8_t* vd = page + (uint64_t)p.hkv * head + (uint64_t)h * head +
-                  ((uint64_t)(s / kQuad) * kQuad * D + (uint64_t)c * kQuad + (s % kQuad)) * ES;
+                  ((uint64_t)(s % kQuad) * kQuad * D + (uint64_t)c * kQuad + (s / kQuad)) * ES;
     const uint8_t* ks = reinterpret_cast<const uint8_t*>(p.k) + idx * ES;
     const uint8_t* vs = reinterpret_cast<const uint8_t*>(p.v) + idx * ES;
     if constexpr (ES == 4) {

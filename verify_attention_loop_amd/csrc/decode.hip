@@ -7,11 +7,15 @@
 // positions through the same rule and its block positions from caller scratch.
 //
 // Mapping (one workgroup = one (sequence, query head, split) row, WAVES waves):
-//   * a wave takes whole 16-token pages; its 4 DPP rows of 16 lanes take the
-//     page's 4 quads, lane li owning channels [li*E, li*E + E), E = D/16;
-//   * K: row g reads token 4g+i of the page per load i (E*2 bytes per lane,
-//     dwordx3 for D = 96), dot products by v_dot2c_f32_bf16, 16-lane DPP sums;
-//   * V: row g reads its quad's [channel][4 tokens] block, 16 B per lane-load;
+//   * a wave takes whole 16-token pages; DPP row g (16 lanes) handles the tokens
+//     4i + g of the page, which V quad g holds (page layout in params.hpp);
+//   * K: load i of row g reads token 4i + g, lane li its channels
+//     [li*E, li*E + E), E = D/16 (dwordx3 for bf16 D = 96), so one load
+//     instruction of the wave reads four whole token rows; scores by
+//     v_dot2c_f32_bf16 and 16-lane DPP sums;
+//   * V: load j of lane li reads 16 B at offset 256 j + 16 li of quad g (two bf16
+//     channels or one fp32 channel, four tokens), again whole lines per instruction;
+//   * page data is read with nontemporal loads (it is read once per call);
 //   * each DPP row keeps its own online softmax (m, l, o); rows and waves merge
 //     through LDS at the end, splits through the LSE merge kernel.
 // The plane of a key is chosen per token by address, so a RIPE boundary inside a
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
   const int32_t* tab_deep = p.tab_deep + (int64_t)slot * p.ring_deep;
   const uint64_t koff = (uint64_t)hk * HEAD + (uint64_t)li * KB;
   const uint64_t voff = (uint64_t)p.hkv * HEAD + (uint64_t)hk * HEAD + (uint64_t)g * (kQuad * D * ES) +
-                        (uint64_t)li * VB;
+                        (uint64_t)li * 16;
 
   for (int pg = p0 + w; pg < p1; pg += WAVES) {
     const int pos = pg * kPage;
@@ -84,20 +88,20 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
     Raw<KB> kr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = pos + 4 * g + i;
+      const int j = pos + 4 * i + g;
       const bool own = (j < n_cached) ? (j >= own_lo) : any_own;
       const uint8_t* bp = own ? base_own : base_deep;
-      load_raw<KB>(kr[i], bp + koff + (uint64_t)(4 * g + i) * (D * ES));
+      load_stream<KB>(kr[i], bp + koff + (uint64_t)(4 * i + g) * (D * ES));
     }
     Raw<VB> vr;
-    load_raw<VB>(vr, (any_own ? base_own : base_deep) + voff);
+    load_vquad<T, D>(vr, (any_own ? base_own : base_deep) + voff);
     if (!full || (any_own && any_deep)) {  // boundary or last page: per-token plane and validity
       Raw<VB> vd;
-      if (any_own && any_deep) load_raw<VB>(vd, base_deep + voff);
+      if (any_own && any_deep) load_vquad<T, D>(vd, base_deep + voff);
       bool take_deep[4], zero[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int j = pos + 4 * g + k;
+        const int j = pos + 4 * k + g;
         take_deep[k] = any_own && any_deep && j < own_lo;
         zero[k] = j >= n_cached;
       }
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int j = pos + 4 * g + i;
+      const int j = pos + 4 * i + g;
       const float s = row_sum16(partial_dot<T, D>(kr[i], qf, qw)) * p.scale_log2;
       x[i] = (j < n_cached) ? s : -INFINITY;
     }
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
       if (h == 0 && li == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = pos + 4 * g + i;
+          const int j = pos + 4 * i + g;
           if (j < n_cached && j < p.trace_len) {
             const bool own = j >= own_lo;
             int32_t* tr = p.trace + ((int64_t)b * p.trace_len + j) * 2;
@@ -135,16 +139,21 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
     for (int i = w * 4 + g; i < p.draft_len; i += WAVES * 4) {
       const int64_t roff = (((int64_t)b * p.draft_len + i) * p.hkv + hk) * D + li * E;
       Raw<KB> kr;
-      Raw<KB> vr;
       load_raw<KB>(kr, reinterpret_cast<const uint8_t*>(p.draft_k) + roff * ES);
-      load_raw<KB>(vr, reinterpret_cast<const uint8_t*>(p.draft_v) + roff * ES);
+      // this lane's V channels (vchan) of the draft token
+      const uint32_t* vrow = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(p.draft_v) +
+                                                               ((((int64_t)b * p.draft_len + i) * p.hkv + hk) * D) * ES);
       float x[1] = {row_sum16(partial_dot<T, D>(kr, qf, qw)) * p.scale_log2};
       softmax_step<E, 1>(st, o, x);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float v;
-        if constexpr (sizeof(T) == 4) v = __uint_as_float(vr.w[e]);
-        else v = (e & 1) ? bf_hi(vr.w[e >> 1]) : bf_lo(vr.w[e >> 1]);
+        if constexpr (sizeof(T) == 4) {
+          v = __uint_as_float(vrow[vchan<T>(e, li)]);
+        } else {
+          const uint32_t pair = vrow[vchan<T>(e & ~1, li) >> 1];
+          v = (e & 1) ? bf_hi(pair) : bf_lo(pair);
+        }
         o[e] = fmaf(x[0], v, o[e]);
       }
       if constexpr (TRACE) {
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
   __shared__ float sm_m[WAVES * 4], sm_l[WAVES * 4];
   const int r = w * 4 + g;
 #pragma unroll
-  for (int e = 0; e < E; ++e) sm_o[r][li * E + e] = o[e];
+  for (int e = 0; e < E; ++e) sm_o[r][vchan<T>(e, li)] = o[e];
   if (li == 0) {
     sm_m[r] = st.m;
     sm_l[r] = st.l;
@@ -194,27 +203,49 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
   }
 }
 
-// Exact log-sum-exp merge of split partials (LoopKV page, Sec. 3.4): with
-// lse_s the base-2 log-sum-exp of split s, o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).
+// Exact log-sum-exp merge of split partials (LoopKV page, Sec. 3.4): with lse_s the
+// base-2 log-sum-exp of part s, o = sum_s 2^(lse_s - M) o_s / sum_s 2^(lse_s - M).
+// One wave per row; the row's part weights come from one parallel load and a
+// butterfly reduction, and the per-channel sums take the parts in index order, so
+// the result does not depend on scheduling.  Up to 128 parts.
+__device__ __forceinline__ float wave_max64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(128) void merge_kernel(const MergeParams p) {
-  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 6);
-  if (row >= p.n_rows) return;
+__global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= p.n_rows) return;  // whole waves leave together
   const int lane = threadIdx.x & 63;
   const float* ws = p.ws + row * p.n_parts * (D + 1);
-  float M = -INFINITY;
-  for (int s = 0; s < p.n_parts; ++s) M = fmaxf(M, ws[s * (D + 1) + D]);
+  const float l0 = lane < p.n_parts ? ws[lane * (D + 1) + D] : -INFINITY;
+  const float l1 = lane + 64 < p.n_parts ? ws[(lane + 64) * (D + 1) + D] : -INFINITY;
+  const float M = wave_max64(fmaxf(l0, l1));
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float Ls = 0.f;
-  for (int s = 0; s < p.n_parts; ++s) Ls += fast_exp2(ws[s * (D + 1) + D] - Mu);
-  for (int c = lane; c < D; c += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < p.n_parts; ++s) {
-      const float wgt = fast_exp2(ws[s * (D + 1) + D] - Mu);
-      if (wgt > 0.f) acc = fmaf(wgt, ws[s * (D + 1) + c], acc);
-    }
-    store_out<T>(p.out, row * D + c, Ls > 0.f ? acc / Ls : 0.f);
+  const float Ls = wave_sum64(fast_exp2(l0 - Mu) + fast_exp2(l1 - Mu));
+  constexpr int NC = (D + 63) / 64;
+  float acc[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) acc[k] = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < p.n_parts; ++s) {
+    const float* part = ws + s * (D + 1);
+    const float wgt = fast_exp2(part[D] - Mu);  // 0 for an empty part (lse = -inf, o = 0)
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      if (lane + 64 * k < D) acc[k] = fmaf(wgt, part[lane + 64 * k], acc[k]);
   }
+#pragma unroll
+  for (int k = 0; k < NC; ++k)
+    if (lane + 64 * k < D) store_out<T>(p.out, row * D + lane + 64 * k, Ls > 0.f ? acc[k] / Ls : 0.f);
   if (lane == 0 && p.lse) p.lse[row] = (Ls > 0.f ? M + fast_log2(Ls) : -INFINITY) * 0.69314718055994531f;
 }
 
@@ -250,15 +281,16 @@ hipError_t launch_decode(const PlainParams& p, int dtype, int head_dim, int wave
 }
 
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t s) {
-  dim3 grid((p.n_rows + 1) / 2);
+  if (p.n_parts < 1 || p.n_parts > 128) return hipErrorInvalidValue;
+  dim3 grid((p.n_rows + 3) / 4);
   if (dtype == 0) {
-    if (head_dim == 64) hipLaunchKernelGGL((merge_kernel<float, 64>), grid, dim3(128), 0, s, p);
-    else if (head_dim == 96) hipLaunchKernelGGL((merge_kernel<float, 96>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((merge_kernel<float, 128>), grid, dim3(128), 0, s, p);
+    if (head_dim == 64) hipLaunchKernelGGL((merge_kernel<float, 64>), grid, dim3(256), 0, s, p);
+    else if (head_dim == 96) hipLaunchKernelGGL((merge_kernel<float, 96>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((merge_kernel<float, 128>), grid, dim3(256), 0, s, p);
   } else {
-    if (head_dim == 64) hipLaunchKernelGGL((merge_kernel<bf16, 64>), grid, dim3(128), 0, s, p);
-    else if (head_dim == 96) hipLaunchKernelGGL((merge_kernel<bf16, 96>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((merge_kernel<bf16, 128>), grid, dim3(128), 0, s, p);
+    if (head_dim == 64) hipLaunchKernelGGL((merge_kernel<bf16, 64>), grid, dim3(256), 0, s, p);
+    else if (head_dim == 96) hipLaunchKernelGGL((merge_kernel<bf16, 96>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((merge_kernel<bf16, 128>), grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

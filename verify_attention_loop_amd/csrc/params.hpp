@@ -17,10 +17,13 @@ enum : int32_t { kDecode = 0, kVerify = 1, kDraft = 2 };
 
 // Plain page layout (one page = one (seq, layer, plane), all KV heads, 16 tokens):
 //   K block: [head][token 0..15][channel 0..D-1]
-//   V block: [head][quad 0..3][channel 0..D-1][token-in-quad 0..3]
-// so each (page, head) K slice and V slice is one contiguous run of 16*D elements;
-// V interleaves four tokens per channel so that a lane reads four tokens of its
-// channels in one 16-byte load, and the verify tile gets V^T operands directly.
+//   V block: [head][quad g 0..3][channel 0..D-1][i 0..3], entry i of quad g = token 4 i + g
+// so each (page, head) K slice and V slice is one contiguous run of 16*D elements.
+// V interleaves four tokens per channel: a lane reads four tokens of two (bf16) or one
+// (fp32) channel in one 16-byte load, and the verify tile gets its V^T operand
+// directly.  A quad holds every fourth token so that the decode kernel, whose DPP
+// row g handles the tokens 4 i + g, reads K four whole token rows per load
+// instruction (whole 128-byte lines) and V whole 256-byte runs per instruction.
 
 // Attention over plain pages (DECODE, VERIFY, DRAFT).
 struct PlainParams {
@@ -85,6 +88,19 @@ struct MergeParams {
   float* lse;                 // [rows] or null
   int32_t n_rows;
   int32_t n_parts;
+};
+
+// Pack logical code arrays into up to 64 code pages (lkv_append_coded).
+struct PackParams {
+  uint8_t* arena;             // code page arena of the cell's kind
+  uint64_t page_bytes;
+  const uint8_t* k_codes;     // [n_pages * 32][hkv][D]
+  const uint16_t* k_meta;     // [n_pages][hkv][D][2]
+  const uint8_t* v_codes;     // [n_pages * 32][hkv][D]
+  const uint16_t* v_meta;     // [n_pages * 32][hkv][D / 32][2]
+  int32_t hkv, bits;
+  int32_t n_pages;
+  int32_t phys[64];           // physical page of batch page i
 };
 
 // Append rows into plain pages.

@@ -9,11 +9,14 @@
 // This is a dense k x 16 x D contraction per page and head, so it runs on MFMA:
 //   S^T[16 keys x 16 queries]  = K[16 x D] * Q^T         (16x16x32 bf16 / 16x16x4 f32)
 //   O^T[D x 16 queries]       += V^T[D x 16 keys] * P^T   (16x16x16 bf16 / 16x16x4 f32)
-// Lane l = (g = l / 16, n = l % 16): n is its query column; its S^T values are
-// keys 4g..4g+3 of the page for query n, which is exactly the P^T operand layout
-// of the PV product, and the V block's [quad][channel][4 keys] layout is exactly
-// the V^T operand (4 keys of one channel per lane).  Rows k..15 of the tile are
-// padding (k <= 16).
+// Lane l = (g = l / 16, n = l % 16): n is its query column.  Row m of the K
+// operand is the page's token 4 (m % 4) + m / 4, so the lane's S^T values (rows
+// 4g..4g+3) are the tokens g, g+4, g+8, g+12 for query n: exactly the P^T operand
+// of the PV product, and exactly the four tokens of V quad g, whose
+// [channel][4 tokens] layout is the V^T operand (four tokens of one channel per
+// lane).  Columns k..15 of the tile are padding (k <= 16).  V is read with
+// nontemporal loads (whole lines per instruction); K rows are 64-byte pieces of
+// 192-256-byte token rows, so they use plain loads, which L2 merges.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -38,8 +41,9 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int ES = F32 ? 4 : 2;
   constexpr int HEAD = kPage * D * ES;
-  // bf16: D/32 QK steps of 32 channels and D/32 PV loads of two 16-channel blocks.
-  // f32:  D/16 loads of 4 channels, 4 QK MFMAs each; D/16 PV loads of 4 keys, 4 MFMAs each.
+  // bf16: D/32 K loads of 8 channels (one 16x16x32 MFMA each) and D/32 V loads of two
+  //       channels x 4 tokens (two 16x16x16 MFMAs each).
+  // f32:  D/16 K loads of 4 channels (4 MFMAs each); D/16 V loads of one channel x 4 tokens.
   constexpr int NB = F32 ? D / 16 : D / 32;
   constexpr int NACC = F32 ? D / 16 : D / 16;  // 16-channel output blocks
 
@@ -83,47 +87,52 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
   const int32_t* tab_own = p.tab_own + (int64_t)slot * p.ring_own;
   const int32_t* tab_deep = p.tab_deep + (int64_t)slot * p.ring_deep;
 
+  // Per lane: K row token 4 (n % 4) + n / 4 (MFMA row n), channel offsets per load s;
+  // V quad g, channels 32 s + 2 n (bf16) or 16 s + n (fp32).
+  const uint64_t koff = (uint64_t)hk * HEAD + (uint64_t)(4 * (n & 3) + (n >> 2)) * D * ES +
+                        (uint64_t)(F32 ? 4 * g * 4 : 8 * g * 2);
+  const uint64_t voff = (uint64_t)p.hkv * HEAD + (uint64_t)hk * HEAD + (uint64_t)g * (kQuad * D * ES) +
+                        (uint64_t)(F32 ? n * kQuad * 4 : 2 * n * kQuad * 2);
+  constexpr int KSTEP = F32 ? 16 * 4 : 32 * 2;              // bytes between a lane's K loads
+  constexpr int VSTEP = F32 ? 16 * kQuad * 4 : 32 * kQuad * 2;  // bytes between a lane's V loads
+
   for (int pg = p0 + w; pg < p1; pg += WAVES) {
     const int pos = pg * kPage;
     const int vend = min(pos + kPage, L);
-    const bool any_own = vend - 1 >= own_min;
+    const bool any_own = vend - 1 >= own_min;  // uniform over the wave; every page has own or deep
     const bool any_deep = pos < own_max;
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = any_own ? 0 : 1; pass < (any_deep ? 2 : 1); ++pass) {
       const bool own = pass == 0;
-      if (own ? !any_own : !any_deep) continue;
       const int phys = own ? tab_own[pg % p.ring_own] : tab_deep[pg];
       const uint8_t* base = p.pool + (uint64_t)phys * p.page_bytes;
-      const uint8_t* kbase = base + (uint64_t)hk * HEAD + (uint64_t)n * D * ES;
-      const uint8_t* vbase = base + (uint64_t)p.hkv * HEAD + (uint64_t)hk * HEAD + (uint64_t)g * (kQuad * D * ES);
+      // Issue every load of the page first: K rows (plain loads) and V quads (streaming).
+      Raw<16> kr[NB], vr[NB];
+#pragma unroll
+      for (int s = 0; s < NB; ++s) load_raw<16>(kr[s], base + koff + s * KSTEP);
+#pragma unroll
+      for (int s = 0; s < NB; ++s) load_stream<16>(vr[s], base + voff + s * VSTEP);
 
       // ---- S^T = K Q^T
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (F32) {
 #pragma unroll
-        for (int s = 0; s < NB; ++s) {
-          Raw<16> kr;
-          load_raw<16>(kr, kbase + (16 * s + 4 * g) * 4);
+      for (int s = 0; s < NB; ++s) {
+        if constexpr (F32) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kr.w[e]), __uint_as_float(qb[s][e]), sc, 0, 0,
-                                                      0);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < NB; ++s) {
-          Raw<16> kr;
-          load_raw<16>(kr, kbase + (32 * s + 8 * g) * 2);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr.w),
+            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kr[s].w[e]), __uint_as_float(qb[s][e]), sc,
+                                                      0, 0, 0);
+        } else {
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[s].w),
                                                        __builtin_bit_cast(bf16x8_t, qb[s]), sc, 0, 0, 0);
         }
       }
 
-      // ---- mask, online softmax for query n
+      // ---- mask, online softmax for query n (S^T element i is token 4i + g)
       float x[4];
       bool keep[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = pos + 4 * g + i;
+        const int j = pos + 4 * i + g;
         const bool plane_ok = own ? (j >= own_n) : (j < own_n);
         const bool vis = qv && j <= tq && plane_ok;
         x[i] = vis ? sc[i] * p.scale_log2 : -INFINITY;
@@ -148,39 +157,28 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
 #pragma unroll
       for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
 
-      // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T; V of tokens this pass does not own is cleared (unused or
+      // poisoned slots may hold NaN, and 0 * NaN is NaN)
       if constexpr (F32) {
         lsum = fmaf(lsum, alpha, (pe[0] + pe[1]) + (pe[2] + pe[3]));
 #pragma unroll
-        for (int s = 0; s < NB; ++s) {
-          Raw<16> vr;
-          load_raw<16>(vr, vbase + (uint64_t)(16 * s + n) * kQuad * 4);
+        for (int s = 0; s < NB; ++s)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float v = keep[e] ? __uint_as_float(vr.w[e]) : 0.f;
+            const float v = __uint_as_float(keep[e] ? vr[s].w[e] : 0u);
             acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pe[e], acc[s], 0, 0, 0);
           }
-        }
       } else {
         // P in bf16 for the MFMA; the row sum uses the same rounded weights.
         const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
         lsum = fmaf(lsum, alpha, (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23)));
         const uint32_t pw[2] = {p01, p23};
-        const bool need_mask = !(keep[0] && keep[1] && keep[2] && keep[3]);
         const uint32_t k01 = (keep[0] ? 0x0000FFFFu : 0u) | (keep[1] ? 0xFFFF0000u : 0u);
         const uint32_t k23 = (keep[2] ? 0x0000FFFFu : 0u) | (keep[3] ? 0xFFFF0000u : 0u);
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
-          Raw<16> vr;
-          load_raw<16>(vr, vbase + (uint64_t)(32 * s + 2 * n) * kQuad * 2);
-          if (need_mask) {
-            vr.w[0] &= k01;
-            vr.w[1] &= k23;
-            vr.w[2] &= k01;
-            vr.w[3] &= k23;
-          }
-          const uint32_t a0[2] = {vr.w[0], vr.w[1]};
-          const uint32_t a1[2] = {vr.w[2], vr.w[3]};
+          const uint32_t a0[2] = {vr[s].w[0] & k01, vr[s].w[1] & k23};
+          const uint32_t a1[2] = {vr[s].w[2] & k01, vr[s].w[3] & k23};
           acc[2 * s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a0),
                                                                  __builtin_bit_cast(bf16x4_t, pw), acc[2 * s], 0, 0, 0);
           acc[2 * s + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
@@ -238,7 +236,10 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
 template <typename T, int D>
 static hipError_t launch_verify_t(const PlainParams& p, int waves, bool trace, hipStream_t s) {
   dim3 grid(p.n_splits, p.hq, p.n_rows);
-  if (waves == 2) {
+  if (waves == 1) {
+    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 1, true>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((verify_kernel<T, D, 1, false>), grid, dim3(64), 0, s, p);
+  } else if (waves == 2) {
     if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 2, true>), grid, dim3(128), 0, s, p);
     else hipLaunchKernelGGL((verify_kernel<T, D, 2, false>), grid, dim3(128), 0, s, p);
   } else {
@@ -250,7 +251,7 @@ static hipError_t launch_verify_t(const PlainParams& p, int waves, bool trace, h
 
 hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s) {
   if (p.q_len < 1 || p.q_len > kMaxBlock) return hipErrorInvalidValue;
-  if (waves != 2) waves = 4;
+  if (waves != 1 && waves != 2) waves = 4;
   if (dtype == 0) {
     if (head_dim == 64) return launch_verify_t<float, 64>(p, waves, trace, s);
     if (head_dim == 96) return launch_verify_t<float, 96>(p, waves, trace, s);

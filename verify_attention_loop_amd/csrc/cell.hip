@@ -5,14 +5,23 @@
 // V codes plus fp16 scale/zero per 32 elements, LoopKV page App. C):
 //   [0,    4D)  K meta   [channel][scale, zero] fp16, per channel over the page
 //   [4D,  20D)  K codes  4-bit, lane-major: [half][g][li][4 tokens][8 nibbles]
-//   [20D, 28D)  V hi     2-bit hi = c >> 2, lane-major: [g][li][8 tokens][8 x 2 bits]
-//   [28D, 36D)  V lo     2-bit lo = c & 3, token-major: [token][D x 2 bits]
+//   [20D, 28D)  V hi     2-bit hi = c >> 2, lane-major: [g][li][8 tokens][16 bits]
+//   [28D, 36D)  V lo     2-bit lo = c & 3, token-major: [token][li][16 bits]
 //   [36D, 40D)  V meta   [g][group][8 tokens][scale, zero] fp16, per token and 32 channels
 // INT2 (24 * D bytes): K meta [0,4D), K codes [4D,12D) as V hi, V codes [12D,20D)
 // as V hi, V meta [20D,24D).  Lane (g, li) of a DPP row owns channels 8li..8li+7
 // and tokens g, g+4, ..., g+28 of the page, so its K codes, V hi and V meta are
 // contiguous 16-32 B runs; V lo is token-major so that a cold token's 32-byte lo
 // row (one token-head) is never requested at all (LoopKV page, Sec. 3.3).
+//
+// Bit order inside a lane's 16-bit word of 2-bit values (its 8 channels c):
+// hi crumbs sit at crumb 2c + 1 (c < 4) or 2(c - 4) (c >= 4), lo and INT2 crumbs
+// at crumb 2c (c < 4) or 2(c - 4) + 1 (c >= 4).  Then x | x << 18 puts hi_c at
+// bits 2-3 of nibble c and y | y << 14 puts lo_c at bits 0-1 of nibble c, so one
+// bitfield insert yields the eight 4-bit codes 4 hi + lo of a hot token, and
+// byte conversions turn nibbles into floats: about 3 VALU instructions per code
+// instead of 6 for separate hi and lo planes.  K codes are plain nibbles (nibble c
+// = channel c).
 #include <hip/hip_runtime.h>
 
 #include "attn_common.hpp"
@@ -24,6 +33,10 @@ namespace lkv {
 uint64_t code_page_bytes(int hkv, int head_dim, int bits) {
   return (uint64_t)hkv * (bits == 4 ? 40 : 24) * head_dim;
 }
+
+// Crumb positions of channel c (0..7) in a lane's 16-bit word (see the layout above).
+__host__ __device__ __forceinline__ int hi_crumb(int c) { return c < 4 ? 2 * c + 1 : 2 * (c - 4); }
+__host__ __device__ __forceinline__ int lo_crumb(int c) { return c < 4 ? 2 * c : 2 * (c - 4) + 1; }
 
 // One thread per (head, token, lane li) of one page (blockIdx.y = page of the batch):
 // packs that lane's 8 channels of one token into the page's lane-major layout.
@@ -49,8 +62,8 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const PackParams p) {
     uint32_t kw = 0, vhi = 0, vlo = 0;
     for (int c = 0; c < 8; ++c) {
       kw |= (uint32_t)(kin[c] & 15u) << (4 * c);
-      vhi |= (uint32_t)((vin[c] >> 2) & 3u) << (2 * c);
-      vlo |= (uint32_t)(vin[c] & 3u) << (2 * c);
+      vhi |= (uint32_t)((vin[c] >> 2) & 3u) << (2 * hi_crumb(c));
+      vlo |= (uint32_t)(vin[c] & 3u) << (2 * lo_crumb(c));
     }
     const int hh = i >> 2, ii = i & 3;
     *reinterpret_cast<uint32_t*>(hb + 4 * D + hh * 1024 + (g * 16 + li) * 16 + ii * 4) = kw;
@@ -59,8 +72,8 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const PackParams p) {
   } else {
     uint32_t kw = 0, vw = 0;
     for (int c = 0; c < 8; ++c) {
-      kw |= (uint32_t)(kin[c] & 3u) << (2 * c);
-      vw |= (uint32_t)(vin[c] & 3u) << (2 * c);
+      kw |= (uint32_t)(kin[c] & 3u) << (2 * lo_crumb(c));
+      vw |= (uint32_t)(vin[c] & 3u) << (2 * lo_crumb(c));
     }
     *reinterpret_cast<uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)kw;
     *reinterpret_cast<uint16_t*>(hb + 12 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)vw;
@@ -94,8 +107,35 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-__device__ __forceinline__ float crumb(uint32_t w, int c) { return (float)((w >> (2 * c)) & 3u); }
-__device__ __forceinline__ float nibble(uint32_t w, int c) { return (float)((w >> (4 * c)) & 15u); }
+// Nibble c of the result = 4 hi_c (bits 2-3) / lo_c (bits 0-1) from a lane's crumb word.
+__device__ __forceinline__ uint32_t hi_nibbles(uint32_t x) { return (x | (x << 18)) & 0xCCCCCCCCu; }
+__device__ __forceinline__ uint32_t lo_nibbles(uint32_t y) { return (y | (y << 14)) & 0x33333333u; }
+
+// Byte k of a word as a float (v_cvt_f32_ubyte{0..3}: one VALU op).  Written as an
+// instruction because the compiler, knowing the bytes hold nibbles, otherwise
+// extracts each one with a separate bitfield op first.
+template <int K>
+__device__ __forceinline__ float ubyte_f32(uint32_t x) {
+  float r;
+  if constexpr (K == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
+  else if constexpr (K == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
+  else if constexpr (K == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
+  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// The eight nibbles of a code word as floats, f[c] = nibble c.
+__device__ __forceinline__ void nibbles_f32(uint32_t code, float* f) {
+  const uint32_t ev = code & 0x0F0F0F0Fu, od = (code >> 4) & 0x0F0F0F0Fu;
+  f[0] = ubyte_f32<0>(ev);
+  f[1] = ubyte_f32<0>(od);
+  f[2] = ubyte_f32<1>(ev);
+  f[3] = ubyte_f32<1>(od);
+  f[4] = ubyte_f32<2>(ev);
+  f[5] = ubyte_f32<2>(od);
+  f[6] = ubyte_f32<3>(ev);
+  f[7] = ubyte_f32<3>(od);
+}
 
 __device__ __forceinline__ uint32_t or4(uint32_t v) {
   v |= (uint32_t)__shfl_xor((int)v, 16);
@@ -117,7 +157,7 @@ __device__ __forceinline__ uint32_t or4(uint32_t v) {
 //     scale and zero fold into the weight p_j (LoopKV page, Sec. 3.3, App. E Alg. 1).
 // Each DPP row keeps its own online softmax; partials go to the workspace and
 // the LSE merge kernel combines them.
-template <int WAVES, bool TRACE>
+template <int WAVES, bool TRACE, int BITS>
 __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
   constexpr int D = 128, E = 8;
   constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
@@ -204,14 +244,14 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
       m0 = fmaxf(m0, __shfl_xor(m0, 32));
     }
     const float thr = m0 - p.thr_offset;
-    const bool masked = p.masked != 0;
+    constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
     const int n_cp = (n_far + kCodePage - 1) / kCodePage;
     const int c0 = (int)((int64_t)part * n_cp / p.n_splits);
     const int c1 = (int)((int64_t)(part + 1) * n_cp / p.n_splits);
     const int32_t* tab_code = p.tab_code + (int64_t)slot * p.code_ring;
-    const uint64_t head_bytes = (uint64_t)(p.bits == 4 ? 40 : 24) * D;
-    const uint64_t vcode_off = p.bits == 4 ? 20 * D : 12 * D;
-    const uint64_t vmeta_off = p.bits == 4 ? 36 * D : 20 * D;
+    constexpr uint64_t head_bytes = (uint64_t)(BITS == 4 ? 40 : 24) * D;
+    constexpr uint64_t vcode_off = BITS == 4 ? 20 * D : 12 * D;
+    constexpr uint64_t vmeta_off = BITS == 4 ? 36 * D : 20 * D;
     for (int cp = c0 + w; cp < c1; cp += WAVES) {
       const uint8_t* hb = p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes;
       // K meta of this lane's 8 channels -> q' = q * scale, bias = q . zero
@@ -224,30 +264,25 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
         bias = fmaf(qf[c], f16_to_f32(km.w[c] >> 16), bias);
       }
       // K codes -> scores of tokens g + 4i
+      // Issue the page's code loads together: K codes, V hi (or INT2 V codes), V meta.
+      Raw<16> k0, k1, vh;
+      Raw<32> vm;
+      load_stream<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
+      if constexpr (BITS == 4) load_stream<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
+      load_stream<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
+      load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
       float ps[8];
-      if (p.bits == 4) {
-        Raw<16> k0, k1;
-        load_stream<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
-        load_stream<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t wd = i < 4 ? k0.w[i] : k1.w[i - 4];
-          float s = bias;
+      for (int i = 0; i < 8; ++i) {
+        uint32_t code;
+        if constexpr (BITS == 4) code = i < 4 ? k0.w[i] : k1.w[i - 4];
+        else code = lo_nibbles((k0.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        float f[E];
+        nibbles_f32(code, f);
+        float s = bias;
 #pragma unroll
-          for (int c = 0; c < E; ++c) s = fmaf(qs[c], nibble(wd, c), s);
-          ps[i] = s;
-        }
-      } else {
-        Raw<16> kk;
-        load_stream<16>(kk, hb + 4 * D + (g * 16 + li) * 16);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t hw = (kk.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-          float s = bias;
-#pragma unroll
-          for (int c = 0; c < E; ++c) s = fmaf(qs[c], crumb(hw, c), s);
-          ps[i] = s;
-        }
+        for (int c = 0; c < E; ++c) s = fmaf(qs[c], f[c], s);
+        ps[i] = s;
       }
       float x[8];
       bool hot[8], valid[8];
@@ -277,9 +312,14 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
 #pragma unroll
       for (int c = 0; c < E; ++c) o[c] *= alpha;
       zacc *= alpha;
+      // V lo rows of the hot tokens only (INT4 and shared cells; LoopKV page, Sec. 3.3)
+      uint32_t lo16[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo16[i] = 0u;
+        if (masked && hot[i]) lo16[i] = *reinterpret_cast<const uint16_t*>(hb + 28 * D + (g + 4 * i) * 32 + li * 2);
+      }
       // V meta of the lane's group for its 8 tokens; fold scale and zero into the weights
-      Raw<32> vm;
-      load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
       float wgt[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -288,26 +328,17 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
         const float zc = valid[i] ? x[i] * zz : 0.f;
         zacc += (masked && valid[i] && !hot[i]) ? fmaf(1.5f, wgt[i], zc) : zc;
       }
-      // V hi plane (INT4) or V codes (INT2)
-      Raw<16> vh;
-      load_stream<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
+      // V codes: INT4 hot 4 hi + lo, cold 4 hi (the bucket midpoint's 1.5 is in zacc); INT2 the code
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t hw = (vh.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        const float coef = masked ? 4.f * wgt[i] : wgt[i];
+        uint32_t code;
+        if constexpr (BITS == 4) code = hi_nibbles(hw) | lo_nibbles(lo16[i]);
+        else code = lo_nibbles(hw);
+        float f[E];
+        nibbles_f32(code, f);
 #pragma unroll
-        for (int c = 0; c < E; ++c) o[c] = fmaf(coef, crumb(hw, c), o[c]);
-      }
-      // V lo plane: fetched for hot tokens only
-      if (masked) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (hot[i]) {
-            const uint32_t lo = *reinterpret_cast<const uint16_t*>(hb + 28 * D + (g + 4 * i) * 32 + li * 2);
-#pragma unroll
-            for (int c = 0; c < E; ++c) o[c] = fmaf(wgt[i], crumb(lo, c), o[c]);
-          }
-        }
+        for (int c = 0; c < E; ++c) o[c] = fmaf(wgt[i], f[c], o[c]);
       }
       if constexpr (TRACE) {
         const uint32_t word = or4(hotbits);
@@ -345,17 +376,24 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
   if (threadIdx.x == 0) wsr[D] = Lsum > 0.f ? M + fast_log2(Lsum) : -INFINITY;
 }
 
+template <int BITS>
+static void launch_cell_t(const CellParams& p, int waves, bool trace, dim3 grid, hipStream_t s) {
+  if (waves == 2) {
+    if (trace) hipLaunchKernelGGL((cell_kernel<2, true, BITS>), grid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((cell_kernel<2, false, BITS>), grid, dim3(128), 0, s, p);
+  } else {
+    if (trace) hipLaunchKernelGGL((cell_kernel<4, true, BITS>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((cell_kernel<4, false, BITS>), grid, dim3(256), 0, s, p);
+  }
+}
+
 hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s) {
-  if (head_dim != 128 || p.sink > kPage) return hipErrorInvalidValue;
+  if (head_dim != 128 || p.sink > kPage || (p.bits != 4 && p.bits != 2) || p.masked != (p.bits == 4 ? 1 : 0))
+    return hipErrorInvalidValue;
   dim3 grid(p.n_splits + 1, p.hq, p.n_rows);
   const bool trace = p.mask_trace != nullptr;
-  if (waves == 2) {
-    if (trace) hipLaunchKernelGGL((cell_kernel<2, true>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((cell_kernel<2, false>), grid, dim3(128), 0, s, p);
-  } else {
-    if (trace) hipLaunchKernelGGL((cell_kernel<4, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((cell_kernel<4, false>), grid, dim3(256), 0, s, p);
-  }
+  if (p.bits == 4) launch_cell_t<4>(p, waves, trace, grid, s);
+  else launch_cell_t<2>(p, waves, trace, grid, s);
   return hipGetLastError();
 }
 

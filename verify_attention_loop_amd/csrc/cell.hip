@@ -158,7 +158,8 @@ __device__ __forceinline__ uint32_t or4(uint32_t v) {
 // Each DPP row keeps its own online softmax; partials go to the workspace and
 // the LSE merge kernel combines them.
 template <int WAVES, bool TRACE, int BITS>
-__global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
+// The kernel is VALU-bound; asking for five waves per SIMD keeps it at 95 VGPRs without spills.
+__global__ __launch_bounds__(WAVES * 64, 5) void cell_kernel(const CellParams p) {
   constexpr int D = 128, E = 8;
   constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
       m0 = fmaxf(m0, __shfl_xor(m0, 16));
       m0 = fmaxf(m0, __shfl_xor(m0, 32));
     }
-    const float thr = m0 - p.thr_offset;
+    const float thr2 = (m0 - p.thr_offset) * 1.4426950408889634f;  // hot test in the base-2 units of x[]
     constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
     const int n_cp = (n_far + kCodePage - 1) / kCodePage;
     const int c0 = (int)((int64_t)part * n_cp / p.n_splits);
@@ -289,10 +290,10 @@ __global__ __launch_bounds__(WAVES * 64) void cell_kernel(const CellParams p) {
       uint32_t hotbits = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float ssum = row_sum16(ps[i]);
+        const float x2 = row_sum16(ps[i]) * p.scale_log2;
         valid[i] = cp * kCodePage + g + 4 * i < n_far;
-        hot[i] = valid[i] && (!masked || ssum * p.scale >= thr);
-        x[i] = valid[i] ? ssum * p.scale_log2 : -INFINITY;
+        hot[i] = valid[i] && (!masked || x2 >= thr2);
+        x[i] = valid[i] ? x2 : -INFINITY;
         if (hot[i]) hotbits |= 1u << (g + 4 * i);
       }
       // online softmax of this row (x[] becomes p_j)

@@ -195,6 +195,31 @@ lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t lo
                             int32_t n_pages, const void* k_codes, const void* k_meta,
                             const void* v_codes, const void* v_meta, void* stream);
 
+/* Quantised caches: the window-exit codec.  Encode far-history code pages
+   [page0, page0 + n_pages) of (seq, layer, loop) from exact keys and values
+   ("LoopKV: Loop-Aware KV Cache Compression for Serving Looped Transformers",
+   Sec. 3.1: KIVI-style codes, keys per channel over the page's tokens and values
+   per token over 32 channels, each group with an fp16 scale and zero; Sec. 3.3:
+   INT4 value codes stored as hi and lo bit planes).  Per group: scale =
+   (max - min) / (2^bits - 1) in fp32, zero = min, both rounded to fp16 (nearest
+   even); code = rint((x - zero16) / scale16) clamped to [0, 2^bits - 1], 0 when
+   scale16 = 0.  bits follow the cell's plan (INT4 or INT2).
+   k, v: device bf16 [(n_pages - 1) * 32 + n_valid_last][n_heads_kv][head_dim],
+   caller-owned, holding positions sink + 32 page0 onwards; n_valid_last
+   (1..32) = valid tokens of the last page (the rest get code 0 and zero
+   metadata).  Errors as lkv_append_coded, plus EINVAL for n_valid_last. */
+lkv_status lkv_encode_pages(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0,
+                            int32_t n_pages, int32_t n_valid_last, const void* k, const void* v,
+                            void* stream);
+
+/* Quantised caches: read code pages back into the logical layout lkv_append_coded
+   takes (the inverse of its packing), into caller-owned device buffers of the
+   same shapes.  Errors: EINVAL (arguments, shared cell), ESTATE (page not
+   resident), EDEVICE. */
+lkv_status lkv_read_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0,
+                          int32_t n_pages, void* k_codes, void* k_meta, void* v_codes, void* v_meta,
+                          void* stream);
+
 /* Workspace an attend call needs (0 when it runs unsplit). */
 lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, size_t* bytes);
 

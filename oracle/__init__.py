@@ -13,6 +13,7 @@ and adds the closed-form memory and byte models the pages print:
 * ``split_partials``/``lse_merge`` -- LoopKV page, Sec. 3.4 and App. E Alg. 1;
 * ``cell_row``          -- LoopKV page, Sec. 3.1-3.4 (INT4 / INT2 / shared cells,
                            bit-plane V, fixed hot rule s >= m0 - offset);
+* ``kivi_encode``       -- LoopKV page, Sec. 3.1 and 3.3 (the window-exit codec);
 * ``mem_full``/``mem_deep``/``mem_ripe`` -- RIPE page, Eq. (3) and Eq. (10);
 * ``loopkv_bytes_per_token_layer`` -- LoopKV page, App. C byte model.
 
@@ -76,6 +77,13 @@ def _lib():
         L.oracle_cell_row.argtypes = [i32, i32, i32, i32, i32, pd, pd, pd, pu8, pd, pd, pu8, pd, pd, dbl, pd, pd,
                                       pu8]
         L.oracle_cell_row.restype = i32
+        L.oracle_kivi_encode.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                          pu8, ctypes.POINTER(ctypes.c_uint16), pu8, ctypes.POINTER(ctypes.c_uint16)]
+        L.oracle_kivi_encode.restype = None
+        L.oracle_f16_from_f32.argtypes = [ctypes.c_float]
+        L.oracle_f16_from_f32.restype = ctypes.c_uint16
+        L.oracle_f32_from_f16.argtypes = [ctypes.c_uint16]
+        L.oracle_f32_from_f16.restype = ctypes.c_float
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = i32
         _LIB = L
@@ -197,6 +205,33 @@ def cell_row(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink: int, tail: int, ki
     n_cold = _lib().oracle_cell_row(d, L, sink, tail, kind, qp, knp, vnp, kcp, ksp, kzp, vcp, vsp, vzp,
                                     float(thr_offset), outp, lsep, hotp)
     return out, float(lse[0]), hot, int(n_cold)
+
+
+def kivi_encode(k, v, bits: int):
+    """Window-exit codec of one far page of one head (LoopKV page, Sec. 3.1 and 3.3).  k, v: [n_tok][d]
+    exact values (float32).  Returns (k_codes [n_tok][d] u8, k_meta [d][2] fp16 bits, v_codes [n_tok][d] u8,
+    v_meta [n_tok][d/32][2] fp16 bits)."""
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    n, d = k.shape
+    assert v.shape == (n, d) and d % 32 == 0 and 1 <= n
+    kc = np.zeros((n, d), dtype=np.uint8)
+    vc = np.zeros((n, d), dtype=np.uint8)
+    km = np.zeros((d, 2), dtype=np.uint16)
+    vm = np.zeros((n, d // 32, 2), dtype=np.uint16)
+    pf = ctypes.POINTER(ctypes.c_float)
+    p16 = ctypes.POINTER(ctypes.c_uint16)
+    _lib().oracle_kivi_encode(n, d, bits, k.ctypes.data_as(pf), v.ctypes.data_as(pf), _u8(kc)[1],
+                              km.ctypes.data_as(p16), _u8(vc)[1], vm.ctypes.data_as(p16))
+    return kc, km, vc, vm
+
+
+def f16_from_f32(x: float) -> int:
+    return int(_lib().oracle_f16_from_f32(float(x)))
+
+
+def f32_from_f16(h: int) -> float:
+    return float(_lib().oracle_f32_from_f16(int(h)))
 
 
 # ----------------------------------------------------------------------------- closed-form models

@@ -259,6 +259,117 @@ int oracle_cell_row(int d, int L, int sink, int tail, int kind, const double* q,
   return n_cold;
 }
 
+/*
+ * The window-exit codec ([LoopKV] Sec. 3.1: KIVI-style codes, keys per channel and
+ * values per token in groups of 32 with an fp16 scale and zero; Sec. 3.3: the
+ * INT4 value code c is stored as hi = c >> 2 and lo = c & 3).  This is the
+ * encoder that turns one far page of exact keys and values into codes.
+ *
+ * Per group of values x (a key channel over the page's tokens, or a token's 32
+ * consecutive value channels):
+ *   mn, mx = smallest and largest x (exact);
+ *   sigma = (mx - mn) / (2^b - 1) in fp32 (one IEEE division), zero = mn;
+ *   both rounded to fp16, nearest-even: s16, z16;
+ *   c = clamp(rint((x - z16) / s16), 0, 2^b - 1) in fp32 (one subtraction and
+ *   one IEEE division, each rounded; rint rounds half to even); c = 0 if s16 = 0.
+ * The arithmetic is fp32 because the method stores fp16 metadata computed from
+ * fp32 statistics; no operation is fused.
+ */
+static uint32_t f32_bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+static float bits_f32(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* fp32 -> fp16 bits, IEEE round to nearest even (normal, subnormal, overflow to inf). */
+uint16_t oracle_f16_from_f32(float f) {
+  const uint32_t u = f32_bits(f);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x7F800000u) return (uint16_t)(sign | 0x7C00u | (a > 0x7F800000u ? 0x200u : 0u));
+  const int e = (int)(a >> 23) - 127; /* unbiased exponent */
+  uint32_t m = (a & 0x7FFFFFu) | (a >= 0x00800000u ? 0x800000u : 0u);
+  if (e > 15) return (uint16_t)(sign | 0x7C00u);
+  /* value = m * 2^(e - 23); fp16 quantum is 2^-24 for subnormals, 2^(e - 10) for normals */
+  const int q = e < -14 ? -24 : e - 10;
+  const int shift = q - (e - 23); /* bits of m below the fp16 quantum */
+  uint32_t h;
+  if (shift >= 32) {
+    h = 0;
+  } else {
+    const uint32_t kept = m >> shift, rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    h = kept + ((rem > half || (rem == half && (kept & 1u))) ? 1u : 0u);
+  }
+  /* h counts quanta: assemble, letting a carry roll into the exponent */
+  uint32_t out;
+  if (e < -14) {
+    out = h; /* subnormal, or the smallest normal after rounding up */
+  } else {
+    out = ((uint32_t)(e + 15) << 10) + (h - 0x400u);
+  }
+  if (out >= 0x7C00u) out = 0x7C00u;
+  return (uint16_t)(sign | out);
+}
+
+float oracle_f32_from_f16(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+  if (e == 0) {
+    const float v = (float)m * bits_f32(0x33800000u); /* m * 2^-24, exact */
+    return sign ? -v : v;
+  }
+  if (e == 31) return bits_f32(sign | 0x7F800000u | (m << 13));
+  return bits_f32(sign | ((e + 112u) << 23) | (m << 13));
+}
+
+static void encode_group(const float* x, int n, int stride, int levels, uint8_t* c, int cstride,
+                         uint16_t* s16, uint16_t* z16) {
+  float mn = x[0], mx = x[0];
+  for (int i = 1; i < n; ++i) {
+    const float v = x[(size_t)i * stride];
+    if (v < mn) mn = v;
+    if (v > mx) mx = v;
+  }
+  const float sigma = (mx - mn) / (float)levels;
+  *s16 = oracle_f16_from_f32(sigma);
+  *z16 = oracle_f16_from_f32(mn);
+  const float s = oracle_f32_from_f16(*s16), z = oracle_f32_from_f16(*z16);
+  for (int i = 0; i < n; ++i) {
+    float q = 0.0f;
+    if (s != 0.0f) {
+      const float t = (x[(size_t)i * stride] - z) / s;
+      q = rintf(t);
+      if (q < 0.0f) q = 0.0f;
+      if (q > (float)levels) q = (float)levels;
+    }
+    c[(size_t)i * cstride] = (uint8_t)q;
+  }
+}
+
+/*
+ * Encode one far page of one head: k, v are [n_tok][d] (exact values, here
+ * bf16 widened to fp32), n_tok <= 32 valid tokens, bits 4 or 2.
+ * Outputs: kc, vc [n_tok][d] codes; kmeta [d][2] (scale, zero) fp16 bits per key
+ * channel; vmeta [n_tok][d/32][2] per token and 32-channel group.
+ */
+void oracle_kivi_encode(int n_tok, int d, int bits, const float* k, const float* v, uint8_t* kc,
+                        uint16_t* kmeta, uint8_t* vc, uint16_t* vmeta) {
+  const int levels = (1 << bits) - 1;
+  for (int ch = 0; ch < d; ++ch)
+    encode_group(k + ch, n_tok, d, levels, kc + ch, d, &kmeta[2 * ch], &kmeta[2 * ch + 1]);
+  for (int t = 0; t < n_tok; ++t)
+    for (int g = 0; g < d / 32; ++g) {
+      uint16_t* m = &vmeta[((size_t)t * (d / 32) + g) * 2];
+      encode_group(v + (size_t)t * d + 32 * g, 32, 1, levels, vc + (size_t)t * d + 32 * g, 1, &m[0], &m[1]);
+    }
+}
+
 /* Threads the row-parallel routines use (OpenMP), for reporting. */
 int oracle_threads(void) {
   int n = 1;

@@ -228,3 +228,25 @@ def test_plan_rules(lib):
     c.lkv_set_plan(plan)
     assert ha.sizes.code4_page_bytes == 16 * 160 * 32  # LoopKV page App. C: 2.5 KiB per token and layer
     assert ha.sizes.code2_page_bytes == 16 * 96 * 32   # 1.5 KiB
+
+
+def test_quant_workspace_matches_the_cell_split_rule(lib):
+    """lkv_workspace_bytes sizes a quantised-cell call by the same split rule lkv_attend uses: far splits
+    min(64, ceil(2048 / (seqs * heads))), at most one per code page, plus the near part."""
+    cfg = vla.LoopCache.config(n_layers=1, n_loops=2, n_heads_q=4, n_heads_kv=4, head_dim=128,
+                               kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=3, max_len=2000,
+                               max_block=1, quant=1, sink=4, tail=128)
+    s = vla.LoopCache.sizes(cfg)
+    meta = np.zeros(max(256, s.meta_bytes), dtype=np.uint8)
+    base = 1 << 40
+    ar = vla.lkv_arenas(base, 256 * s.page_bytes, base + (1 << 38), 256 * s.code4_page_bytes, base + (1 << 39),
+                        256 * s.code2_page_bytes, meta.ctypes.data, s.meta_bytes)
+    c = vla.LoopCache(cfg, ar, 0)
+    seqs = [c.lkv_add_seq() for _ in range(3)]
+    for sq, L in zip(seqs, (2000, 400, 140)):
+        c.lkv_reserve(sq, 0, 0, 0, L)
+    rows = 3 * 4
+    n_cp = (2000 - 132 + 31) // 32
+    S = min(64, -(-2048 // rows), n_cp)
+    assert c.lkv_workspace_bytes(0, 0, seqs) == rows * (S + 1) * 129 * 4
+    assert c.lkv_workspace_bytes(0, 0, seqs[2:], split_k=5) == 4 * (1 + 1) * 129 * 4  # 1 code page caps the splits

@@ -24,7 +24,8 @@ PAGE_TOKENS, CODE_PAGE_TOKENS = 16, 32
 
 EXPORTS = [
     "lkv_sizes", "lkv_create", "lkv_destroy", "lkv_add_seq", "lkv_free_seq", "lkv_reserve", "lkv_append_plane",
-    "lkv_commit", "lkv_truncate", "lkv_set_plan", "lkv_append_coded", "lkv_workspace_bytes", "lkv_attend",
+    "lkv_commit", "lkv_truncate", "lkv_set_plan", "lkv_append_coded", "lkv_encode_pages", "lkv_read_coded",
+    "lkv_workspace_bytes", "lkv_attend",
     "lkv_mem_stats", "lkv_debug_resolve", "lkv_seq_info", "lkv_last_error", "lkv_status_str",
 ]
 
@@ -94,6 +95,8 @@ def load():
         "lkv_truncate": [vp, i32, i32],
         "lkv_set_plan": [vp, P(ctypes.c_int8)],
         "lkv_append_coded": [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp],
+        "lkv_encode_pages": [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp],
+        "lkv_read_coded": [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "lkv_workspace_bytes": [vp, P(lkv_attend_args), P(ctypes.c_size_t)],
         "lkv_attend": [vp, P(lkv_attend_args), vp],
         "lkv_mem_stats": [vp, P(lkv_mem_info)],
@@ -223,6 +226,16 @@ class LoopCache:
                          v_meta, stream=None):
         self._check(self.lib.lkv_append_coded(self.h, seq, layer, loop, page0, n_pages, _ptr(k_codes), _ptr(k_meta),
                                               _ptr(v_codes), _ptr(v_meta), _stream(stream)), "lkv_append_coded")
+
+    def lkv_encode_pages(self, seq: int, layer: int, loop: int, page0: int, n_pages: int, n_valid_last: int, k, v,
+                         stream=None):
+        self._check(self.lib.lkv_encode_pages(self.h, seq, layer, loop, page0, n_pages, n_valid_last, _ptr(k), _ptr(v),
+                                              _stream(stream)), "lkv_encode_pages")
+
+    def lkv_read_coded(self, seq: int, layer: int, loop: int, page0: int, n_pages: int, k_codes, k_meta, v_codes,
+                       v_meta, stream=None):
+        self._check(self.lib.lkv_read_coded(self.h, seq, layer, loop, page0, n_pages, _ptr(k_codes), _ptr(k_meta),
+                                            _ptr(v_codes), _ptr(v_meta), _stream(stream)), "lkv_read_coded")
 
     def _args(self, layer, loop, seq_ids, q, out, q_len=1, mode=MODE_DECODE, window=-1, split_k=0,
               v_thresh_offset=4.0, lse=None, workspace=None, draft_k=None, draft_v=None, draft_len=0,

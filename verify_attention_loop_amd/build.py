@@ -29,7 +29,8 @@ def hipcc() -> str:
 
 def flags() -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fhip-fp32-correctly-rounded-divide-sqrt",
+            "-Wno-unused-command-line-argument"]
 
 
 def _compile(src: str, obj: str):

@@ -26,6 +26,9 @@ hipError_t launch_append(const CopyParams& p, int dtype, int head_dim, hipStream
 hipError_t launch_fill(void* dst, uint64_t n_bytes, uint32_t value, hipStream_t s);
 hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s);
 hipError_t launch_pack_codes(const PackParams& p, int head_dim, hipStream_t s);
+hipError_t launch_encode_pages(const EncodeParams& p, int head_dim, hipStream_t s);
+hipError_t launch_read_codes(const PackParams& p, int head_dim, void* k_codes, void* k_meta, void* v_codes,
+                             void* v_meta, hipStream_t s);
 uint64_t code_page_bytes(int hkv, int head_dim, int bits);
 }  // namespace lkv
 
@@ -492,32 +495,35 @@ lkv_status lkv_set_plan(lkv_cache* c, const int8_t* kinds) {
   return LKV_OK;
 }
 
-lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0, int32_t n_pages,
-                            const void* k_codes, const void* k_meta, const void* v_codes, const void* v_meta,
-                            void* stream) {
-  if (!c) return LKV_EINVAL;
+// Checks shared by the code-page calls; on success fills the cell's table, free list,
+// arena, page size and bit width.
+static lkv_status code_cell(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0, int32_t n_pages,
+                            Table** T, FreeList** fl, uint8_t** arena, uint64_t* cpb, int* bits) {
   if (!c->cfg.quant) return c->fail(LKV_ESTATE, "the cache has no quantised cells");
   if (!c->plan_set) return c->fail(LKV_ESTATE, "lkv_set_plan first");
   if (!c->live(seq)) return c->fail(LKV_EINVAL, "sequence %d is not live", seq);
   if (layer < 0 || layer >= c->cfg.n_layers || loop < 0 || loop >= c->cfg.n_loops)
     return c->fail(LKV_EINVAL, "cell (%d, %d) out of range", layer, loop);
-  if (!k_codes || !k_meta || !v_codes || !v_meta) return c->fail(LKV_EINVAL, "NULL code buffer");
   const int8_t kind = c->plan[(size_t)layer * c->cfg.n_loops + loop];
   if (kind == LKV_CELL_SHARED) return c->fail(LKV_EINVAL, "cell (%d, %d) is shared and stores no pages", layer, loop);
   if (page0 < 0 || n_pages < 1 || page0 + n_pages > c->max_code_pages)
     return c->fail(LKV_EINVAL, "code pages [%d, %d) outside [0, %d)", page0, page0 + n_pages, c->max_code_pages);
-  Table& T = c->ctab(layer, loop);
-  FreeList& fl = kind == LKV_CELL_INT2 ? c->codes2 : c->codes4;
-  const uint64_t cpb = kind == LKV_CELL_INT2 ? c->code2_bytes : c->code4_bytes;
-  uint8_t* arena = (uint8_t*)(kind == LKV_CELL_INT2 ? c->ar.codes2 : c->ar.codes4);
+  *T = &c->ctab(layer, loop);
+  *fl = kind == LKV_CELL_INT2 ? &c->codes2 : &c->codes4;
+  *cpb = kind == LKV_CELL_INT2 ? c->code2_bytes : c->code4_bytes;
+  *arena = (uint8_t*)(kind == LKV_CELL_INT2 ? c->ar.codes2 : c->ar.codes4);
+  *bits = kind == LKV_CELL_INT2 ? 2 : 4;
+  return LKV_OK;
+}
+
+// Hand out the pages [page0, page0 + n_pages) of a cell that are not resident yet.
+static lkv_status claim_code_pages(lkv_cache* c, Table& T, FreeList& fl, int32_t seq, int32_t page0,
+                                   int32_t n_pages) {
   int64_t need = 0;
   for (int p = page0; p < page0 + n_pages; ++p)
     if (T.owner[(size_t)seq * T.ring + p] != p) ++need;
   if (need > fl.available())
     return c->fail(LKV_ENOMEM, "need %lld code pages, %lld free", (long long)need, (long long)fl.available());
-  const int bits = kind == LKV_CELL_INT2 ? 2 : 4;
-  const int hkv = c->cfg.n_heads_kv, d = c->cfg.head_dim;
-  hipStream_t s = (hipStream_t)stream;
   for (int p = page0; p < page0 + n_pages; ++p) {
     const size_t i = (size_t)seq * T.ring + p;
     if (T.owner[i] != p) {
@@ -526,6 +532,25 @@ lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t lo
       T.dirty[(size_t)seq] = 1;
     }
   }
+  T.hi[(size_t)seq] = std::max(T.hi[(size_t)seq], page0 + n_pages);
+  return LKV_OK;
+}
+
+lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0, int32_t n_pages,
+                            const void* k_codes, const void* k_meta, const void* v_codes, const void* v_meta,
+                            void* stream) {
+  if (!c) return LKV_EINVAL;
+  Table* T;
+  FreeList* fl;
+  uint8_t* arena;
+  uint64_t cpb;
+  int bits;
+  lkv_status st = code_cell(c, seq, layer, loop, page0, n_pages, &T, &fl, &arena, &cpb, &bits);
+  if (st != LKV_OK) return st;
+  if (!k_codes || !k_meta || !v_codes || !v_meta) return c->fail(LKV_EINVAL, "NULL code buffer");
+  if ((st = claim_code_pages(c, *T, *fl, seq, page0, n_pages)) != LKV_OK) return st;
+  const int hkv = c->cfg.n_heads_kv, d = c->cfg.head_dim;
+  hipStream_t s = (hipStream_t)stream;
   for (int q0 = page0; q0 < page0 + n_pages; q0 += 64) {
     PackParams P{};
     P.arena = arena;
@@ -538,11 +563,77 @@ lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t lo
     P.hkv = hkv;
     P.bits = bits;
     P.n_pages = std::min(64, page0 + n_pages - q0);
-    for (int x = 0; x < P.n_pages; ++x) P.phys[x] = T.phys[(size_t)seq * T.ring + q0 + x];
+    for (int x = 0; x < P.n_pages; ++x) P.phys[x] = T->phys[(size_t)seq * T->ring + q0 + x];
     hipError_t e = launch_pack_codes(P, d, s);
     if (e != hipSuccess) return hip_fail(c, e, "pack kernel");
   }
-  T.hi[(size_t)seq] = std::max(T.hi[(size_t)seq], page0 + n_pages);
+  return LKV_OK;
+}
+
+lkv_status lkv_encode_pages(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0, int32_t n_pages,
+                            int32_t n_valid_last, const void* k, const void* v, void* stream) {
+  if (!c) return LKV_EINVAL;
+  Table* T;
+  FreeList* fl;
+  uint8_t* arena;
+  uint64_t cpb;
+  int bits;
+  lkv_status st = code_cell(c, seq, layer, loop, page0, n_pages, &T, &fl, &arena, &cpb, &bits);
+  if (st != LKV_OK) return st;
+  if (!k || !v) return c->fail(LKV_EINVAL, "k and v must not be NULL");
+  if (n_valid_last < 1 || n_valid_last > kCodePage)
+    return c->fail(LKV_EINVAL, "n_valid_last %d outside [1, %d]", n_valid_last, kCodePage);
+  if ((st = claim_code_pages(c, *T, *fl, seq, page0, n_pages)) != LKV_OK) return st;
+  const int hkv = c->cfg.n_heads_kv, d = c->cfg.head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  for (int q0 = page0; q0 < page0 + n_pages; q0 += 64) {
+    EncodeParams P{};
+    P.arena = arena;
+    P.page_bytes = cpb;
+    const int64_t off = (int64_t)(q0 - page0) * kCodePage * hkv * d;
+    P.k = (const uint16_t*)k + off;
+    P.v = (const uint16_t*)v + off;
+    P.hkv = hkv;
+    P.bits = bits;
+    P.n_pages = std::min(64, page0 + n_pages - q0);
+    P.n_valid_last = q0 + P.n_pages == page0 + n_pages ? n_valid_last : kCodePage;
+    for (int x = 0; x < P.n_pages; ++x) P.phys[x] = T->phys[(size_t)seq * T->ring + q0 + x];
+    hipError_t e = launch_encode_pages(P, d, s);
+    if (e != hipSuccess) return hip_fail(c, e, "encode kernel");
+  }
+  return LKV_OK;
+}
+
+lkv_status lkv_read_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0, int32_t n_pages,
+                          void* k_codes, void* k_meta, void* v_codes, void* v_meta, void* stream) {
+  if (!c) return LKV_EINVAL;
+  Table* T;
+  FreeList* fl;
+  uint8_t* arena;
+  uint64_t cpb;
+  int bits;
+  lkv_status st = code_cell(c, seq, layer, loop, page0, n_pages, &T, &fl, &arena, &cpb, &bits);
+  if (st != LKV_OK) return st;
+  if (!k_codes || !k_meta || !v_codes || !v_meta) return c->fail(LKV_EINVAL, "NULL code buffer");
+  for (int p = page0; p < page0 + n_pages; ++p)
+    if (T->owner[(size_t)seq * T->ring + p] != p)
+      return c->fail(LKV_ESTATE, "code page %d of cell (%d, %d) is not resident", p, layer, loop);
+  const int hkv = c->cfg.n_heads_kv, d = c->cfg.head_dim;
+  hipStream_t s = (hipStream_t)stream;
+  for (int q0 = page0; q0 < page0 + n_pages; q0 += 64) {
+    PackParams P{};
+    P.arena = arena;
+    P.page_bytes = cpb;
+    P.hkv = hkv;
+    P.bits = bits;
+    P.n_pages = std::min(64, page0 + n_pages - q0);
+    for (int x = 0; x < P.n_pages; ++x) P.phys[x] = T->phys[(size_t)seq * T->ring + q0 + x];
+    const int64_t k = q0 - page0;
+    hipError_t e = launch_read_codes(P, d, (uint8_t*)k_codes + k * kCodePage * hkv * d,
+                                     (uint8_t*)k_meta + k * hkv * d * 4, (uint8_t*)v_codes + k * kCodePage * hkv * d,
+                                     (uint8_t*)v_meta + k * kCodePage * hkv * (d / 32) * 4, s);
+    if (e != hipSuccess) return hip_fail(c, e, "read kernel");
+  }
   return LKV_OK;
 }
 
@@ -626,18 +717,30 @@ int auto_splits(const lkv_cache* c, int n_seqs, int q_len, int max_pages) {
   return std::max(1, std::min(s, 64));
 }
 
+// Far splits of a quantised-cell call: enough (split, head, seq) workgroups to fill the
+// chip, at most one per code page and at most 64.
+int cell_splits(const lkv_cache* c, int n_seqs, int split_k, int max_code_pages) {
+  const int rows = n_seqs * c->cfg.n_heads_q;
+  int S = split_k > 0 ? split_k : std::max(1, std::min(64, (env_int("LKV_TARGET_WGS", 2048) + rows - 1) / rows));
+  return std::min(S, std::max(1, max_code_pages));
+}
+
 }  // namespace
 
 extern "C" {
 
 lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, size_t* bytes) {
   if (!c || !a || !bytes) return LKV_EINVAL;
-  int max_pages = 0;
+  int max_pages = 0, max_cp = 0;
   for (int b = 0; b < a->n_seqs && a->seq_ids; ++b) {
     const int32_t s = a->seq_ids[b];
-    if (s >= 0 && s < c->cfg.max_seqs) max_pages = std::max(max_pages, (c->seqs[(size_t)s].len + kPage - 1) / kPage);
+    if (s < 0 || s >= c->cfg.max_seqs) continue;
+    const int L = c->seqs[(size_t)s].len;
+    max_pages = std::max(max_pages, (L + kPage - 1) / kPage);
+    max_cp = std::max(max_cp, (std::max(0, L - c->cfg.sink - c->cfg.tail) + kCodePage - 1) / kCodePage);
   }
-  const int S = a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->q_len, max_pages);
+  const int S = c->cfg.quant ? cell_splits(c, a->n_seqs, a->split_k, max_cp)
+                             : (a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->q_len, max_pages));
   const int parts = c->cfg.quant ? S + 1 : S;
   if (parts <= 1) {
     *bytes = 0;
@@ -795,9 +898,7 @@ static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_
   }
   const int D = cfg.head_dim, hq = cfg.n_heads_q;
   const int max_cp = (max_far + kCodePage - 1) / kCodePage;
-  int S = a->split_k > 0 ? a->split_k : std::max(1, std::min(64, (env_int("LKV_TARGET_WGS", 2048) + a->n_seqs * hq - 1) /
-                                                                  (a->n_seqs * hq)));
-  S = std::min(S, std::max(1, max_cp));
+  const int S = cell_splits(c, a->n_seqs, a->split_k, max_cp);
   const size_t ws_need = (size_t)a->n_seqs * hq * (S + 1) * (D + 1) * 4;
   if (!a->workspace || a->workspace_bytes < ws_need)
     return c->fail(LKV_ENOMEM, "workspace of %zu bytes needed", ws_need);

@@ -38,26 +38,18 @@ uint64_t code_page_bytes(int hkv, int head_dim, int bits) {
 __host__ __device__ __forceinline__ int hi_crumb(int c) { return c < 4 ? 2 * c + 1 : 2 * (c - 4); }
 __host__ __device__ __forceinline__ int lo_crumb(int c) { return c < 4 ? 2 * c : 2 * (c - 4) + 1; }
 
-// One thread per (head, token, lane li) of one page (blockIdx.y = page of the batch):
-// packs that lane's 8 channels of one token into the page's lane-major layout.
-__global__ __launch_bounds__(256) void pack_codes_kernel(const PackParams p) {
+// Byte offsets inside one head's slice of a code page (d = 128).
+__host__ __device__ constexpr uint64_t code_head_bytes(int bits) { return (uint64_t)(bits == 4 ? 40 : 24) * 128; }
+__host__ __device__ constexpr uint64_t vcode_offset(int bits) { return (bits == 4 ? 20 : 12) * 128; }
+__host__ __device__ constexpr uint64_t vmeta_offset(int bits) { return (bits == 4 ? 36 : 20) * 128; }
+
+// Store lane li's 8 channels of token tok (codes kin[0..7], vin[0..7]) into the head
+// slice hb.  Lanes li < 4 also store the token's V metadata of group li (vm_src:
+// scale, zero), tokens tok < 8 the K metadata of channel 16 tok + li (km_src).
+__device__ __forceinline__ void pack_item(uint8_t* hb, int bits, int tok, int li, const uint8_t* kin,
+                                          const uint8_t* vin, const uint16_t* vm_src, const uint16_t* km_src) {
   constexpr int D = 128;
-  const int pi = blockIdx.y;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const int hkv = p.hkv, bits = p.bits;
-  if (idx >= hkv * kCodePage * 16 || pi >= p.n_pages) return;
-  const int li = idx & 15;
-  const int tok = (idx >> 4) & 31;
-  const int h = idx >> 9;
   const int g = tok & 3, i = tok >> 2;
-  uint8_t* page = p.arena + (uint64_t)p.phys[pi] * p.page_bytes;
-  const uint8_t* kc = p.k_codes + (int64_t)pi * kCodePage * hkv * D;
-  const uint8_t* vc = p.v_codes + (int64_t)pi * kCodePage * hkv * D;
-  const uint16_t* km = p.k_meta + (int64_t)pi * hkv * D * 2;
-  const uint16_t* vm = p.v_meta + (int64_t)pi * kCodePage * hkv * (D / 32) * 2;
-  uint8_t* hb = page + (uint64_t)h * (bits == 4 ? 40 : 24) * D;
-  const uint8_t* kin = kc + ((int64_t)tok * hkv + h) * D + 8 * li;
-  const uint8_t* vin = vc + ((int64_t)tok * hkv + h) * D + 8 * li;
   if (bits == 4) {
     uint32_t kw = 0, vhi = 0, vlo = 0;
     for (int c = 0; c < 8; ++c) {
@@ -78,22 +70,165 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const PackParams p) {
     *reinterpret_cast<uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)kw;
     *reinterpret_cast<uint16_t*>(hb + 12 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)vw;
   }
-  // V meta: group li & 3 of this token (threads li < 4)
   if (li < 4) {
-    const int grp = li;
-    const uint16_t* src = vm + (((int64_t)tok * hkv + h) * (D / 32) + grp) * 2;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(hb + (bits == 4 ? 36 : 20) * D + ((g * 4 + grp) * 8 + i) * 4);
-    dst[0] = src[0];
-    dst[1] = src[1];
+    uint16_t* dst = reinterpret_cast<uint16_t*>(hb + vmeta_offset(bits) + ((g * 4 + li) * 8 + i) * 4);
+    dst[0] = vm_src[0];
+    dst[1] = vm_src[1];
   }
-  // K meta: channel tok * 16 + li (tokens 0..7 cover the 128 channels)
   if (tok < 8) {
-    const int c = tok * 16 + li;
-    const uint16_t* src = km + ((int64_t)h * D + c) * 2;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(hb + c * 4);
-    dst[0] = src[0];
-    dst[1] = src[1];
+    uint16_t* dst = reinterpret_cast<uint16_t*>(hb + (tok * 16 + li) * 4);
+    dst[0] = km_src[0];
+    dst[1] = km_src[1];
   }
+}
+
+// Inverse of pack_item: read lane li's 8 channels of token tok back into plain codes.
+__device__ __forceinline__ void unpack_item(const uint8_t* hb, int bits, int tok, int li, uint8_t* kout,
+                                            uint8_t* vout, uint16_t* vm_dst, uint16_t* km_dst) {
+  constexpr int D = 128;
+  const int g = tok & 3, i = tok >> 2;
+  if (bits == 4) {
+    const int hh = i >> 2, ii = i & 3;
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(hb + 4 * D + hh * 1024 + (g * 16 + li) * 16 + ii * 4);
+    const uint32_t vhi = *reinterpret_cast<const uint16_t*>(hb + 20 * D + (g * 16 + li) * 16 + i * 2);
+    const uint32_t vlo = *reinterpret_cast<const uint16_t*>(hb + 28 * D + tok * 32 + li * 2);
+    for (int c = 0; c < 8; ++c) {
+      kout[c] = (uint8_t)((kw >> (4 * c)) & 15u);
+      vout[c] = (uint8_t)((((vhi >> (2 * hi_crumb(c))) & 3u) << 2) | ((vlo >> (2 * lo_crumb(c))) & 3u));
+    }
+  } else {
+    const uint32_t kw = *reinterpret_cast<const uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + i * 2);
+    const uint32_t vw = *reinterpret_cast<const uint16_t*>(hb + 12 * D + (g * 16 + li) * 16 + i * 2);
+    for (int c = 0; c < 8; ++c) {
+      kout[c] = (uint8_t)((kw >> (2 * lo_crumb(c))) & 3u);
+      vout[c] = (uint8_t)((vw >> (2 * lo_crumb(c))) & 3u);
+    }
+  }
+  if (li < 4) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(hb + vmeta_offset(bits) + ((g * 4 + li) * 8 + i) * 4);
+    vm_dst[0] = src[0];
+    vm_dst[1] = src[1];
+  }
+  if (tok < 8) {
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(hb + (tok * 16 + li) * 4);
+    km_dst[0] = src[0];
+    km_dst[1] = src[1];
+  }
+}
+
+// One thread per (head, token, lane li) of one page (blockIdx.y = page of the batch):
+// packs that lane's 8 channels of one token from the logical arrays.
+__global__ __launch_bounds__(256) void pack_codes_kernel(const PackParams p) {
+  constexpr int D = 128;
+  const int pi = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int hkv = p.hkv;
+  if (idx >= hkv * kCodePage * 16 || pi >= p.n_pages) return;
+  const int li = idx & 15, tok = (idx >> 4) & 31, h = idx >> 9;
+  uint8_t* hb = p.arena + (uint64_t)p.phys[pi] * p.page_bytes + (uint64_t)h * code_head_bytes(p.bits);
+  const int64_t row = ((int64_t)pi * kCodePage + tok) * hkv + h;
+  pack_item(hb, p.bits, tok, li, p.k_codes + row * D + 8 * li, p.v_codes + row * D + 8 * li,
+            p.v_meta + (row * (D / 32) + (li & 3)) * 2,
+            p.k_meta + (((int64_t)pi * hkv + h) * D + ((tok & 7) * 16 + li)) * 2);
+}
+
+// Inverse: one thread per (head, token, lane li) of one page, into the logical arrays.
+__global__ __launch_bounds__(256) void read_codes_kernel(const PackParams p, uint8_t* k_codes, uint16_t* k_meta,
+                                                         uint8_t* v_codes, uint16_t* v_meta) {
+  constexpr int D = 128;
+  const int pi = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int hkv = p.hkv;
+  if (idx >= hkv * kCodePage * 16 || pi >= p.n_pages) return;
+  const int li = idx & 15, tok = (idx >> 4) & 31, h = idx >> 9;
+  const uint8_t* hb = p.arena + (uint64_t)p.phys[pi] * p.page_bytes + (uint64_t)h * code_head_bytes(p.bits);
+  const int64_t row = ((int64_t)pi * kCodePage + tok) * hkv + h;
+  unpack_item(hb, p.bits, tok, li, k_codes + row * D + 8 * li, v_codes + row * D + 8 * li,
+              v_meta + (row * (D / 32) + (li & 3)) * 2, k_meta + (((int64_t)pi * hkv + h) * D + ((tok & 7) * 16 + li)) * 2);
+}
+
+// The window-exit codec (LoopKV page, Sec. 3.1 and 3.3; KIVI-style): one workgroup
+// of 128 threads per (page, head) encodes 32 tokens of exact bf16 keys and values.
+// Keys: one group per channel over the page's valid tokens; values: one group per
+// token and 32 channels.  Per group: mn, mx; scale = (mx - mn) / (2^b - 1) in fp32
+// (IEEE division), zero = mn, both rounded to fp16 (nearest even); a value's code is
+// rint((x - zero16) / scale16) clamped to [0, 2^b - 1] (0 when scale16 = 0), each
+// operation rounded in fp32.  Tokens past n_valid of the last page get code 0 and
+// zero metadata.  The codes go through LDS into the page's packed layout.
+__device__ __forceinline__ float bf16_bits_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ void encode_group(const uint16_t* x, int n, int stride, int levels, uint8_t* c,
+                                             int cstride, uint16_t* meta) {
+  float mn = bf16_bits_f32(x[0]), mx = mn;
+  for (int i = 1; i < n; ++i) {
+    const float v = bf16_bits_f32(x[(int64_t)i * stride]);
+    if (v < mn) mn = v;
+    if (v > mx) mx = v;
+  }
+  const float sigma = (mx - mn) / (float)levels;  // correctly rounded (HIP's fp32 division)
+  const _Float16 s16 = (_Float16)sigma, z16 = (_Float16)mn;  // v_cvt_f16_f32: nearest even
+  const float sf = (float)s16, zf = (float)z16;
+  for (int i = 0; i < n; ++i) {
+    float q = 0.f;
+    if (sf != 0.f) {
+      q = rintf((bf16_bits_f32(x[(int64_t)i * stride]) - zf) / sf);
+      q = fminf(fmaxf(q, 0.f), (float)levels);
+    }
+    c[i * cstride] = (uint8_t)q;
+  }
+  meta[0] = __builtin_bit_cast(uint16_t, s16);
+  meta[1] = __builtin_bit_cast(uint16_t, z16);
+}
+
+__global__ __launch_bounds__(128) void encode_pages_kernel(const EncodeParams p) {
+  constexpr int D = 128;
+  const int pi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (pi >= p.n_pages || h >= p.hkv) return;  // uniform per workgroup
+  const int n = pi == p.n_pages - 1 ? p.n_valid_last : kCodePage;
+  const int levels = (1 << p.bits) - 1;
+  __shared__ uint8_t kc[kCodePage][D], vc[kCodePage][D];
+  __shared__ uint16_t km[D][2], vm[kCodePage][4][2];
+  const int64_t tok_stride = (int64_t)p.hkv * D;
+  const uint16_t* kin = p.k + ((int64_t)pi * kCodePage * p.hkv + h) * D;
+  const uint16_t* vin = p.v + ((int64_t)pi * kCodePage * p.hkv + h) * D;
+  // keys: thread = channel
+  encode_group(kin + tid, n, (int)tok_stride, levels, &kc[0][tid], D, km[tid]);
+  for (int t = n; t < kCodePage; ++t) kc[t][tid] = 0;
+  // values: thread = (token, 32-channel group)
+  {
+    const int t = tid >> 2, grp = tid & 3;
+    if (t < n) {
+      encode_group(vin + t * tok_stride + 32 * grp, 32, 1, levels, &vc[t][32 * grp], 1, vm[t][grp]);
+    } else {
+      for (int c = 0; c < 32; ++c) vc[t][32 * grp + c] = 0;
+      vm[t][grp][0] = 0;
+      vm[t][grp][1] = 0;
+    }
+  }
+  __syncthreads();
+  uint8_t* hb = p.arena + (uint64_t)p.phys[pi] * p.page_bytes + (uint64_t)h * code_head_bytes(p.bits);
+  for (int it = tid; it < kCodePage * 16; it += 128) {
+    const int tok = it >> 4, li = it & 15;
+    pack_item(hb, p.bits, tok, li, &kc[tok][8 * li], &vc[tok][8 * li], vm[tok][li & 3], km[(tok & 7) * 16 + li]);
+  }
+}
+
+hipError_t launch_encode_pages(const EncodeParams& p, int head_dim, hipStream_t s) {
+  if (head_dim != 128 || p.n_pages < 1 || p.n_pages > 64 || p.n_valid_last < 1 || p.n_valid_last > kCodePage ||
+      (p.bits != 4 && p.bits != 2))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(encode_pages_kernel, dim3(p.n_pages, p.hkv), dim3(128), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_read_codes(const PackParams& p, int head_dim, void* k_codes, void* k_meta, void* v_codes,
+                             void* v_meta, hipStream_t s) {
+  if (head_dim != 128 || p.n_pages < 1 || p.n_pages > 64) return hipErrorInvalidValue;
+  const int n = p.hkv * kCodePage * 16;
+  hipLaunchKernelGGL(read_codes_kernel, dim3((n + 255) / 256, p.n_pages), dim3(256), 0, s, p,
+                     reinterpret_cast<uint8_t*>(k_codes), reinterpret_cast<uint16_t*>(k_meta),
+                     reinterpret_cast<uint8_t*>(v_codes), reinterpret_cast<uint16_t*>(v_meta));
+  return hipGetLastError();
 }
 
 hipError_t launch_pack_codes(const PackParams& p, int head_dim, hipStream_t s) {

@@ -103,6 +103,19 @@ struct PackParams {
   int32_t phys[64];           // physical page of batch page i
 };
 
+// Encode exact bf16 keys and values of up to 64 far pages into code pages (the
+// window-exit codec).
+struct EncodeParams {
+  uint8_t* arena;
+  uint64_t page_bytes;
+  const uint16_t* k;          // bf16 [n_pages * 32][hkv][D]
+  const uint16_t* v;
+  int32_t hkv, bits;
+  int32_t n_pages;
+  int32_t n_valid_last;       // valid tokens of the last page (1..32)
+  int32_t phys[64];
+};
+
 // Append rows into plain pages.
 struct CopyParams {
   uint8_t* pool;

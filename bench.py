@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="huginn_ripe",
-                    choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "loopkv_cells"])
+                    choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "loopkv_cells", "raven_ripe"])
     ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers held in HBM (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -86,12 +86,13 @@ def cpu_baseline(w, seconds: float):
     loops = np.empty(n_rows, dtype=np.int32)
     for i in range(n_rows):
         b, h, r = int(rng.integers(w.batch)), int(rng.integers(w.n_heads)), int(rng.integers(R))
+        hk = h // (w.n_heads // w.hkv)  # the query head's KV head
         loops[i] = r
-        ko[i] = harness.cpu_values(w, synth.T_K, b, 0, r, h, L)
-        vo[i] = harness.cpu_values(w, synth.T_V, b, 0, r, h, L)
+        ko[i] = harness.cpu_values(w, synth.T_K, b, 0, r, hk, L)
+        vo[i] = harness.cpu_values(w, synth.T_V, b, 0, r, hk, L)
         if pol == oracle.RIPE and r != R - 1:
-            kd[i] = harness.cpu_values(w, synth.T_K, b, 0, R - 1, h, L)
-            vd[i] = harness.cpu_values(w, synth.T_V, b, 0, R - 1, h, L)
+            kd[i] = harness.cpu_values(w, synth.T_K, b, 0, R - 1, hk, L)
+            vd[i] = harness.cpu_values(w, synth.T_V, b, 0, R - 1, hk, L)
         else:
             kd[i], vd[i] = ko[i], vo[i]
         q[i] = harness.cpu_query(w, b, 0, r, h, L - 1)
@@ -282,6 +283,7 @@ def main():
         data = ("synthetic (seeded counter-hash generator; Huginn-shaped ripening planes)"
                 if w.mode == synth.MODE_RIPEN else "synthetic (seeded counter-hash generator)")
     cfg = {"workload": w.name, "batch": B, "core_layers": w.n_layers, "loops": R, "heads": w.n_heads,
+           "kv_heads": w.hkv,
            "head_dim": w.head_dim, "context": w.length, "q_len": q_len, "policy": w.policy, "window": w.window,
            "page_tokens": 32 if w.quant else 16, "split_k": split, "calls_per_step": len(calls),
            "layers_resident": len(layers), "kernel_ms_per_step": round(float(kern_ms.sum(axis=1).mean()), 4),

@@ -71,14 +71,14 @@ def build_plain(w: synth.Workload, *, lengths=None, layers=(0,), planes=None, po
     if policy == vla.POLICY_RIPE and R - 1 not in planes:
         planes = planes + [R - 1]
     n_pages = pages_needed(w, lengths, layers, planes, policy, W, q_len) + extra_pages
-    cfg = vla.LoopCache.config(n_layers=w.n_layers, n_loops=R, n_heads_q=w.n_heads, n_heads_kv=w.n_heads,
+    cfg = vla.LoopCache.config(n_layers=w.n_layers, n_loops=R, n_heads_q=w.n_heads, n_heads_kv=w.hkv,
                                head_dim=w.head_dim, kv_dtype=w.dtype, policy=policy, window=W,
                                max_seqs=len(lengths), max_len=max_len or max(lengths),
                                max_block=max_block or max(1, q_len),
                                poison=1 if poison else 0, shuffle_seed=(0x5EED + seed) if shuffle else 0)
     cache = vla.LoopCache.on_device(cfg, n_pages)
     dt = torch_dtype(w.dtype)
-    H, d = w.n_heads, w.head_dim
+    H, d = w.hkv, w.head_dim  # keys and values per KV head
     stream = torch.cuda.current_stream().cuda_stream
     seqs = []
     chunk = min(chunk_tokens, max(lengths))
@@ -123,8 +123,8 @@ def gpu_queries(built: Built, layer: int, loop: int, q_len: int, t0s=None, seed=
 
 
 def cpu_values(w: synth.Workload, tensor: int, b: int, layer: int, plane: int, head: int, n_pos: int, seed=None):
-    """fp64 values [n_pos][d] of one (tensor, row, layer, plane, head), as the cache holds them."""
-    x = synth.kv(w.dtype, w.seed if seed is None else seed, tensor, b, layer, plane, w.n_heads, w.head_dim, 0,
+    """fp64 values [n_pos][d] of one (tensor, row, layer, plane, KV head), as the cache holds them."""
+    x = synth.kv(w.dtype, w.seed if seed is None else seed, tensor, b, layer, plane, w.hkv, w.head_dim, 0,
                  n_pos, w.mode, w.n_loops, w.scale, heads=[head])[:, 0, :]
     return to_f64(x, w.dtype)
 
@@ -150,23 +150,26 @@ def out_f64(t):
 
 def oracle_rows(w: synth.Workload, rows, layer: int, loop: int, lengths, q_len: int, policy: int, W: int,
                 synth_rows=None):
-    """Oracle outputs of sampled rows: rows is a list of (b, i, h) with query position L_b - q_len + i."""
+    """Oracle outputs of sampled rows: rows is a list of (b, i, h) with query position L_b - q_len + i; query head
+    h reads KV head h // (n_heads / n_kv_heads)."""
     import oracle
     R = w.n_loops
+    group = w.n_heads // w.hkv
     outs, lses = [], []
     cache = {}
     for (b, i, h) in rows:
         L = lengths[b]
         sb = synth_rows[b] if synth_rows is not None else b
-        key = (sb, h, L)
+        hk = h // group
+        key = (sb, hk, L)
         if key not in cache:
-            ko = cpu_values(w, synth.T_K, sb, layer, loop, h, L)
-            vo = cpu_values(w, synth.T_V, sb, layer, loop, h, L)
+            ko = cpu_values(w, synth.T_K, sb, layer, loop, hk, L)
+            vo = cpu_values(w, synth.T_V, sb, layer, loop, hk, L)
             if loop == R - 1 or policy == oracle.FULL:
                 kd, vd = ko, vo
             else:
-                kd = cpu_values(w, synth.T_K, sb, layer, R - 1, h, L)
-                vd = cpu_values(w, synth.T_V, sb, layer, R - 1, h, L)
+                kd = cpu_values(w, synth.T_K, sb, layer, R - 1, hk, L)
+                vd = cpu_values(w, synth.T_V, sb, layer, R - 1, hk, L)
             cache = {key: (ko, vo, kd, vd)}
         ko, vo, kd, vd = cache[key]
         t0 = L - q_len
@@ -194,7 +197,7 @@ def algorithmic_bytes_per_call(w: synth.Workload, lengths, q_len: int = 1) -> in
     """Distinct K/V bytes one (layer, loop) call must read: every visible position once per
     (sequence, KV head), in the cache dtype, plus Q and O."""
     es = 4 if w.dtype == synth.DT_F32 else 2
-    kv = sum(2 * L * w.n_heads * w.head_dim * es for L in lengths)
+    kv = sum(2 * L * w.hkv * w.head_dim * es for L in lengths)
     qo = 2 * len(lengths) * q_len * w.n_heads * w.head_dim * es
     return kv + qo
 

@@ -284,6 +284,11 @@ class Workload:
     tail: int = 0
     seed: int = 0
     extra: dict = field(default_factory=dict)
+    n_kv_heads: int = 0      # 0: multi-head (= n_heads); else grouped-query attention
+
+    @property
+    def hkv(self) -> int:
+        return self.n_kv_heads or self.n_heads
 
 
 WORKLOADS = {
@@ -299,6 +304,10 @@ WORKLOADS = {
     "ouro_splitk": Workload("ouro_splitk", 32, 24, 4, 16, 128, 8192, DT_BF16, "full", 0, 1, 16,
                             MODE_PLAIN, 1.0, split_k=8, shuffle=True),
     # LoopKV-style cells on the Ouro shape at L=16384, batch 16; sink 4, tail 128.
+    # Raven-shaped RIPE decode with grouped-query attention: 6 core layers x 32 planes, 8 KV heads x 64 shared
+    # by groups of 4 query heads (32 query heads), L=1024, W=64, batch 64.
+    "raven_ripe": Workload("raven_ripe", 64, 6, 32, 32, 64, 1024, DT_BF16, "ripe", 64, 1, 16, MODE_RIPEN, 1.0,
+                           split_k=0, n_kv_heads=8),
     # split_k 0: the library chooses the number of far splits.
     "loopkv_cells": Workload("loopkv_cells", 16, 24, 4, 16, 128, 16384, DT_BF16, "full", 0, 1, 16,
                              MODE_PLAIN, 1.0, split_k=0, quant=True, sink=4, tail=128),

@@ -708,9 +708,10 @@ lkv_status upload(lkv_cache* c, Table& T, const std::vector<int32_t>& seq_slots,
   return LKV_OK;
 }
 
-int auto_splits(const lkv_cache* c, int n_seqs, int q_len, int max_pages) {
-  const int rows = n_seqs * c->cfg.n_heads_q;
-  (void)q_len;
+// Splits of a plain-cache call: enough workgroups to fill the chip.  Decode and draft
+// workgroups serve all query heads of one KV head; verify workgroups one query head.
+int auto_splits(const lkv_cache* c, int n_seqs, int mode, int max_pages) {
+  const int rows = n_seqs * (mode == LKV_MODE_VERIFY ? c->cfg.n_heads_q : c->cfg.n_heads_kv);
   const int target = env_int("LKV_TARGET_WGS", 2048);
   int s = (target + rows - 1) / rows;
   s = std::min(s, std::max(1, max_pages / 8));
@@ -740,7 +741,7 @@ lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, siz
     max_cp = std::max(max_cp, (std::max(0, L - c->cfg.sink - c->cfg.tail) + kCodePage - 1) / kCodePage);
   }
   const int S = c->cfg.quant ? cell_splits(c, a->n_seqs, a->split_k, max_cp)
-                             : (a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->q_len, max_pages));
+                             : (a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, max_pages));
   const int parts = c->cfg.quant ? S + 1 : S;
   if (parts <= 1) {
     *bytes = 0;
@@ -784,7 +785,7 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
   if (st != LKV_OK) return st;
   int max_pages = 0;
   for (const auto& r : rows) max_pages = std::max(max_pages, (r.n_cached + kPage - 1) / kPage);
-  const int S = a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->q_len, max_pages);
+  const int S = a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, max_pages);
   const int D = cfg.head_dim, hq = cfg.n_heads_q, es = elem_bytes(cfg);
   const size_t ws_need = S > 1 ? (size_t)a->n_seqs * a->q_len * hq * S * (D + 1) * 4 : 0;
   if (ws_need > 0 && (!a->workspace || a->workspace_bytes < ws_need))

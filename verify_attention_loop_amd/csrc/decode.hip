@@ -6,7 +6,8 @@
 // block, else the deepest plane.  A draft step (RIPE page, Alg. 1) reads cached
 // positions through the same rule and its block positions from caller scratch.
 //
-// Mapping (one workgroup = one (sequence, query head, split) row, WAVES waves):
+// Mapping (one workgroup = one (sequence, KV head, split) with its G query heads,
+// G = 1 for multi-head attention, 2, 4 or 8 under grouped-query attention; WAVES waves):
 //   * a wave takes whole 16-token pages; DPP row g (16 lanes) handles the tokens
 //     4i + g of the page, which V quad g holds (page layout in params.hpp);
 //   * K: load i of row g reads token 4i + g, lane li its channels
@@ -28,14 +29,17 @@
 
 namespace lkv {
 
-template <typename T, int D, int WAVES, bool TRACE>
-__global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p) {
+// Seven waves per SIMD fit the multi-head bf16 d = 96 kernel in 72 VGPRs; the hint keeps
+// the register allocator there.
+template <typename T, int D, int WAVES, bool TRACE, int G>
+__global__ __launch_bounds__(WAVES * 64, (G == 1 && D == 96 && sizeof(T) == 2) ? 7 : 1) void decode_kernel(const PlainParams p) {
   using Tl = DecodeTile<T, D>;
   constexpr int E = Tl::E, KB = Tl::KB, VB = Tl::VB, ES = Tl::ES, HEAD = Tl::HEAD;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // blockIdx.y is the KV head; the workgroup serves its G query heads hk G .. hk G + G - 1
+  // (grouped-query attention), so each K/V page is streamed once for all of them.
+  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, li = lane & 15;
-  const int hk = h / (p.hq / p.hkv);
   const int slot = p.slot[b];
   const int n_cached = p.len[b];
   const int L = n_cached + p.draft_len;
@@ -43,18 +47,19 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
   const int t0 = p.draft_len > 0 ? n_cached : t;
   const int own_lo = p.ripe ? max(0, min(t0, t - p.window)) : 0;
 
-  // Query: this lane's channels.
-  float qf[E];
-  uint32_t qw[(E + 1) / 2];
-  {
-    const int64_t qbase = ((int64_t)b * p.hq + h) * D + li * E;
+  // Queries: this lane's channels of each of the G heads.
+  float qf[G][E];
+  uint32_t qw[G][(E + 1) / 2];
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq) {
+    const int64_t qbase = ((int64_t)b * p.hq + hk * G + gq) * D + li * E;
     if constexpr (sizeof(T) == 4) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) qf[e] = reinterpret_cast<const float*>(p.q)[qbase + e];
+      for (int e = 0; e < E; ++e) qf[gq][e] = reinterpret_cast<const float*>(p.q)[qbase + e];
     } else {
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + qbase;
 #pragma unroll
-      for (int e2 = 0; e2 < E / 2; ++e2) qw[e2] = (uint32_t)qp[2 * e2] | ((uint32_t)qp[2 * e2 + 1] << 16);
+      for (int e2 = 0; e2 < E / 2; ++e2) qw[gq][e2] = (uint32_t)qp[2 * e2] | ((uint32_t)qp[2 * e2 + 1] << 16);
     }
   }
 
@@ -62,10 +67,14 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
   const int p0 = (int)((int64_t)split * n_pages / p.n_splits);
   const int p1 = (int)((int64_t)(split + 1) * n_pages / p.n_splits);
 
-  Softmax st{-INFINITY, 0.f};
-  float o[E];
+  Softmax st[G];
+  float o[G][E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  for (int gq = 0; gq < G; ++gq) {
+    st[gq] = Softmax{-INFINITY, 0.f};
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[gq][e] = 0.f;
+  }
 
   const int32_t* tab_own = p.tab_own + (int64_t)slot * p.ring_own;
   const int32_t* tab_deep = p.tab_deep + (int64_t)slot * p.ring_deep;
@@ -108,18 +117,21 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
       blend_quad<T, D>(vr, vd, take_deep, zero);
     }
 
-    float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = pos + 4 * i + g;
-      const float s = row_sum16(partial_dot<T, D>(kr[i], qf, qw)) * p.scale_log2;
-      x[i] = (j < n_cached) ? s : -INFINITY;
+    for (int gq = 0; gq < G; ++gq) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = pos + 4 * i + g;
+        const float s = row_sum16(partial_dot<T, D>(kr[i], qf[gq], qw[gq])) * p.scale_log2;
+        x[i] = (j < n_cached) ? s : -INFINITY;
+      }
+      softmax_step<E, 4>(st[gq], o[gq], x);
+      accum_quad<T, D>(o[gq], vr, x);
     }
-    softmax_step<E, 4>(st, o, x);
-    accum_quad<T, D>(o, vr, x);
 
     if constexpr (TRACE) {
-      if (h == 0 && li == 0) {
+      if (hk == 0 && li == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = pos + 4 * i + g;
@@ -143,21 +155,24 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
       // this lane's V channels (vchan) of the draft token
       const uint32_t* vrow = reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(p.draft_v) +
                                                                ((((int64_t)b * p.draft_len + i) * p.hkv + hk) * D) * ES);
-      float x[1] = {row_sum16(partial_dot<T, D>(kr, qf, qw)) * p.scale_log2};
-      softmax_step<E, 1>(st, o, x);
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float v;
-        if constexpr (sizeof(T) == 4) {
-          v = __uint_as_float(vrow[vchan<T>(e, li)]);
-        } else {
-          const uint32_t pair = vrow[vchan<T>(e & ~1, li) >> 1];
-          v = (e & 1) ? bf_hi(pair) : bf_lo(pair);
+      for (int gq = 0; gq < G; ++gq) {
+        float x[1] = {row_sum16(partial_dot<T, D>(kr, qf[gq], qw[gq])) * p.scale_log2};
+        softmax_step<E, 1>(st[gq], o[gq], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          float v;
+          if constexpr (sizeof(T) == 4) {
+            v = __uint_as_float(vrow[vchan<T>(e, li)]);
+          } else {
+            const uint32_t pair = vrow[vchan<T>(e & ~1, li) >> 1];
+            v = (e & 1) ? bf_hi(pair) : bf_lo(pair);
+          }
+          o[gq][e] = fmaf(x[0], v, o[gq][e]);
         }
-        o[e] = fmaf(x[0], v, o[e]);
       }
       if constexpr (TRACE) {
-        if (h == 0 && li == 0 && n_cached + i < p.trace_len) {
+        if (hk == 0 && li == 0 && n_cached + i < p.trace_len) {
           int32_t* tr = p.trace + ((int64_t)b * p.trace_len + n_cached + i) * 2;
           tr[0] = p.loop;
           tr[1] = -2;
@@ -166,39 +181,43 @@ __global__ __launch_bounds__(WAVES * 64) void decode_kernel(const PlainParams p)
     }
   }
 
-  // Merge the 4*WAVES row states of this workgroup.
+  // Merge the 4*WAVES row states of this workgroup, one query head at a time.
   __shared__ float sm_o[WAVES * 4][D];
   __shared__ float sm_m[WAVES * 4], sm_l[WAVES * 4];
   const int r = w * 4 + g;
 #pragma unroll
-  for (int e = 0; e < E; ++e) sm_o[r][vchan<T>(e, li)] = o[e];
-  if (li == 0) {
-    sm_m[r] = st.m;
-    sm_l[r] = st.l;
-  }
-  __syncthreads();
-  float M = -INFINITY;
+  for (int gq = 0; gq < G; ++gq) {
+    if (gq > 0) __syncthreads();  // the previous head's reads are done
 #pragma unroll
-  for (int k = 0; k < WAVES * 4; ++k) M = fmaxf(M, sm_m[k]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float Lsum = 0.f;
+    for (int e = 0; e < E; ++e) sm_o[r][vchan<T>(e, li)] = o[gq][e];
+    if (li == 0) {
+      sm_m[r] = st[gq].m;
+      sm_l[r] = st[gq].l;
+    }
+    __syncthreads();
+    float M = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < WAVES * 4; ++k) Lsum += sm_l[k] * fast_exp2(sm_m[k] - Mu);
-  const int64_t row = (int64_t)b * p.hq + h;
-  for (int c = threadIdx.x; c < D; c += WAVES * 64) {
-    float acc = 0.f;
+    for (int k = 0; k < WAVES * 4; ++k) M = fmaxf(M, sm_m[k]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float Lsum = 0.f;
 #pragma unroll
-    for (int k = 0; k < WAVES * 4; ++k) acc += sm_o[k][c] * fast_exp2(sm_m[k] - Mu);
-    const float val = Lsum > 0.f ? acc / Lsum : 0.f;
-    if (p.n_splits == 1) store_out<T>(p.out, row * D + c, val);
-    else p.ws[(row * p.n_splits + split) * (D + 1) + c] = val;
-  }
-  if (threadIdx.x == 0) {
-    const float lse2 = Lsum > 0.f ? M + fast_log2(Lsum) : -INFINITY;
-    if (p.n_splits == 1) {
-      if (p.lse) p.lse[row] = lse2 * 0.69314718055994531f;
-    } else {
-      p.ws[(row * p.n_splits + split) * (D + 1) + D] = lse2;
+    for (int k = 0; k < WAVES * 4; ++k) Lsum += sm_l[k] * fast_exp2(sm_m[k] - Mu);
+    const int64_t row = (int64_t)b * p.hq + hk * G + gq;
+    for (int c = threadIdx.x; c < D; c += WAVES * 64) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < WAVES * 4; ++k) acc += sm_o[k][c] * fast_exp2(sm_m[k] - Mu);
+      const float val = Lsum > 0.f ? acc / Lsum : 0.f;
+      if (p.n_splits == 1) store_out<T>(p.out, row * D + c, val);
+      else p.ws[(row * p.n_splits + split) * (D + 1) + c] = val;
+    }
+    if (threadIdx.x == 0) {
+      const float lse2 = Lsum > 0.f ? M + fast_log2(Lsum) : -INFINITY;
+      if (p.n_splits == 1) {
+        if (p.lse) p.lse[row] = lse2 * 0.69314718055994531f;
+      } else {
+        p.ws[(row * p.n_splits + split) * (D + 1) + D] = lse2;
+      }
     }
   }
 }
@@ -251,18 +270,32 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 
 // ----------------------------------------------------------------------------- launchers
 
+template <typename T, int D, int G>
+static void launch_decode_g(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+  dim3 grid(p.n_splits, p.hkv, p.n_rows);
+  if (waves == 2) {
+    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 2, true, G>), grid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((decode_kernel<T, D, 2, false, G>), grid, dim3(128), 0, s, p);
+  } else if (waves == 8) {
+    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 8, true, G>), grid, dim3(512), 0, s, p);
+    else hipLaunchKernelGGL((decode_kernel<T, D, 8, false, G>), grid, dim3(512), 0, s, p);
+  } else {
+    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 4, true, G>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((decode_kernel<T, D, 4, false, G>), grid, dim3(256), 0, s, p);
+  }
+}
+
+// Group sizes 1 (multi-head), 2, 4 and 8 (grouped-query attention).
 template <typename T, int D>
 static hipError_t launch_decode_t(const PlainParams& p, int waves, bool trace, hipStream_t s) {
-  dim3 grid(p.n_splits, p.hq, p.n_rows);
-  if (waves == 2) {
-    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 2, true>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<T, D, 2, false>), grid, dim3(128), 0, s, p);
-  } else if (waves == 8) {
-    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 8, true>), grid, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<T, D, 8, false>), grid, dim3(512), 0, s, p);
-  } else {
-    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 4, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<T, D, 4, false>), grid, dim3(256), 0, s, p);
+  const int G = p.hq / p.hkv;
+  if (G * p.hkv != p.hq) return hipErrorInvalidValue;
+  switch (G) {
+    case 1: launch_decode_g<T, D, 1>(p, waves, trace, s); break;
+    case 2: launch_decode_g<T, D, 2>(p, waves, trace, s); break;
+    case 4: launch_decode_g<T, D, 4>(p, waves, trace, s); break;
+    case 8: launch_decode_g<T, D, 8>(p, waves, trace, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -346,3 +346,158 @@ def cell_bytes_per_call(bc: BuiltCells, layer: int, loop: int, n_cold: int = 0) 
     qo = 2 * len(bc.lengths) * H * D * 2
     lo_skipped = 32 * n_cold if cell_bits(bc.plan, layer, loop) == 4 else 0
     return far + near + qo - lo_skipped
+
+
+# ----------------------------------------------------------------------------- multi-step self-speculative loop
+
+class SpecLoop:
+    """A synthetic run of the RIPE page's self-speculative step (Sec. 4, Algorithm 1) through the C-ABI.
+
+    The cache holds positions [0, len) of each sequence; the next block starts with the last emitted token x at
+    position len.  One step: gamma draft passes (q = 1 at loops 0..d-1, cached positions read plane R, the block
+    from caller scratch), one verify pass over the block of gamma + 1 tokens at every loop (the block's plane r is
+    appended before loop r attends), then a seeded acceptance of a in [0, gamma] drafts: the planes of x and the
+    accepted drafts stay (commit to len + 1 + a, which also drops non-deepest planes that left the window) and
+    the rest is truncated.  Keys and values of position j are generated with a per-position version that grows
+    every time the position is written again, so a truncated and rewritten position holds new values.  There are
+    no logits: acceptance is drawn, and the attention outputs are what the caller checks."""
+
+    def __init__(self, w: synth.Workload, prefix_lengths, gamma: int, d: int, window: int, seed: int = 0):
+        import torch
+        self.w, self.gamma, self.d, self.W = w, gamma, d, window
+        self.k = gamma + 1
+        self.rng = np.random.default_rng(seed)
+        R, H, D = w.n_loops, w.hkv, w.head_dim
+        max_len = max(prefix_lengths) + 64 * self.k
+        self.max_len = max_len
+        cfg = vla.LoopCache.config(n_layers=w.n_layers, n_loops=R, n_heads_q=w.n_heads, n_heads_kv=H, head_dim=D,
+                                   kv_dtype=w.dtype, policy=vla.POLICY_RIPE, window=window,
+                                   max_seqs=len(prefix_lengths), max_len=max_len, max_block=self.k, poison=1,
+                                   shuffle_seed=0x5EED + seed)
+        n_pages = len(prefix_lengths) * w.n_layers * ((max_len + 15) // 16 + (R - 1) * ((window + self.k) // 16 + 2))
+        self.cache = vla.LoopCache.on_device(cfg, n_pages)
+        self.version = [np.zeros(max_len, dtype=np.int64) for _ in prefix_lengths]
+        self.seqs = [self.cache.lkv_add_seq() for _ in prefix_lengths]
+        self.lengths = list(prefix_lengths)
+        for b, L in enumerate(prefix_lengths):
+            for layer in range(w.n_layers):
+                self._append(b, layer, R - 1, 0, L)
+            self.cache.lkv_commit(self.seqs[b], L)  # the window is measured from the committed length
+            for layer in range(w.n_layers):
+                for plane in range(R - 1):
+                    a = max(0, L - window)
+                    self._append(b, layer, plane, a, L - a)
+        torch.cuda.synchronize()
+
+    # generator coordinates of (seq b, position j): one row per (b, version)
+    def _row(self, b, j):
+        return b * 4096 + int(self.version[b][j])
+
+    def _append(self, b, layer, plane, pos0, n):
+        import torch
+        w = self.w
+        dt = torch_dtype(w.dtype)
+        k = torch.empty((n, w.hkv, w.head_dim), dtype=dt, device="cuda")
+        v = torch.empty_like(k)
+        st = torch.cuda.current_stream().cuda_stream
+        for j in range(pos0, pos0 + n):
+            r = self._row(b, j)
+            synth.gpu_kv(k[j - pos0].data_ptr(), w.dtype, w.seed, synth.T_K, r, layer, plane, w.hkv, w.head_dim, j, 1,
+                         w.mode, w.n_loops, w.scale, st)
+            synth.gpu_kv(v[j - pos0].data_ptr(), w.dtype, w.seed, synth.T_V, r, layer, plane, w.hkv, w.head_dim, j, 1,
+                         w.mode, w.n_loops, w.scale, st)
+        self.cache.lkv_append_plane(self.seqs[b], layer, plane, pos0, k, v)
+
+    def host_kv(self, tensor, b, layer, plane, hk, L):
+        """fp64 [L][d] keys or values of positions 0..L-1 as currently written (their versions)."""
+        w = self.w
+        out = np.empty((L, w.head_dim))
+        for j in range(L):
+            x = synth.kv(w.dtype, w.seed, tensor, self._row(b, j), layer, plane, w.hkv, w.head_dim, j, 1, w.mode,
+                         w.n_loops, w.scale, heads=[hk])[0, 0]
+            out[j] = to_f64(x, w.dtype)
+        return out
+
+    def query(self, b, layer, loop, h, pos, salt=0):
+        return cpu_query(self.w, self._row(b, pos) + 100000 * salt, layer, loop, h, pos)
+
+    def gpu_query(self, layer, loop, t0s, q_len, salt=0):
+        import torch
+        w = self.w
+        out = torch.empty((len(self.seqs), q_len, w.n_heads, w.head_dim), dtype=torch_dtype(w.dtype), device="cuda")
+        st = torch.cuda.current_stream().cuda_stream
+        for b, t0 in enumerate(t0s):
+            for i in range(q_len):
+                synth.gpu_q(out[b, i].data_ptr(), w.dtype, w.seed, [self._row(b, t0 + i) + 100000 * salt], [t0 + i],
+                            layer, loop, 1, w.n_heads, w.head_dim, w.scale, st)
+        return out
+
+    def draft_pass(self, i):
+        """Draft token i (1..gamma) at every draft loop; returns {(layer, loop): (out, draft scratch k, v)}."""
+        import torch
+        w = self.w
+        dt = torch_dtype(w.dtype)
+        res = {}
+        st = torch.cuda.current_stream().cuda_stream
+        for layer in range(w.n_layers):
+            for loop in range(self.d):
+                dk = torch.empty((len(self.seqs), i, w.hkv, w.head_dim), dtype=dt, device="cuda")
+                dv = torch.empty_like(dk)
+                for b, L in enumerate(self.lengths):
+                    synth.gpu_kv(dk[b].data_ptr(), w.dtype, w.seed, synth.T_DRAFTK, self._row(b, L), layer, loop,
+                                 w.hkv, w.head_dim, L, i, synth.MODE_PLAIN, w.n_loops, w.scale, st)
+                    synth.gpu_kv(dv[b].data_ptr(), w.dtype, w.seed, synth.T_DRAFTV, self._row(b, L), layer, loop,
+                                 w.hkv, w.head_dim, L, i, synth.MODE_PLAIN, w.n_loops, w.scale, st)
+                q = self.gpu_query(layer, loop, [L + i - 1 for L in self.lengths], 1, salt=1)
+                out = torch.empty_like(q)
+                ws = torch.empty(max(4, self.cache.lkv_workspace_bytes(layer, loop, self.seqs, mode=vla.MODE_DRAFT,
+                                                                       split_k=2)), dtype=torch.uint8, device="cuda")
+                self.cache.lkv_attend(layer, loop, self.seqs, q, out, mode=vla.MODE_DRAFT, window=0, split_k=2,
+                                      workspace=ws, draft_k=dk, draft_v=dv, draft_len=i)
+                res[(layer, loop)] = (out, dk, dv)
+        return res
+
+    def verify_pass(self):
+        """Append the block's planes and verify at every (layer, loop); returns {(layer, loop): out}."""
+        import torch
+        w, k = self.w, self.k
+        outs = {}
+        for loop in range(w.n_loops):
+            for layer in range(w.n_layers):
+                for b, L in enumerate(self.lengths):
+                    self._append(b, layer, loop, L, k)
+                q = self.gpu_query(layer, loop, self.lengths, k)
+                out = torch.empty_like(q)
+                ws = torch.empty(max(4, self.cache.lkv_workspace_bytes(layer, loop, self.seqs, q_len=k,
+                                                                       mode=vla.MODE_VERIFY, split_k=2)),
+                                 dtype=torch.uint8, device="cuda")
+                self.cache.lkv_attend(layer, loop, self.seqs, q, out, q_len=k, mode=vla.MODE_VERIFY, split_k=2,
+                                      workspace=ws)
+                outs[(layer, loop)] = out
+        self.lengths = [L + k for L in self.lengths]
+        return outs
+
+    def accept(self):
+        """Seeded acceptance: keep x and a in [0, gamma] drafts of each sequence, drop the rest."""
+        accepted = []
+        for b, L in enumerate(self.lengths):
+            a = int(self.rng.integers(0, self.gamma + 1))
+            new_len = L - self.k + 1 + a
+            self.cache.lkv_commit(self.seqs[b], new_len)
+            self.cache.lkv_truncate(self.seqs[b], new_len)
+            self.version[b][new_len:] += 1  # positions past the accepted prefix get new values when rewritten
+            self.lengths[b] = new_len
+            accepted.append(a)
+        return accepted
+
+    def expected_pages(self):
+        """Physical pages a RIPE cache must hold now: plane R of every position, and the non-deepest planes of
+        positions >= len - W (the window ring), per sequence and layer."""
+        w, W = self.w, self.W
+        n = 0
+        for L in self.lengths:
+            deep = (L + 15) // 16
+            lo = max(0, L - W)
+            ring = ((L - 1) // 16 - lo // 16 + 1) if L > lo else 0
+            n += w.n_layers * (deep + (w.n_loops - 1) * ring)
+        return n

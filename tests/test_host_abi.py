@@ -250,3 +250,51 @@ def test_quant_workspace_matches_the_cell_split_rule(lib):
     S = min(64, -(-2048 // rows), n_cp)
     assert c.lkv_workspace_bytes(0, 0, seqs) == rows * (S + 1) * 129 * 4
     assert c.lkv_workspace_bytes(0, 0, seqs[2:], split_k=5) == 4 * (1 + 1) * 129 * 4  # 1 code page caps the splits
+
+
+@pytest.mark.parametrize("gamma,W", [(4, 8), (7, 7), (2, 40)])
+def test_speculative_steps_keep_exactly_the_ripe_pages(lib, gamma, W):
+    """Host bookkeeping of many self-speculative steps (RIPE page, Sec. 4 and Algorithm 1): reserve the block's
+    planes at every loop, accept a seeded prefix, commit and truncate.  After every step the pages in use are the
+    deepest plane of every position plus the window ring of every other plane, the logical bytes follow Eq. (10),
+    and every cached position that the next token (at position len) reads resolves to a resident page of the
+    plane the policy names."""
+    R, n_layers, L0 = 4, 2, [5, 33, 70]
+    c = make(n_pages=4096, n_layers=n_layers, n_loops=R, window=W, max_block=gamma + 1, max_len=2048, max_seqs=3)
+    seqs = [c.lkv_add_seq() for _ in L0]
+    lens = list(L0)
+    for s, L in zip(seqs, lens):
+        for layer in range(n_layers):
+            c.lkv_reserve(s, layer, R - 1, 0, L)
+        c.lkv_commit(s, L)  # the window is measured from the committed length
+        for layer in range(n_layers):
+            for plane in range(R - 1):
+                lo = max(0, L - W)
+                c.lkv_reserve(s, layer, plane, lo, L - lo)
+    rng = np.random.default_rng(gamma * 100 + W)
+    k = gamma + 1
+    b_tok = 2 * 2 * 64 * 2
+    for step in range(60):
+        for b, s in enumerate(seqs):
+            for loop in range(R):
+                for layer in range(n_layers):
+                    c.lkv_reserve(s, layer, loop, lens[b], k)
+            a = int(rng.integers(0, gamma + 1))
+            new_len = lens[b] + 1 + a
+            c.lkv_commit(s, new_len)
+            c.lkv_truncate(s, new_len)
+            lens[b] = new_len
+            assert c.lkv_seq_info(s) == (new_len, new_len)
+        want = 0
+        for L in lens:
+            lo = max(0, L - W)
+            want += n_layers * ((L + 15) // 16 + (R - 1) * ((L - 1) // 16 - lo // 16 + 1))
+        assert c.lkv_mem_stats()["pages_in_use"] == want
+        assert c.lkv_mem_stats()["logical_bytes"] == sum(b_tok * n_layers * (L + (R - 1) * min(W, L)) for L in lens)
+        for s, L in zip(seqs, lens):
+            t = L  # the next token x sits at position L; it reads cached positions 0..L-1
+            for loop in (0, R - 2, R - 1):
+                for j in range(L):
+                    plane, phys, slot = c.lkv_debug_resolve(s, 1, loop, t, t, j)
+                    assert plane == oracle.oracle_plane(oracle.RIPE, loop, R, t, t, j, W)
+                    assert phys >= 0 and slot == j % 16

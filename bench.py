@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="distinct layers held in HBM (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--v-rule", choices=["fixed", "running"], default="fixed",
+                    help="quantised cells: the workload's fixed hot rule (s >= m0 - 4) or the running-maximum rule")
+    ap.add_argument("--v-tau", type=float, default=14.0, help="tau of the running-maximum rule")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -199,7 +202,11 @@ def main():
         outs[(layer, loop)] = torch.empty_like(qs[(layer, loop)])
     ws_bytes = cache.lkv_workspace_bytes(0, 0, built.seqs, q_len=q_len, mode=mode, split_k=split)
     ws = torch.empty(max(4, ws_bytes), dtype=torch.uint8, device="cuda")
-    extra = {"v_thresh_offset": 4.0} if w.quant else {}
+    extra = {}
+    if w.quant:
+        extra = {"v_thresh_offset": 4.0}
+        if args.v_rule == "running":
+            extra = {"v_rule": vla.VRULE_RUNNING, "v_tau": args.v_tau}
 
     # Algorithmic bytes of each call.  Quantised cells skip the V lo plane of cold tokens, so one untimed
     # pass with the hot-mask trace counts them first.
@@ -289,7 +296,8 @@ def main():
            "layers_resident": len(layers), "kernel_ms_per_step": round(float(kern_ms.sum(axis=1).mean()), 4),
            "setup_s": round(setup_s, 1)}
     if w.quant:
-        cfg.update(sink=w.sink, tail=w.tail, v_thresh="m0 - 4.0",
+        cfg.update(sink=w.sink, tail=w.tail,
+                   v_thresh="m0 - 4.0" if args.v_rule == "fixed" else f"max(m, m0) - {args.v_tau} ln 2 (running)",
                    plan={k: int((built.plan == v).sum()) for k, v in (("int4", synth.CELL_INT4),
                                                                       ("int2", synth.CELL_INT2),
                                                                       ("shared", synth.CELL_SHARED))})

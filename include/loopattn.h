@@ -56,6 +56,15 @@ enum { LKV_POLICY_FULL = 0, LKV_POLICY_RIPE = 1 };
 enum { LKV_MODE_DECODE = 0, LKV_MODE_VERIFY = 1, LKV_MODE_DRAFT = 2 };
 /* Cell kinds of a quantised cache (LoopKV page, Sec. 3.1-3.2).  BF16 is reserved. */
 enum { LKV_CELL_BF16 = 0, LKV_CELL_INT4 = 1, LKV_CELL_INT2 = 2, LKV_CELL_SHARED = 3 };
+/* Hot test of a far token in an INT4 or shared cell (which decides whether its V lo
+   plane is read; LoopKV page, Sec. 3.3).  FIXED: s_j >= m0 - v_thresh_offset, with m0
+   the largest sink score.  RUNNING (the page's own rule, App. E Algorithm 1): the far
+   history's 32-token pages are shared out to the call's far splits, split c taking
+   pages [floor(c n / S), floor((c + 1) n / S)); a split walks its pages in order and
+   token j of page p is hot iff s_j >= max(m, m0) - v_tau ln 2, where m is the largest
+   score of the split's pages up to and including p.  Scores are logits in natural
+   units (q.k / sqrt(d)); ties are hot. */
+enum { LKV_VRULE_FIXED = 0, LKV_VRULE_RUNNING = 1 };
 
 /* Tokens per plain page and per code page. */
 #define LKV_PAGE_TOKENS 16
@@ -128,6 +137,9 @@ typedef struct {
      (not the merge), for timing. */
   void* ev_begin;
   void* ev_end;
+  /* Quantised cells: hot-test rule (LKV_VRULE_*) and, for RUNNING, tau (the page uses 14). */
+  int32_t v_rule;
+  float v_tau;
 } lkv_attend_args;
 
 typedef struct {

@@ -13,6 +13,7 @@ and adds the closed-form memory and byte models the pages print:
 * ``split_partials``/``lse_merge`` -- LoopKV page, Sec. 3.4 and App. E Alg. 1;
 * ``cell_row``          -- LoopKV page, Sec. 3.1-3.4 (INT4 / INT2 / shared cells,
                            bit-plane V, fixed hot rule s >= m0 - offset);
+* ``cell_row_running``  -- LoopKV page, Sec. 3.3 and App. E Algorithm 1 (the running-maximum V-precision rule);
 * ``kivi_encode``       -- LoopKV page, Sec. 3.1 and 3.3 (the window-exit codec);
 * ``mem_full``/``mem_deep``/``mem_ripe`` -- RIPE page, Eq. (3) and Eq. (10);
 * ``loopkv_bytes_per_token_layer`` -- LoopKV page, App. C byte model.
@@ -26,6 +27,7 @@ fp64 scaled-dot-product attention on a materialised view) and brute force.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -77,6 +79,9 @@ def _lib():
         L.oracle_cell_row.argtypes = [i32, i32, i32, i32, i32, pd, pd, pd, pu8, pd, pd, pu8, pd, pd, dbl, pd, pd,
                                       pu8]
         L.oracle_cell_row.restype = i32
+        L.oracle_cell_row_rule.argtypes = [i32, i32, i32, i32, i32, pd, pd, pd, pu8, pd, pd, pu8, pd, pd, i32, dbl,
+                                           i32, pd, pd, pu8, pd]
+        L.oracle_cell_row_rule.restype = i32
         L.oracle_kivi_encode.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                           pu8, ctypes.POINTER(ctypes.c_uint16), pu8, ctypes.POINTER(ctypes.c_uint16)]
         L.oracle_kivi_encode.restype = None
@@ -232,6 +237,31 @@ def f16_from_f32(x: float) -> int:
 
 def f32_from_f16(h: int) -> float:
     return float(_lib().oracle_f32_from_f16(int(h)))
+
+
+def cell_row_running(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink: int, tail: int, kind: int, tau: float,
+                     n_splits: int):
+    """One cell row under the LoopKV page's own V-precision rule (Sec. 3.3, App. E Algorithm 1): far block c of
+    n_splits walks its 32-token pages in order with a running maximum m of its scores so far; a token is hot
+    iff s >= max(m, m0) - tau ln 2.  Returns (out[d], lse, hot_bits[n_far], n_cold, thresholds[n_far])."""
+    q, qp = _d(q)
+    kn, knp = _d(k_near)
+    vn, vnp = _d(v_near)
+    L, d = kn.shape
+    n_far = L - sink - tail
+    kca, kcp = _u8(kc)
+    vca, vcp = _u8(vc)
+    ksa, ksp = _d(ks)
+    kza, kzp = _d(kz)
+    vsa, vsp = _d(vs)
+    vza, vzp = _d(vz)
+    out, outp = _d(np.zeros(d))
+    lse, lsep = _d(np.zeros(1))
+    hot, hotp = _u8(np.zeros(n_far, dtype=np.uint8))
+    thr, thrp = _d(np.zeros(n_far))
+    n_cold = _lib().oracle_cell_row_rule(d, L, sink, tail, kind, qp, knp, vnp, kcp, ksp, kzp, vcp, vsp, vzp, 1,
+                                         float(tau) * math.log(2.0), int(n_splits), outp, lsep, hotp, thrp)
+    return out, float(lse[0]), hot, int(n_cold), thr
 
 
 # ----------------------------------------------------------------------------- closed-form models

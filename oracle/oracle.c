@@ -193,17 +193,26 @@ void oracle_lse_merge(int n_parts, int d, const double* o_parts, const double* m
  *     INT4 / SHARED (bit planes hi = c >> 2, lo = c & 3): a hot token reads
  *       both planes (4*hi + lo = c), a cold token only hi and decodes to the
  *       bucket midpoint 4*hi + 1.5.
- * Hot test (fixed rule): m0 = max score over the sink keys; far token j is hot
- * iff s_j >= m0 - thr_offset (s in natural logit units, ties hot).  INT2 cells
- * have no lo plane and no test (hot_bits are written as 1).
+ * Seed: m0 = max score over the sink keys ([LoopKV] Sec. 3.3, footnote 9).
+ * Hot test of far token j (s in natural logit units, ties hot); INT2 cells
+ * have no lo plane and no test (hot_bits are written as 1):
+ *   rule 0 (fixed):   s_j >= m0 - thr;
+ *   rule 1 (running, [LoopKV] Sec. 3.3 and App. E Algorithm 1): the far history's
+ *     32-token pages are shared out to n_splits far blocks, block c taking pages
+ *     [floor(c n / S), floor((c+1) n / S)); each block walks its pages in order,
+ *     and after reading page p's keys its running maximum m is the largest score
+ *     of its pages up to and including p; token j of page p is hot iff
+ *     s_j >= max(m, m0) - thr, where thr = tau ln 2 is passed in.
  * Softmax over S, F and T as in oracle_attend_row.  Writes out[d], *lse,
- * hot_bits[L-tail-sink] (0/1) and returns the number of cold far tokens.
+ * hot_bits[L-tail-sink] (0/1), thr_used[L-tail-sink] (the threshold each far
+ * token was tested against, or NaN for INT2; may be NULL) and returns the number
+ * of cold far tokens.
  */
-int oracle_cell_row(int d, int L, int sink, int tail, int kind, const double* q,
-                    const double* k_near, const double* v_near, const uint8_t* kc,
-                    const double* ks, const double* kz, const uint8_t* vc, const double* vs,
-                    const double* vz, double thr_offset, double* out, double* lse,
-                    uint8_t* hot_bits) {
+int oracle_cell_row_rule(int d, int L, int sink, int tail, int kind, const double* q,
+                         const double* k_near, const double* v_near, const uint8_t* kc,
+                         const double* ks, const double* kz, const uint8_t* vc, const double* vs,
+                         const double* vz, int rule, double thr_offset, int n_splits, double* out,
+                         double* lse, uint8_t* hot_bits, double* thr_used) {
   const double scale = 1.0 / sqrt((double)d);
   const int n_far = L - tail - sink;
   const int n_grp = d / 32;
@@ -222,12 +231,33 @@ int oracle_cell_row(int d, int L, int sink, int tail, int kind, const double* q,
     s[sink + f] = dot(q, kh, d) * scale;
   }
   const int masked = (kind == CELL_INT4 || kind == CELL_SHARED);
-  const double thr = m0 - thr_offset;
   int n_cold = 0;
-  for (int f = 0; f < n_far; ++f) {
-    const int hot = masked ? (s[sink + f] >= thr) : 1;
-    hot_bits[f] = (uint8_t)hot;
-    n_cold += !hot;
+  if (!masked || rule == 0) {
+    const double thr = m0 - thr_offset;
+    for (int f = 0; f < n_far; ++f) {
+      const int hot = masked ? (s[sink + f] >= thr) : 1;
+      hot_bits[f] = (uint8_t)hot;
+      if (thr_used) thr_used[f] = masked ? thr : NAN;
+      n_cold += !hot;
+    }
+  } else {
+    const int n_pages = (n_far + 31) / 32;
+    for (int c = 0; c < n_splits; ++c) {
+      const int p0 = (int)((int64_t)c * n_pages / n_splits), p1 = (int)((int64_t)(c + 1) * n_pages / n_splits);
+      double m = -INFINITY;
+      for (int p = p0; p < p1; ++p) {
+        const int f0 = 32 * p, f1 = 32 * p + 32 < n_far ? 32 * p + 32 : n_far;
+        for (int f = f0; f < f1; ++f)
+          if (s[sink + f] > m) m = s[sink + f];
+        const double thr = (m > m0 ? m : m0) - thr_offset;
+        for (int f = f0; f < f1; ++f) {
+          const int hot = s[sink + f] >= thr;
+          hot_bits[f] = (uint8_t)hot;
+          if (thr_used) thr_used[f] = thr;
+          n_cold += !hot;
+        }
+      }
+    }
   }
   double m = -INFINITY;
   for (int j = 0; j < L; ++j)
@@ -257,6 +287,15 @@ int oracle_cell_row(int d, int L, int sink, int tail, int kind, const double* q,
   free(kh);
   free(s);
   return n_cold;
+}
+
+/* The fixed rule (s_j >= m0 - thr_offset) of oracle_cell_row_rule. */
+int oracle_cell_row(int d, int L, int sink, int tail, int kind, const double* q, const double* k_near,
+                    const double* v_near, const uint8_t* kc, const double* ks, const double* kz,
+                    const uint8_t* vc, const double* vs, const double* vz, double thr_offset, double* out,
+                    double* lse, uint8_t* hot_bits) {
+  return oracle_cell_row_rule(d, L, sink, tail, kind, q, k_near, v_near, kc, ks, kz, vc, vs, vz, 0, thr_offset, 1,
+                              out, lse, hot_bits, NULL);
 }
 
 /*

@@ -1,5 +1,5 @@
 """GPU parity of LoopKV-style quantised cells (INT4 / INT2 / shared; bit-plane V with the
-fixed hot rule s >= m0 - offset) through the C-ABI against the fp64 oracle.
+fixed hot rule s >= m0 - offset and the page's running-maximum rule) through the C-ABI against the fp64 oracle.
 
 Outputs: max-abs 2e-2 (bf16 out).  Hot masks: bit-exact for every far token whose score
 lies outside a 1e-4 band around the threshold (both sides compute the score in a
@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import harness
+import oracle
 import synth
 import verify_attention_loop_amd as vla
 
@@ -116,4 +117,52 @@ def test_loopkv_full_shape_sampled():
             got = _bits(mask[b, h], n_far)
             near = np.abs(s_far - thr) <= BAND
             assert np.array_equal(got[~near], hot[~near])
+    bc.cache.close()
+
+
+@pytest.mark.parametrize("tau", [14.0, 2.0, 0.5])
+@pytest.mark.parametrize("split_k", [1, 3, 7])
+def test_cells_running_rule(tau, split_k):
+    """The LoopKV page's own V-precision rule (Sec. 3.3, App. E Algorithm 1): each far split walks its pages in
+    order with a running maximum m; a token is hot iff s >= max(m, m0) - tau ln 2.  Outputs vs the oracle's rule
+    with the same page partition (max-abs 2e-2) and hot masks bit-exact outside a 1e-4 band around each token's
+    threshold; INT2 cells read their whole codes."""
+    w = _cells_wl()
+    lengths = [133, 300, 1000]
+    bc = harness.build_cells(w, lengths=lengths, layers=(0, 1), plan=PLAN)
+    band_hits, cold = 0, 0
+    for layer in (0, 1):
+        for loop in range(4):
+            n = len(bc.seqs)
+            q = harness.gpu_queries(bc, layer, loop, 1)
+            out = torch.empty_like(q)
+            words = (max(lengths) - w.sink - w.tail + 31) // 32
+            mask = torch.empty((n, w.n_heads, words), dtype=torch.int32, device="cuda")
+            ws = torch.empty(bc.cache.lkv_workspace_bytes(layer, loop, bc.seqs, split_k=split_k) + 4,
+                             dtype=torch.uint8, device="cuda")
+            bc.cache.lkv_attend(layer, loop, bc.seqs, q, out, split_k=split_k, workspace=ws, mask_trace=mask,
+                                v_rule=vla.VRULE_RUNNING, v_tau=tau)
+            torch.cuda.synchronize()
+            o = harness.out_f64(out)
+            m = mask.cpu().numpy().view(np.uint32)
+            # the call's far splits: split_k, at most the longest row's code pages (shorter rows leave splits empty)
+            S = min(split_k, max((L - w.sink - w.tail + 31) // 32 for L in lengths))
+            for b, L in enumerate(lengths):
+                n_far = L - w.sink - w.tail
+                for h in range(w.n_heads):
+                    a = harness.cell_inputs(bc, b, layer, loop, h)
+                    want, _, hot, n_cold, thr = oracle.cell_row_running(
+                        a["q"], a["k_near"], a["v_near"], a["kc"], a["ks"], a["kz"], a["vc"], a["vs"], a["vz"],
+                        a["sink"], a["tail"], a["kind"], tau, S)
+                    assert np.abs(o[b, 0, h] - want).max() <= TOL, (layer, loop, b, h)
+                    g = np.arange(n_far) // 32
+                    s_far = (a["kz"][g] + a["ks"][g] * a["kc"]) @ a["q"] / math.sqrt(w.head_dim)
+                    got = _bits(m[b, h], n_far)
+                    near = np.abs(s_far - thr) <= BAND if a["kind"] != oracle.CELL_INT2 else np.zeros(n_far, bool)
+                    assert np.array_equal(got[~near], hot[~near]), (layer, loop, b, h)
+                    band_hits += int(near.sum())
+                    cold += n_cold
+    assert band_hits < 5
+    if tau <= 2.0:
+        assert cold > 0
     bc.cache.close()

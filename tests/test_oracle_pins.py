@@ -417,3 +417,96 @@ def test_cell_hot_rule_closed_form():
     _, _, hot, n_cold = oracle.cell_row(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail, oracle.CELL_INT4, 4.0)
     np.testing.assert_array_equal(hot, (kc[:, 0] >= 4).astype(np.uint8))
     assert n_cold == int((kc[:, 0] < 4).sum())
+
+
+# ----------------------------------------------------------------------------- the running-maximum V-precision rule
+
+def test_running_rule_worked_case():
+    """LoopKV page, Sec. 3.3 and App. E Algorithm 1: a far block's running maximum m covers its pages so far and a
+    token is hot iff s >= max(m, m0) - tau ln 2.  With q = sqrt(d) e_0 a score is the key's channel 0.  One far
+    token scores 20 (code 10 at scale 2), every other far token 0, the sink maximum m0 is 5, tau = 14
+    (tau ln 2 = 9.70).  With two far blocks the first block's later tokens fall below 20 - 9.70 and are cold, the
+    second block never sees the 20 and keeps all its tokens hot (0 >= 5 - 9.70); with one block every token after
+    the 20 is cold."""
+    d, sink, tail = 32, 4, 4
+    n_far = 128
+    L = sink + n_far + tail
+    q = np.zeros(d)
+    q[0] = math.sqrt(d)
+    k_near = np.zeros((L, d))
+    k_near[:sink, 0] = [5.0, 1.0, 1.0, 1.0]
+    v_near = np.zeros((L, d))
+    kc = np.zeros((n_far, d), dtype=np.uint8)
+    kc[0, 0] = 10
+    ks = np.full((4, d), 2.0)
+    kz = np.zeros((4, d))
+    vc = np.zeros((n_far, d), dtype=np.uint8)
+    vs = np.full((n_far, 1), 0.25)
+    vz = np.zeros((n_far, 1))
+    _, _, hot2, cold2, _ = oracle.cell_row_running(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail,
+                                                   oracle.CELL_INT4, 14.0, 2)
+    want2 = np.zeros(n_far, np.uint8)
+    want2[0] = 1
+    want2[64:] = 1
+    np.testing.assert_array_equal(hot2, want2)
+    assert cold2 == 63
+    _, _, hot1, cold1, _ = oracle.cell_row_running(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail,
+                                                   oracle.CELL_INT4, 14.0, 1)
+    want1 = np.zeros(n_far, np.uint8)
+    want1[0] = 1
+    np.testing.assert_array_equal(hot1, want1)
+    assert cold1 == n_far - 1
+
+
+@pytest.mark.parametrize("n_splits", [1, 3, 8])
+def test_running_rule_bounds(n_splits):
+    """The running maximum never exceeds the row maximum (LoopKV page, footnote 9 and Prop. 1): cold tokens lie
+    below s_max - tau ln 2, tokens at or above it are hot, and the output is within
+    1.5 * sum_{cold} a_j sigma_j <= 1.5 sigma_max |C| 2^-tau a_max of the reader of both planes."""
+    rng = np.random.default_rng(20 + n_splits)
+    L, d, sink, tail = 900, 64, 4, 16
+    k_near, v_near, kc, ks, kz, vc, vs, vz = _cell_inputs(rng, L, d, sink, tail, 4)
+    q = rng.standard_normal(d) * 3.0
+    for tau in (2.0, 5.0, 14.0):
+        out, lse, hot, n_cold, thr = oracle.cell_row_running(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail,
+                                                             oracle.CELL_INT4, tau, n_splits)
+        ref, lref, _, _ = oracle.cell_row(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail, oracle.CELL_INT4,
+                                          thr_offset=math.inf)
+        assert abs(lse - lref) < 1e-12
+        kh, _ = _dequant(kc, ks, kz, vc, vs, vz, vc.astype(np.float64))
+        s = np.concatenate([k_near[:sink], kh, k_near[L - tail:]]) @ q / math.sqrt(d)
+        s_far = s[sink:L - tail]
+        smax = s.max()
+        cold = hot == 0
+        assert np.all(s_far[cold] < smax - tau * math.log(2))
+        assert np.all(hot[s_far >= smax - tau * math.log(2)] == 1)
+        a = np.exp(s - smax)
+        a /= a.sum()
+        grp = np.arange(d) // 32
+        bound_c = 1.5 * (a[sink:L - tail][cold, None] * vs[cold][:, grp]).sum(axis=0)
+        assert np.all(np.abs(out - ref) <= bound_c + 1e-13)
+        assert np.abs(out - ref).max() <= 1.5 * vs.max() * cold.sum() * 2.0 ** -tau * a.max() + 1e-13
+        if tau == 2.0:
+            assert 0 < n_cold < L - sink - tail
+
+
+def test_running_rule_with_dominant_seed_is_the_fixed_rule():
+    """If the sink maximum m0 is at least every far score, max(m, m0) = m0 throughout and the running rule is the
+    fixed rule s >= m0 - tau ln 2; at tau = infinity every token is hot and the row is the reader of both planes."""
+    rng = np.random.default_rng(31)
+    L, d, sink, tail = 600, 64, 4, 16
+    k_near, v_near, kc, ks, kz, vc, vs, vz = _cell_inputs(rng, L, d, sink, tail, 4)
+    q = rng.standard_normal(d)
+    k_near[0] = q * (60.0 * math.sqrt(d) / (q @ q))  # sink score 60, above every far score
+    for tau in (3.0, 6.0):
+        _, _, hot_r, _, _ = oracle.cell_row_running(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail,
+                                                    oracle.CELL_INT4, tau, 4)
+        _, _, hot_f, _ = oracle.cell_row(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail, oracle.CELL_INT4,
+                                         thr_offset=tau * math.log(2))
+        np.testing.assert_array_equal(hot_r, hot_f)
+    out, _, hot, n_cold, _ = oracle.cell_row_running(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail,
+                                                     oracle.CELL_INT4, math.inf, 4)
+    assert hot.all() and n_cold == 0
+    kh, vh = _dequant(kc, ks, kz, vc, vs, vz, vc.astype(np.float64))
+    kk, vv = _view(k_near, v_near, kh, vh, sink, tail)
+    np.testing.assert_allclose(out, _sdpa(q, kk, vv), rtol=0, atol=1e-12)

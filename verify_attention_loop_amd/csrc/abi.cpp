@@ -774,6 +774,9 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
   if (a->split_k < 0 || a->split_k > 64) return c->fail(LKV_EINVAL, "split_k %d outside [0, 64]", a->split_k);
   if (a->index_trace && a->trace_len < 1) return c->fail(LKV_EINVAL, "trace_len must be >= 1");
   if (a->window < -1) return c->fail(LKV_EINVAL, "window %d", a->window);
+  if (a->v_rule != LKV_VRULE_FIXED && a->v_rule != LKV_VRULE_RUNNING)
+    return c->fail(LKV_EINVAL, "v_rule %d", a->v_rule);
+  if (a->v_rule == LKV_VRULE_RUNNING && !(a->v_tau >= 0.f)) return c->fail(LKV_EINVAL, "v_tau must be >= 0");
   hipStream_t s = (hipStream_t)stream;
   if (cfg.quant) return attend_cell(c, a, s);
 
@@ -926,6 +929,8 @@ static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_
     P.bits = bits;
     P.masked = bits == 4 ? 1 : 0;
     P.thr_offset = a->v_thresh_offset;
+    P.rule = a->v_rule;
+    P.v_tau = a->v_tau;
     P.q = (const uint8_t*)a->q + (int64_t)b0 * hq * D * 2;
     P.out = (uint8_t*)a->out + (int64_t)b0 * hq * D * 2;
     P.lse = a->lse ? a->lse + (int64_t)b0 * hq : nullptr;

@@ -286,15 +286,18 @@ __device__ __forceinline__ uint32_t or4(uint32_t v) {
 //     the final loop's for a shared cell).  Per page the K scale is folded into q
 //     and q.z into a bias (LoopKV page, App. E), so a score is bias + sum q'_c c_jc.
 //     The seed m0 is the largest sink score, recomputed by every far block from
-//     the 4 sink keys (no wait on another block); a far token is hot iff
-//     s_j >= m0 - offset.  V: hot tokens read both bit planes (4 hi + lo), cold
+//     the sink keys (no wait on another block).  Hot test of a far token: the fixed
+//     rule s_j >= m0 - offset, or the page's own rule s_j >= max(m, m0) - tau ln 2
+//     with m the far block's running maximum over its pages so far (RUNNING).  V: hot tokens read both bit planes (4 hi + lo), cold
 //     tokens only hi and take the bucket midpoint 4 hi + 1.5; the per-token V
 //     scale and zero fold into the weight p_j (LoopKV page, Sec. 3.3, App. E Alg. 1).
 // Each DPP row keeps its own online softmax; partials go to the workspace and
 // the LSE merge kernel combines them.
-template <int WAVES, bool TRACE, int BITS>
-// The kernel is VALU-bound; asking for five waves per SIMD keeps it at 95 VGPRs without spills.
-__global__ __launch_bounds__(WAVES * 64, 5) void cell_kernel(const CellParams p) {
+template <int WAVES, bool TRACE, int BITS, bool RUNNING>
+// The kernel is VALU-bound; five waves per SIMD fit the fixed rule in 96 VGPRs without spills
+// (the running rule keeps a page's scores across a barrier and takes four; the traced
+// variants, for tests, are left unconstrained).
+__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cell_kernel(const CellParams p) {
   constexpr int D = 128, E = 8;
   constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(WAVES * 64, 5) void cell_kernel(const CellParams p)
       m0 = fmaxf(m0, __shfl_xor(m0, 16));
       m0 = fmaxf(m0, __shfl_xor(m0, 32));
     }
-    const float thr2 = (m0 - p.thr_offset) * 1.4426950408889634f;  // hot test in the base-2 units of x[]
+    constexpr float kLog2e = 1.4426950408889634f;
     constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
     const int n_cp = (n_far + kCodePage - 1) / kCodePage;
     const int c0 = (int)((int64_t)part * n_cp / p.n_splits);
@@ -388,26 +391,26 @@ __global__ __launch_bounds__(WAVES * 64, 5) void cell_kernel(const CellParams p)
     constexpr uint64_t head_bytes = (uint64_t)(BITS == 4 ? 40 : 24) * D;
     constexpr uint64_t vcode_off = BITS == 4 ? 20 * D : 12 * D;
     constexpr uint64_t vmeta_off = BITS == 4 ? 36 * D : 20 * D;
-    for (int cp = c0 + w; cp < c1; cp += WAVES) {
-      const uint8_t* hb = p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes;
+
+    // Key phase of code page cp: loads, K dequant folded into q, scores of tokens g + 4i in
+    // base-2 units (x2), validity; the V codes and V meta are loaded here too.
+    auto far_keys = [&](int cp, const uint8_t*& hb, float* x2, bool* valid, Raw<16>& vh, Raw<32>& vm) {
+      hb = p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes;
       // K meta of this lane's 8 channels -> q' = q * scale, bias = q . zero
       Raw<32> km;
       load_raw<32>(km, hb + li * 32);
+      // Issue the page's code loads together: K codes, V hi (or INT2 V codes), V meta.
+      Raw<16> k0, k1;
+      load_stream<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
+      if constexpr (BITS == 4) load_stream<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
+      load_stream<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
+      load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
       float qs[E], bias = 0.f;
 #pragma unroll
       for (int c = 0; c < E; ++c) {
         qs[c] = qf[c] * f16_to_f32(km.w[c] & 0xFFFFu);
         bias = fmaf(qf[c], f16_to_f32(km.w[c] >> 16), bias);
       }
-      // K codes -> scores of tokens g + 4i
-      // Issue the page's code loads together: K codes, V hi (or INT2 V codes), V meta.
-      Raw<16> k0, k1, vh;
-      Raw<32> vm;
-      load_stream<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
-      if constexpr (BITS == 4) load_stream<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
-      load_stream<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
-      load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
-      float ps[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t code;
@@ -415,20 +418,25 @@ __global__ __launch_bounds__(WAVES * 64, 5) void cell_kernel(const CellParams p)
         else code = lo_nibbles((k0.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
         float f[E];
         nibbles_f32(code, f);
-        float s = bias;
+        float sc = bias;
 #pragma unroll
-        for (int c = 0; c < E; ++c) s = fmaf(qs[c], f[c], s);
-        ps[i] = s;
+        for (int c = 0; c < E; ++c) sc = fmaf(qs[c], f[c], sc);
+        x2[i] = row_sum16(sc) * p.scale_log2;
+        valid[i] = cp * kCodePage + g + 4 * i < n_far;
       }
+    };
+
+    // Value phase: hot test against thr2 (base-2 units), online softmax, V lo of hot tokens,
+    // V dequant folded into the weights, accumulation.
+    auto far_values = [&](int cp, const uint8_t* hb, float* x2, const bool* valid, float thr2, const Raw<16>& vh,
+                          const Raw<32>& vm) {
       float x[8];
-      bool hot[8], valid[8];
+      bool hot[8];
       uint32_t hotbits = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float x2 = row_sum16(ps[i]) * p.scale_log2;
-        valid[i] = cp * kCodePage + g + 4 * i < n_far;
-        hot[i] = valid[i] && (!masked || x2 >= thr2);
-        x[i] = valid[i] ? x2 : -INFINITY;
+        hot[i] = valid[i] && (!masked || x2[i] >= thr2);
+        x[i] = valid[i] ? x2[i] : -INFINITY;
         if (hot[i]) hotbits |= 1u << (g + 4 * i);
       }
       // online softmax of this row (x[] becomes p_j)
@@ -480,6 +488,58 @@ __global__ __launch_bounds__(WAVES * 64, 5) void cell_kernel(const CellParams p)
         const uint32_t word = or4(hotbits);
         if (lane == 0 && p.mask_trace) p.mask_trace[((int64_t)b * p.hq + h) * p.mask_words + cp] = word;
       }
+    };
+
+    if constexpr (!RUNNING || !masked) {
+      // Fixed rule: hot iff s >= m0 - offset.
+      const float thr2 = (m0 - p.thr_offset) * kLog2e;
+      for (int cp = c0 + w; cp < c1; cp += WAVES) {
+        const uint8_t* hb;
+        float x2[8];
+        bool valid[8];
+        Raw<16> vh;
+        Raw<32> vm;
+        far_keys(cp, hb, x2, valid, vh, vm);
+        far_values(cp, hb, x2, valid, thr2, vh, vm);
+      }
+    } else {
+      // The LoopKV page's rule (App. E Algorithm 1): this far block walks its pages in order
+      // with a running maximum m of its scores so far; a token is hot iff
+      // s >= max(m, m0) - tau ln 2, i.e. x2 >= max(m2, m0 log2 e) - tau in base-2 units.
+      // The waves take the block's pages in rounds (page c0 + WAVES r + w) and trade page
+      // maxima through LDS once per round, so the rule is the sequential one whatever the
+      // schedule.  Every wave runs every round, with or without a page, to meet the barrier.
+      __shared__ float sm_pm[2][WAVES];
+      const float m0_2 = m0 * kLog2e;
+      float m_run = -INFINITY;
+      for (int base = c0, round = 0; base < c1; base += WAVES, ++round) {
+        const int cp = base + w;
+        const bool active = cp < c1;  // uniform per wave
+        const uint8_t* hb = nullptr;
+        float x2[8];
+        bool valid[8];
+        Raw<16> vh;
+        Raw<32> vm;
+        float pm = -INFINITY;
+        if (active) {
+          far_keys(cp, hb, x2, valid, vh, vm);
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (valid[i]) pm = fmaxf(pm, x2[i]);
+          pm = fmaxf(pm, __shfl_xor(pm, 16));
+          pm = fmaxf(pm, __shfl_xor(pm, 32));
+        }
+        if (lane == 0) sm_pm[round & 1][w] = pm;
+        __syncthreads();
+        float m_page = m_run;
+#pragma unroll
+        for (int v = 0; v < WAVES; ++v) {
+          const float pv = sm_pm[round & 1][v];
+          if (v <= w) m_page = fmaxf(m_page, pv);
+          m_run = fmaxf(m_run, pv);
+        }
+        if (active) far_values(cp, hb, x2, valid, fmaxf(m_page, m0_2) - p.v_tau, vh, vm);
+      }
     }
   }
 
@@ -512,24 +572,26 @@ __global__ __launch_bounds__(WAVES * 64, 5) void cell_kernel(const CellParams p)
   if (threadIdx.x == 0) wsr[D] = Lsum > 0.f ? M + fast_log2(Lsum) : -INFINITY;
 }
 
-template <int BITS>
+template <int BITS, bool RUNNING>
 static void launch_cell_t(const CellParams& p, int waves, bool trace, dim3 grid, hipStream_t s) {
   if (waves == 2) {
-    if (trace) hipLaunchKernelGGL((cell_kernel<2, true, BITS>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((cell_kernel<2, false, BITS>), grid, dim3(128), 0, s, p);
+    if (trace) hipLaunchKernelGGL((cell_kernel<2, true, BITS, RUNNING>), grid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((cell_kernel<2, false, BITS, RUNNING>), grid, dim3(128), 0, s, p);
   } else {
-    if (trace) hipLaunchKernelGGL((cell_kernel<4, true, BITS>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((cell_kernel<4, false, BITS>), grid, dim3(256), 0, s, p);
+    if (trace) hipLaunchKernelGGL((cell_kernel<4, true, BITS, RUNNING>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((cell_kernel<4, false, BITS, RUNNING>), grid, dim3(256), 0, s, p);
   }
 }
 
 hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s) {
-  if (head_dim != 128 || p.sink > kPage || (p.bits != 4 && p.bits != 2) || p.masked != (p.bits == 4 ? 1 : 0))
+  if (head_dim != 128 || p.sink > kPage || (p.bits != 4 && p.bits != 2) || p.masked != (p.bits == 4 ? 1 : 0) ||
+      (p.rule != 0 && p.rule != 1))
     return hipErrorInvalidValue;
   dim3 grid(p.n_splits + 1, p.hq, p.n_rows);
   const bool trace = p.mask_trace != nullptr;
-  if (p.bits == 4) launch_cell_t<4>(p, waves, trace, grid, s);
-  else launch_cell_t<2>(p, waves, trace, grid, s);
+  if (p.bits == 2) launch_cell_t<2, false>(p, waves, trace, grid, s);  // INT2 cells have no hot test
+  else if (p.rule == 1) launch_cell_t<4, true>(p, waves, trace, grid, s);
+  else launch_cell_t<4, false>(p, waves, trace, grid, s);
   return hipGetLastError();
 }
 

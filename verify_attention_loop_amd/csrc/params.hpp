@@ -65,7 +65,9 @@ struct CellParams {
   int32_t code_ring;
   int32_t bits;               // 4 or 2
   int32_t masked;             // 1: V lo plane read only for hot tokens (INT4 / shared cells)
-  float thr_offset;           // hot iff s >= m0 - thr_offset (natural-log units)
+  float thr_offset;           // rule 0: hot iff s >= m0 - thr_offset (natural-log units)
+  int32_t rule;               // 0: fixed offset from m0; 1: running maximum (LoopKV page, App. E Alg. 1)
+  float v_tau;                // rule 1: hot iff s log2(e) >= max(m, m0) log2(e) - v_tau
   const void* q;
   void* out;
   float* lse;

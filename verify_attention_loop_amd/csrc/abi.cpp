@@ -2,8 +2,11 @@
 // block tables, cell descriptors and argument checking, and the kernel launches.
 //
 // Host bookkeeping only touches host memory; device work (copies, table uploads,
-// kernels) happens in lkv_append_plane / lkv_append_coded / lkv_attend on the
-// caller's stream.  The library never allocates device memory.
+// kernels) happens in lkv_append_plane / lkv_append_coded / lkv_encode_pages /
+// lkv_attend on the caller's stream.  The library never allocates device memory,
+// and every device write it issues is a kernel (block-table rows travel as kernel
+// arguments; trace buffers are cleared by a fill kernel), so the calls can be
+// captured into a graph and never copy from pageable host memory.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -24,6 +27,7 @@ hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int wave
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_append(const CopyParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_fill(void* dst, uint64_t n_bytes, uint32_t value, hipStream_t s);
+hipError_t launch_table_write(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s);
 hipError_t launch_pack_codes(const PackParams& p, int head_dim, hipStream_t s);
 hipError_t launch_encode_pages(const EncodeParams& p, int head_dim, hipStream_t s);
@@ -700,8 +704,8 @@ lkv_status upload(lkv_cache* c, Table& T, const std::vector<int32_t>& seq_slots,
   for (int32_t q : seq_slots) {
     if (!T.dirty[(size_t)q]) continue;
     const size_t off = T.dev_off + (size_t)q * T.ring * 4;
-    hipError_t e = hipMemcpyAsync((uint8_t*)c->ar.meta + off, T.phys.data() + (size_t)q * T.ring, (size_t)T.ring * 4,
-                                  hipMemcpyHostToDevice, s);
+    hipError_t e = launch_table_write((int32_t*)((uint8_t*)c->ar.meta + off), T.phys.data() + (size_t)q * T.ring,
+                                      T.ring, s);
     if (e != hipSuccess) return hip_fail(c, e, "table upload");
     T.dirty[(size_t)q] = 0;
   }
@@ -802,7 +806,7 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
   if (&To != &Td && (st = upload(c, Td, slots, s)) != LKV_OK) return st;
 
   if (a->index_trace) {
-    hipError_t e = hipMemsetAsync(a->index_trace, 0xFF, (size_t)a->n_seqs * a->q_len * a->trace_len * 8, s);
+    hipError_t e = launch_fill(a->index_trace, (uint64_t)a->n_seqs * a->q_len * a->trace_len * 8, 0xFFFFFFFFu, s);
     if (e != hipSuccess) return hip_fail(c, e, "trace clear");
   }
   // Waves per workgroup: 4 for q = 1 rows, 2 for verify tiles (measured best on MI355X
@@ -911,7 +915,7 @@ static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_
   if ((st = upload(c, Tc, slots, s)) != LKV_OK) return st;
   const int mask_words = (max_far + 31) / 32;
   if (a->mask_trace) {
-    hipError_t e = hipMemsetAsync(a->mask_trace, 0, (size_t)a->n_seqs * hq * mask_words * 4, s);
+    hipError_t e = launch_fill(a->mask_trace, (uint64_t)a->n_seqs * hq * mask_words * 4, 0u, s);
     if (e != hipSuccess) return hip_fail(c, e, "mask clear");
   }
   const int waves = env_int("LKV_CELL_WAVES", 4);

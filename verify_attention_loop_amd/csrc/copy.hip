@@ -41,6 +41,10 @@ __global__ __launch_bounds__(256) void fill_words_kernel(uint32_t* dst, int64_t 
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += stride) dst[i] = value;
 }
 
+__global__ __launch_bounds__(256) void table_write_kernel(const TableWriteParams p) {
+  for (int i = threadIdx.x; i < p.n; i += blockDim.x) p.dst[i] = p.vals[i];
+}
+
 static inline int grid_for(int64_t total) {
   int64_t g = (total + 255) / 256;
   if (g > 16384) g = 16384;
@@ -64,6 +68,21 @@ hipError_t launch_fill(void* dst, uint64_t n_bytes, uint32_t value, hipStream_t 
   hipLaunchKernelGGL(fill_words_kernel, dim3(grid_for(n)), dim3(256), 0, s, reinterpret_cast<uint32_t*>(dst), n,
                      value);
   return hipGetLastError();
+}
+
+// Copy n block-table entries from host memory to dst (device) on the stream, in
+// chunks carried as kernel arguments.
+hipError_t launch_table_write(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s) {
+  for (int64_t i0 = 0; i0 < n; i0 += kTableChunk) {
+    TableWriteParams P;
+    P.dst = dst + i0;
+    P.n = (int32_t)(n - i0 < kTableChunk ? n - i0 : kTableChunk);
+    for (int i = 0; i < P.n; ++i) P.vals[i] = src[i0 + i];
+    hipLaunchKernelGGL(table_write_kernel, dim3(1), dim3(256), 0, s, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace lkv

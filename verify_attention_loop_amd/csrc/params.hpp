@@ -118,6 +118,15 @@ struct EncodeParams {
   int32_t phys[64];
 };
 
+// Write up to kTableChunk int32 block-table entries (values passed by value, so no
+// host-to-device copy of pageable memory is needed and the write is a plain kernel).
+constexpr int kTableChunk = 960;
+struct TableWriteParams {
+  int32_t* dst;
+  int32_t n;
+  int32_t vals[kTableChunk];
+};
+
 // Append rows into plain pages.
 struct CopyParams {
   uint8_t* pool;

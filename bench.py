@@ -28,15 +28,25 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "loop-query tokens/s + achieved HBM GB/s (% of MI355X peak), looped-KV attention"
-KERNEL_SOURCES = ["verify_attention_loop_amd/csrc/decode.hip", "verify_attention_loop_amd/csrc/attn_common.hpp",
-                  "verify_attention_loop_amd/csrc/verify.hip", "verify_attention_loop_amd/csrc/copy.hip",
-                  "verify_attention_loop_amd/csrc/cell.hip", "verify_attention_loop_amd/csrc/device.hpp",
-                  "verify_attention_loop_amd/csrc/params.hpp"]
+# Sources of each workload's timed attention kernel (with the shared device headers): the
+# counter summary in profiles/ holds their hash and is ignored once any of them changes.
+_CSRC = "verify_attention_loop_amd/csrc/"
+_COMMON = [_CSRC + "device.hpp", _CSRC + "params.hpp"]
+KERNEL_SOURCES = {
+    "huginn_ripe": [_CSRC + "decode.hip", _CSRC + "attn_common.hpp"] + _COMMON,
+    "ouro_splitk": [_CSRC + "decode.hip", _CSRC + "attn_common.hpp"] + _COMMON,
+    "huginn_verify": [_CSRC + "verify.hip"] + _COMMON,
+    "loopkv_cells": [_CSRC + "cell.hip", _CSRC + "attn_common.hpp"] + _COMMON,
+    "raven_ripe": [_CSRC + "gqa.hip", _CSRC + "attn_common.hpp"] + _COMMON,
+}
+# The timed attention kernel of each workload (rocprofv3 kernel name prefix).
+KERNEL_NAME = {"huginn_ripe": "decode_kernel", "ouro_splitk": "decode_kernel", "huginn_verify": "verify_kernel",
+               "loopkv_cells": "cell_kernel", "raven_ripe": "gqa_decode_kernel"}
 
 
-def kernel_hash() -> str:
+def kernel_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[workload]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -189,11 +199,10 @@ def main():
     if w.quant:
         built = harness.build_cells(w, layers=layers)
         mode = vla.MODE_DECODE
-        kernel = "cell_kernel"
     else:
         built, layers = build_workload(w, args)
         mode = vla.MODE_VERIFY if q_len > 1 else vla.MODE_DECODE
-        kernel = "decode_kernel" if mode == vla.MODE_DECODE else "verify_kernel"
+    kernel = KERNEL_NAME[w.name]
     cache = built.cache
     n_layers_step = w.n_layers
     # Queries and outputs of every (layer, loop) call of a step, resident in HBM.
@@ -272,7 +281,7 @@ def main():
     alg_bytes = float(np.mean(call_bytes))
     # achieved = algorithmic bytes of the sampled launches / their summed duration
     achieved = float(sum(call_bytes[n] for (_, n) in sampled)) / (kern.sum() / 1e3) / 1e9
-    khash = kernel_hash()
+    khash = kernel_hash(args.workload)
     traffic = read_traffic(args.workload, khash)
 
     if args.calibrate_copy:

@@ -33,7 +33,7 @@ def _cells_wl(batch=3):
                           1.0, quant=True, sink=4, tail=128)
 
 
-def _attend_cells(bc, layer, loop, offset, split_k=0):
+def _attend_cells(bc, layer, loop, offset, split_k=0, v_rule=vla.VRULE_FIXED, v_tau=14.0):
     w = bc.w
     n = len(bc.seqs)
     q = harness.gpu_queries(bc, layer, loop, 1)
@@ -45,7 +45,7 @@ def _attend_cells(bc, layer, loop, offset, split_k=0):
     ws = torch.empty(max(4, bc.cache.lkv_workspace_bytes(layer, loop, bc.seqs, split_k=split_k)) + (1 << 20),
                      dtype=torch.uint8, device="cuda")
     bc.cache.lkv_attend(layer, loop, bc.seqs, q, out, split_k=split_k, v_thresh_offset=offset, lse=lse,
-                        workspace=ws, mask_trace=mask)
+                        workspace=ws, mask_trace=mask, v_rule=v_rule, v_tau=v_tau)
     torch.cuda.synchronize()
     return harness.out_f64(out), lse.cpu().numpy(), mask.cpu().numpy().view(np.uint32)
 
@@ -165,4 +165,44 @@ def test_cells_running_rule(tau, split_k):
     assert band_hits < 5
     if tau <= 2.0:
         assert cold > 0
+    bc.cache.close()
+
+
+def test_running_rule_infinite_tau_is_the_all_hot_reader_bitwise():
+    """LoopKV page, Sec. 3.3 and App. I: at tau = infinity the running rule keeps every far token hot, so the
+    cell equals the reader of both V planes (the fixed rule at offset +inf), bit for bit, masks included."""
+    w = _cells_wl(3)
+    bc = harness.build_cells(w, lengths=[133, 640, 1000], layers=(0, 1), plan=PLAN)
+    for layer in (0, 1):
+        for loop in range(4):
+            for split_k in (1, 4):
+                a, la, ma = _attend_cells(bc, layer, loop, math.inf, split_k)
+                b, lb, mb = _attend_cells(bc, layer, loop, 4.0, split_k, v_rule=vla.VRULE_RUNNING, v_tau=math.inf)
+                assert np.array_equal(a, b) and np.array_equal(la, lb) and np.array_equal(ma, mb), (layer, loop)
+    bc.cache.close()
+
+
+@pytest.mark.parametrize("tau", [5.0, 3.0])
+def test_running_rule_hot_set_within_fixed_rule_when_tau_ln2_below_offset(tau):
+    """When tau ln 2 <= offset the page's threshold max(m, m0) - tau ln 2 is never below the fixed m0 - offset,
+    so every token the running rule keeps hot is hot under the fixed rule (both masks come from the same
+    kernel's scores, so the inclusion is exact); with offset 4 and tau 5 or 3 the running rule turns cold
+    at least as many tokens."""
+    w = _cells_wl(3)
+    lengths = [300, 777, 1000]
+    bc = harness.build_cells(w, lengths=lengths, layers=(0,), plan=PLAN)
+    strict = 0
+    for loop in range(4):
+        if PLAN[0, loop] == synth.CELL_INT2:
+            continue
+        for split_k in (1, 3):
+            _, _, mf = _attend_cells(bc, 0, loop, 4.0, split_k)
+            _, _, mr = _attend_cells(bc, 0, loop, 4.0, split_k, v_rule=vla.VRULE_RUNNING, v_tau=tau)
+            for b, L in enumerate(lengths):
+                n_far = L - w.sink - w.tail
+                for h in range(w.n_heads):
+                    f, r = _bits(mf[b, h], n_far), _bits(mr[b, h], n_far)
+                    assert not np.any(r & ~f), (loop, split_k, b, h)
+                    strict += int(np.sum(f & ~r))
+    assert strict > 0
     bc.cache.close()

@@ -1,6 +1,8 @@
-"""Grouped-query attention through the C-ABI against the fp64 oracle: the decode kernel serves the G query heads
-of a KV head from one stream of its pages (G = 2, 4, 8); query head h reads KV head h // G.  Verify and draft run
-on the same caches.  Tolerances as for multi-head caches: 1e-5 (fp32), 2e-2 (bf16)."""
+"""Grouped-query attention through the C-ABI against the fp64 oracle: a workgroup serves the G query heads of a
+KV head from one stream of its pages (G = 2, 4, 8); query head h reads KV head h // G.  Decode runs on the MFMA
+tile kernel (G columns) and, with LKV_GQA_VALU=1, on the VALU decode kernel; verify blocks whose k G fits the
+tile's 16 columns share the tile too.  Draft runs on the same caches.  Tolerances as for multi-head caches:
+1e-5 (fp32), 2e-2 (bf16)."""
 import numpy as np
 import pytest
 
@@ -38,10 +40,12 @@ def _attend(built, layer, loop, q, split_k, mode=vla.MODE_DECODE, trace_len=0, *
     return harness.out_f64(out), lse.cpu().numpy(), tr
 
 
+@pytest.mark.parametrize("kernel", ["tile", "valu"])
 @pytest.mark.parametrize("G", [2, 4, 8])
 @pytest.mark.parametrize("D,dt,tol", [(64, synth.DT_F32, 1e-5), (128, synth.DT_BF16, 2e-2), (96, synth.DT_BF16, 2e-2)])
 @pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 20)])
-def test_gqa_decode_every_row(G, D, dt, tol, policy, W):
+def test_gqa_decode_every_row(G, D, dt, tol, policy, W, kernel, monkeypatch):
+    monkeypatch.setenv("LKV_GQA_VALU", "1" if kernel == "valu" else "0")
     w = _wl(D, G, dt, scale=0.25 if dt == synth.DT_F32 else 1.0)
     lengths = [1, 17, 100, 300]
     built = harness.build_plain(w, lengths=lengths, policy=policy, window=W, shuffle=True, poison=True)
@@ -62,20 +66,29 @@ def test_gqa_decode_every_row(G, D, dt, tol, policy, W):
     built.cache.close()
 
 
-@pytest.mark.parametrize("G", [2, 4])
-def test_gqa_verify_every_row(G):
-    """Verify tiles on a GQA cache (each query head reads its group's KV head)."""
-    w = _wl(64, G, q_len=8)
-    lengths = [8, 40, 300]
-    built = harness.build_plain(w, lengths=lengths, policy=vla.POLICY_RIPE, window=20, q_len=8, shuffle=True,
+@pytest.mark.parametrize("G,k", [(2, 8), (4, 8), (4, 4), (8, 2), (8, 1), (2, 5)])
+def test_gqa_verify_every_row(G, k):
+    """Verify tiles on a GQA cache (each query head reads its group's KV head): k G <= 16 puts the block's rows
+    of all G heads in one tile, k G > 16 (4 x 8) takes one head per tile; RIPE window 20 >= k - 1."""
+    w = _wl(64, G, q_len=k)
+    lengths = [k, 40, 300]
+    built = harness.build_plain(w, lengths=lengths, policy=vla.POLICY_RIPE, window=20, q_len=k, shuffle=True,
                                 poison=True)
-    rows = [(b, i, h) for b in range(3) for i in range(8) for h in range(w.n_heads)]
+    rows = [(b, i, h) for b in range(3) for i in range(k) for h in range(w.n_heads)]
     for loop in (1, 4):
-        want, _ = harness.oracle_rows(w, rows, 0, loop, lengths, 8, vla.POLICY_RIPE, 20)
-        q = harness.gpu_queries(built, 0, loop, 8)
-        o, _, _ = _attend(built, 0, loop, q, 2, mode=vla.MODE_VERIFY)
-        got = np.array([o[b, i, h] for (b, i, h) in rows])
-        assert np.abs(got - want).max() <= 2e-2
+        want, want_lse = harness.oracle_rows(w, rows, 0, loop, lengths, k, vla.POLICY_RIPE, 20)
+        q = harness.gpu_queries(built, 0, loop, k)
+        for split_k in (1, 2):
+            o, lse, tr = _attend(built, 0, loop, q, split_k, mode=vla.MODE_VERIFY, trace_len=300)
+            got = np.array([o[b, i, h] for (b, i, h) in rows])
+            assert np.abs(got - want).max() <= 2e-2, (loop, split_k)
+            got_lse = np.array([lse[b, i, h] for (b, i, h) in rows])
+            assert np.abs(got_lse - want_lse).max() <= 2e-2
+            t = tr.cpu().numpy()
+            for b, L in enumerate(lengths):
+                for i in range(k):
+                    pm = oracle.plane_map(vla.POLICY_RIPE, loop, w.n_loops, L - k + i, L - k, 300, 20)
+                    np.testing.assert_array_equal(t[b, i, :, 0], pm)
     built.cache.close()
 
 

@@ -24,6 +24,8 @@
 namespace lkv {
 hipError_t launch_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s);
 hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s);
+int verify_heads_per_wg(int hq, int hkv, int q_len);
+hipError_t launch_gqa_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_append(const CopyParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_fill(void* dst, uint64_t n_bytes, uint32_t value, hipStream_t s);
@@ -713,10 +715,16 @@ lkv_status upload(lkv_cache* c, Table& T, const std::vector<int32_t>& seq_slots,
 }
 
 // Splits of a plain-cache call: enough workgroups to fill the chip.  Decode and draft
-// workgroups serve all query heads of one KV head; verify workgroups one query head.
-int auto_splits(const lkv_cache* c, int n_seqs, int mode, int max_pages) {
-  const int rows = n_seqs * (mode == LKV_MODE_VERIFY ? c->cfg.n_heads_q : c->cfg.n_heads_kv);
-  const int target = env_int("LKV_TARGET_WGS", 2048);
+// workgroups serve all query heads of one KV head; verify workgroups the query heads of
+// one KV head when the block fits the tile's 16 columns, else one query head.
+// Grouped-query decode aims at two workgroups per CU rather than eight: its kernel time
+// hardly depends on the split count (measured on MI355X), and a call without splits
+// skips the merge kernel.
+int auto_splits(const lkv_cache* c, int n_seqs, int mode, int q_len, int max_pages) {
+  const int hq = c->cfg.n_heads_q, hkv = c->cfg.n_heads_kv;
+  const int rows = n_seqs * (mode == LKV_MODE_VERIFY ? hq / verify_heads_per_wg(hq, hkv, std::max(1, q_len)) : hkv);
+  const bool gqa = mode == LKV_MODE_DECODE && hq > hkv;
+  const int target = gqa ? env_int("LKV_GQA_TARGET_WGS", 512) : env_int("LKV_TARGET_WGS", 2048);
   int s = (target + rows - 1) / rows;
   s = std::min(s, std::max(1, max_pages / 8));
   return std::max(1, std::min(s, 64));
@@ -745,7 +753,7 @@ lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, siz
     max_cp = std::max(max_cp, (std::max(0, L - c->cfg.sink - c->cfg.tail) + kCodePage - 1) / kCodePage);
   }
   const int S = c->cfg.quant ? cell_splits(c, a->n_seqs, a->split_k, max_cp)
-                             : (a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, max_pages));
+                             : (a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, a->q_len, max_pages));
   const int parts = c->cfg.quant ? S + 1 : S;
   if (parts <= 1) {
     *bytes = 0;
@@ -792,7 +800,7 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
   if (st != LKV_OK) return st;
   int max_pages = 0;
   for (const auto& r : rows) max_pages = std::max(max_pages, (r.n_cached + kPage - 1) / kPage);
-  const int S = a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, max_pages);
+  const int S = a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, a->q_len, max_pages);
   const int D = cfg.head_dim, hq = cfg.n_heads_q, es = elem_bytes(cfg);
   const size_t ws_need = S > 1 ? (size_t)a->n_seqs * a->q_len * hq * S * (D + 1) * 4 : 0;
   if (ws_need > 0 && (!a->workspace || a->workspace_bytes < ws_need))
@@ -809,9 +817,16 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
     hipError_t e = launch_fill(a->index_trace, (uint64_t)a->n_seqs * a->q_len * a->trace_len * 8, 0xFFFFFFFFu, s);
     if (e != hipSuccess) return hip_fail(c, e, "trace clear");
   }
+  // q = 1 decode of a grouped-query cache runs on the MFMA kernel (its G query heads are
+  // G columns of one tile); multi-head decode and the draft on the VALU decode kernel.
+  const int group = hq / cfg.n_heads_kv;
+  const bool gqa = a->mode == LKV_MODE_DECODE && (group == 2 || group == 4 || group == 8) &&
+                   env_int("LKV_GQA_VALU", 0) == 0;
   // Waves per workgroup: 4 for q = 1 rows, 2 for verify tiles (measured best on MI355X
   // at the workloads' shapes; the environment can override for experiments).
-  const int waves = a->mode == LKV_MODE_VERIFY ? env_int("LKV_VERIFY_WAVES", 2) : env_int("LKV_WAVES", 4);
+  const int waves = a->mode == LKV_MODE_VERIFY ? env_int("LKV_VERIFY_WAVES", 2)
+                    : gqa                     ? env_int("LKV_GQA_WAVES", 4)
+                                              : env_int("LKV_WAVES", 4);
   const int64_t qrow = (int64_t)a->q_len * hq * D;
   for (int b0 = 0; b0 < a->n_seqs; b0 += kMaxRows) {
     const int nb = std::min(kMaxRows, a->n_seqs - b0);
@@ -849,9 +864,10 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
       P.len[b] = rows[(size_t)(b0 + b)].n_cached;
     }
     if (a->ev_begin && b0 == 0) (void)hipEventRecord((hipEvent_t)a->ev_begin, s);
-    hipError_t e = a->mode == LKV_MODE_VERIFY
-                       ? launch_verify(P, cfg.kv_dtype, D, waves, a->index_trace != nullptr, s)
-                       : launch_decode(P, cfg.kv_dtype, D, waves, a->index_trace != nullptr, s);
+    const bool tr = a->index_trace != nullptr;
+    hipError_t e = a->mode == LKV_MODE_VERIFY ? launch_verify(P, cfg.kv_dtype, D, waves, tr, s)
+                   : gqa                     ? launch_gqa_decode(P, cfg.kv_dtype, D, waves, tr, s)
+                                             : launch_decode(P, cfg.kv_dtype, D, waves, tr, s);
     if (e != hipSuccess) return hip_fail(c, e, "attention kernel");
     if (a->ev_end && b0 + nb >= a->n_seqs) (void)hipEventRecord((hipEvent_t)a->ev_end, s);
     if (S > 1) {

@@ -14,9 +14,15 @@
 // 4g..4g+3) are the tokens g, g+4, g+8, g+12 for query n: exactly the P^T operand
 // of the PV product, and exactly the four tokens of V quad g, whose
 // [channel][4 tokens] layout is the V^T operand (four tokens of one channel per
-// lane).  Columns k..15 of the tile are padding (k <= 16).  V is read with
-// nontemporal loads (whole lines per instruction); K rows are 64-byte pieces of
-// 192-256-byte token rows, so they use plain loads, which L2 merges.
+// lane).  Columns beyond the block are padding.  V is read with nontemporal loads
+// (whole lines per instruction); K rows are 64-byte pieces of 128-256-byte token
+// rows, so they use plain loads, which L2 merges.
+//
+// Grouped-query attention: with G > 1 a workgroup serves the G query heads of one
+// KV head and column n is (block row n / G, head n % G), so every K/V page is read
+// once for all G heads and the softmax work per page does not grow with G.  The
+// q = 1 decode of a grouped cache runs here too (k = 1, G columns): its scores and
+// weighted sums are the same contractions with G columns instead of one.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -36,7 +42,7 @@ __device__ __forceinline__ float xsum4(float v) {
   return v;
 }
 
-template <typename T, int D, int WAVES, bool TRACE>
+template <typename T, int D, int WAVES, bool TRACE, int G>
 __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p) {
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int ES = F32 ? 4 : 2;
@@ -47,16 +53,19 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
   constexpr int NB = F32 ? D / 16 : D / 32;
   constexpr int NACC = F32 ? D / 16 : D / 16;  // 16-channel output blocks
 
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // blockIdx.y: the query head (G = 1) or the KV head whose G query heads share the tile.
+  const int split = blockIdx.x, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
-  const int hk = h / (p.hq / p.hkv);
+  const int hk = G == 1 ? blockIdx.y / (p.hq / p.hkv) : blockIdx.y;
+  const int qi = n / G;                 // block row of column n
+  const int h = blockIdx.y * G + n % G;  // query head of column n
   const int slot = p.slot[b];
   const int L = p.len[b];
   const int k = p.q_len;
   const int t0 = L - k;
-  const bool qv = n < k;
-  const int tq = t0 + n;
+  const bool qv = qi < k;
+  const int tq = t0 + qi;
   const int own_n = p.ripe ? max(0, min(t0, tq - p.window)) : 0;
   const int own_min = p.ripe ? max(0, min(t0, t0 - p.window)) : 0;
   const int own_max = p.ripe ? max(0, min(t0, t0 + k - 1 - p.window)) : 0;
@@ -64,7 +73,7 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
   // Q^T operand (query n), zero for padding columns.
   uint32_t qb[NB][4];
   {
-    const int64_t qrow = (((int64_t)b * k + (qv ? n : 0)) * p.hq + h) * D;
+    const int64_t qrow = (((int64_t)b * k + (qv ? qi : 0)) * p.hq + h) * D;
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + qrow * ES;
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -138,8 +147,8 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
         x[i] = vis ? sc[i] * p.scale_log2 : -INFINITY;
         keep[i] = j < L && (own ? j >= own_min : j < own_max);
         if constexpr (TRACE) {
-          if (h == 0 && vis && j < p.trace_len) {
-            int32_t* tr = p.trace + (((int64_t)b * k + n) * p.trace_len + j) * 2;
+          if (h == 0 && vis && j < p.trace_len) {  // column of head 0 only
+            int32_t* tr = p.trace + (((int64_t)b * k + qi) * p.trace_len + j) * 2;
             tr[0] = own ? p.loop : p.deepest;
             tr[1] = phys * kPage + (j % kPage);
           }
@@ -207,21 +216,21 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
     sm_l[w][n] = lsum;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < k * D; idx += WAVES * 64) {
-    const int qi = idx / D, c = idx % D;
+  for (int idx = threadIdx.x; idx < k * G * D; idx += WAVES * 64) {
+    const int col = idx / D, c = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sm_m[v][qi]);
+    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sm_m[v][col]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float Ls = 0.f, O = 0.f;
 #pragma unroll
     for (int v = 0; v < WAVES; ++v) {
-      const float f = fast_exp2(sm_m[v][qi] - Mu);
-      Ls = fmaf(sm_l[v][qi], f, Ls);
-      O = fmaf(sm_o[v][qi][c], f, O);
+      const float f = fast_exp2(sm_m[v][col] - Mu);
+      Ls = fmaf(sm_l[v][col], f, Ls);
+      O = fmaf(sm_o[v][col][c], f, O);
     }
     const float val = Ls > 0.f ? O / Ls : 0.f;
-    const int64_t row = ((int64_t)b * k + qi) * p.hq + h;
+    const int64_t row = ((int64_t)b * k + col / G) * p.hq + blockIdx.y * G + col % G;
     if (p.n_splits == 1) {
       store_out<T>(p.out, row * D + c, val);
       if (c == 0 && p.lse) p.lse[row] = (Ls > 0.f ? M + fast_log2(Ls) : -INFINITY) * 0.69314718055994531f;
@@ -233,24 +242,42 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
   }
 }
 
+template <typename T, int D, int G>
+static void launch_verify_g(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+  dim3 grid(p.n_splits, p.hq / G, p.n_rows);
+  if (waves == 1) {
+    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 1, true, G>), grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((verify_kernel<T, D, 1, false, G>), grid, dim3(64), 0, s, p);
+  } else if (waves == 2) {
+    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 2, true, G>), grid, dim3(128), 0, s, p);
+    else hipLaunchKernelGGL((verify_kernel<T, D, 2, false, G>), grid, dim3(128), 0, s, p);
+  } else {
+    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 4, true, G>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((verify_kernel<T, D, 4, false, G>), grid, dim3(256), 0, s, p);
+  }
+}
+
+// Query heads per workgroup: the whole group of a KV head when its block rows fit the
+// 16 columns of the tile, else one.
+int verify_heads_per_wg(int hq, int hkv, int q_len) {
+  const int group = hq / hkv;
+  return (group == 2 || group == 4 || group == 8) && q_len * group <= kMaxBlock ? group : 1;
+}
+
 template <typename T, int D>
 static hipError_t launch_verify_t(const PlainParams& p, int waves, bool trace, hipStream_t s) {
-  dim3 grid(p.n_splits, p.hq, p.n_rows);
-  if (waves == 1) {
-    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 1, true>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((verify_kernel<T, D, 1, false>), grid, dim3(64), 0, s, p);
-  } else if (waves == 2) {
-    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 2, true>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((verify_kernel<T, D, 2, false>), grid, dim3(128), 0, s, p);
-  } else {
-    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 4, true>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((verify_kernel<T, D, 4, false>), grid, dim3(256), 0, s, p);
+  switch (verify_heads_per_wg(p.hq, p.hkv, p.q_len)) {
+    case 2: launch_verify_g<T, D, 2>(p, waves, trace, s); break;
+    case 4: launch_verify_g<T, D, 4>(p, waves, trace, s); break;
+    case 8: launch_verify_g<T, D, 8>(p, waves, trace, s); break;
+    default: launch_verify_g<T, D, 1>(p, waves, trace, s); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s) {
-  if (p.q_len < 1 || p.q_len > kMaxBlock) return hipErrorInvalidValue;
+  if (p.q_len < 1 || p.q_len > kMaxBlock || p.draft_len != 0) return hipErrorInvalidValue;
+  if (p.hkv < 1 || p.hq % p.hkv != 0) return hipErrorInvalidValue;
   if (waves != 1 && waves != 2) waves = 4;
   if (dtype == 0) {
     if (head_dim == 64) return launch_verify_t<float, 64>(p, waves, trace, s);

@@ -133,8 +133,11 @@ typedef struct {
   int32_t* index_trace;
   int32_t trace_len;
   uint32_t* mask_trace;
-  /* Optional hipEvent_t pair recorded on `stream` around the main attention kernel
-     (not the merge), for timing. */
+  /* Optional hipEvent_t pair for timing the main attention kernel (not the merge):
+     the launch itself stamps ev_begin with the kernel's start and ev_end with its
+     end (hipExtLaunchKernel), so no marker packets are added to `stream`.  With
+     more than 64 sequences the call launches one kernel per 64; ev_begin then marks
+     the first one's start and ev_end the last one's end.  Either may be NULL. */
   void* ev_begin;
   void* ev_end;
   /* Quantised cells: hot-test rule (LKV_VRULE_*) and, for RUNNING, tau (the page uses 14). */

@@ -19,18 +19,22 @@
 #include <vector>
 
 #include "loopattn.h"
+#include "launch.hpp"
 #include "params.hpp"
 
 namespace lkv {
-hipError_t launch_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s);
-hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s);
+hipError_t launch_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s,
+                         const LaunchEvents& ev);
+hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s,
+                         const LaunchEvents& ev);
 int verify_heads_per_wg(int hq, int hkv, int q_len);
-hipError_t launch_gqa_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s);
+hipError_t launch_gqa_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s,
+                             const LaunchEvents& ev);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_append(const CopyParams& p, int dtype, int head_dim, hipStream_t s);
 hipError_t launch_fill(void* dst, uint64_t n_bytes, uint32_t value, hipStream_t s);
 hipError_t launch_table_write(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
-hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s);
+hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_pack_codes(const PackParams& p, int head_dim, hipStream_t s);
 hipError_t launch_encode_pages(const EncodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_read_codes(const PackParams& p, int head_dim, void* k_codes, void* k_meta, void* v_codes,
@@ -714,6 +718,16 @@ lkv_status upload(lkv_cache* c, Table& T, const std::vector<int32_t>& seq_slots,
   return LKV_OK;
 }
 
+// Timing events of one chunk of an attend call: the caller's begin event is stamped by
+// the first chunk's attention kernel, the end event by the last chunk's (the launch
+// itself stamps them, so no marker packets are added to the stream).
+LaunchEvents launch_events(const lkv_attend_args* a, bool first, bool last) {
+  LaunchEvents ev;
+  if (first) ev.start = (hipEvent_t)a->ev_begin;
+  if (last) ev.stop = (hipEvent_t)a->ev_end;
+  return ev;
+}
+
 // Splits of a plain-cache call: enough workgroups to fill the chip.  Decode and draft
 // workgroups serve all query heads of one KV head; verify workgroups the query heads of
 // one KV head when the block fits the tile's 16 columns, else one query head.
@@ -863,13 +877,12 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
       P.slot[b] = rows[(size_t)(b0 + b)].slot;
       P.len[b] = rows[(size_t)(b0 + b)].n_cached;
     }
-    if (a->ev_begin && b0 == 0) (void)hipEventRecord((hipEvent_t)a->ev_begin, s);
     const bool tr = a->index_trace != nullptr;
-    hipError_t e = a->mode == LKV_MODE_VERIFY ? launch_verify(P, cfg.kv_dtype, D, waves, tr, s)
-                   : gqa                     ? launch_gqa_decode(P, cfg.kv_dtype, D, waves, tr, s)
-                                             : launch_decode(P, cfg.kv_dtype, D, waves, tr, s);
+    const LaunchEvents ev = launch_events(a, b0 == 0, b0 + nb >= a->n_seqs);
+    hipError_t e = a->mode == LKV_MODE_VERIFY ? launch_verify(P, cfg.kv_dtype, D, waves, tr, s, ev)
+                   : gqa                     ? launch_gqa_decode(P, cfg.kv_dtype, D, waves, tr, s, ev)
+                                             : launch_decode(P, cfg.kv_dtype, D, waves, tr, s, ev);
     if (e != hipSuccess) return hip_fail(c, e, "attention kernel");
-    if (a->ev_end && b0 + nb >= a->n_seqs) (void)hipEventRecord((hipEvent_t)a->ev_end, s);
     if (S > 1) {
       MergeParams M{};
       M.ws = P.ws;
@@ -969,10 +982,8 @@ static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_
       P.slot[b] = slots[(size_t)(b0 + b)];
       P.len[b] = c->seqs[(size_t)slots[(size_t)(b0 + b)]].len;
     }
-    if (a->ev_begin && b0 == 0) (void)hipEventRecord((hipEvent_t)a->ev_begin, s);
-    hipError_t e = launch_cell(P, D, waves, s);
+    hipError_t e = launch_cell(P, D, waves, s, launch_events(a, b0 == 0, b0 + nb >= a->n_seqs));
     if (e != hipSuccess) return hip_fail(c, e, "cell kernel");
-    if (a->ev_end && b0 + nb >= a->n_seqs) (void)hipEventRecord((hipEvent_t)a->ev_end, s);
     MergeParams M{};
     M.ws = P.ws;
     M.out = P.out;

@@ -35,6 +35,7 @@
 
 #include "attn_common.hpp"
 #include "device.hpp"
+#include "launch.hpp"
 #include "params.hpp"
 
 namespace lkv {
@@ -683,25 +684,25 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
 }
 
 template <int BITS, bool RUNNING>
-static void launch_cell_t(const CellParams& p, int waves, bool trace, dim3 grid, hipStream_t s) {
+static void launch_cell_t(const CellParams& p, int waves, bool trace, dim3 grid, hipStream_t s, const LaunchEvents& ev) {
   if (waves == 2) {
-    if (trace) hipLaunchKernelGGL((cell_kernel<2, true, BITS, RUNNING>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((cell_kernel<2, false, BITS, RUNNING>), grid, dim3(128), 0, s, p);
+    if (trace) launch_k((cell_kernel<2, true, BITS, RUNNING>), grid, dim3(128), s, ev, p);
+    else launch_k((cell_kernel<2, false, BITS, RUNNING>), grid, dim3(128), s, ev, p);
   } else {
-    if (trace) hipLaunchKernelGGL((cell_kernel<4, true, BITS, RUNNING>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((cell_kernel<4, false, BITS, RUNNING>), grid, dim3(256), 0, s, p);
+    if (trace) launch_k((cell_kernel<4, true, BITS, RUNNING>), grid, dim3(256), s, ev, p);
+    else launch_k((cell_kernel<4, false, BITS, RUNNING>), grid, dim3(256), s, ev, p);
   }
 }
 
-hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s) {
+hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s, const LaunchEvents& ev) {
   if (head_dim != 128 || p.sink > kPage || (p.bits != 4 && p.bits != 2) || p.masked != (p.bits == 4 ? 1 : 0) ||
       (p.rule != 0 && p.rule != 1))
     return hipErrorInvalidValue;
   dim3 grid(p.n_splits + 1, p.hq, p.n_rows);
   const bool trace = p.mask_trace != nullptr;
-  if (p.bits == 2) launch_cell_t<2, false>(p, waves, trace, grid, s);  // INT2 cells have no hot test
-  else if (p.rule == 1) launch_cell_t<4, true>(p, waves, trace, grid, s);
-  else launch_cell_t<4, false>(p, waves, trace, grid, s);
+  if (p.bits == 2) launch_cell_t<2, false>(p, waves, trace, grid, s, ev);  // INT2 cells have no hot test
+  else if (p.rule == 1) launch_cell_t<4, true>(p, waves, trace, grid, s, ev);
+  else launch_cell_t<4, false>(p, waves, trace, grid, s, ev);
   return hipGetLastError();
 }
 

@@ -25,6 +25,7 @@
 
 #include "attn_common.hpp"
 #include "device.hpp"
+#include "launch.hpp"
 #include "params.hpp"
 
 namespace lkv {
@@ -271,44 +272,44 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeParams p) {
 // ----------------------------------------------------------------------------- launchers
 
 template <typename T, int D, int G>
-static void launch_decode_g(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+static void launch_decode_g(const PlainParams& p, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   dim3 grid(p.n_splits, p.hkv, p.n_rows);
   if (waves == 2) {
-    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 2, true, G>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<T, D, 2, false, G>), grid, dim3(128), 0, s, p);
+    if (trace) launch_k((decode_kernel<T, D, 2, true, G>), grid, dim3(128), s, ev, p);
+    else launch_k((decode_kernel<T, D, 2, false, G>), grid, dim3(128), s, ev, p);
   } else if (waves == 8) {
-    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 8, true, G>), grid, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<T, D, 8, false, G>), grid, dim3(512), 0, s, p);
+    if (trace) launch_k((decode_kernel<T, D, 8, true, G>), grid, dim3(512), s, ev, p);
+    else launch_k((decode_kernel<T, D, 8, false, G>), grid, dim3(512), s, ev, p);
   } else {
-    if (trace) hipLaunchKernelGGL((decode_kernel<T, D, 4, true, G>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<T, D, 4, false, G>), grid, dim3(256), 0, s, p);
+    if (trace) launch_k((decode_kernel<T, D, 4, true, G>), grid, dim3(256), s, ev, p);
+    else launch_k((decode_kernel<T, D, 4, false, G>), grid, dim3(256), s, ev, p);
   }
 }
 
 // Group sizes 1 (multi-head), 2, 4 and 8 (grouped-query attention).
 template <typename T, int D>
-static hipError_t launch_decode_t(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+static hipError_t launch_decode_t(const PlainParams& p, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   const int G = p.hq / p.hkv;
   if (G * p.hkv != p.hq) return hipErrorInvalidValue;
   switch (G) {
-    case 1: launch_decode_g<T, D, 1>(p, waves, trace, s); break;
-    case 2: launch_decode_g<T, D, 2>(p, waves, trace, s); break;
-    case 4: launch_decode_g<T, D, 4>(p, waves, trace, s); break;
-    case 8: launch_decode_g<T, D, 8>(p, waves, trace, s); break;
+    case 1: launch_decode_g<T, D, 1>(p, waves, trace, s, ev); break;
+    case 2: launch_decode_g<T, D, 2>(p, waves, trace, s, ev); break;
+    case 4: launch_decode_g<T, D, 4>(p, waves, trace, s, ev); break;
+    case 8: launch_decode_g<T, D, 8>(p, waves, trace, s, ev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s) {
+hipError_t launch_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   if (dtype == 0) {
-    if (head_dim == 64) return launch_decode_t<float, 64>(p, waves, trace, s);
-    if (head_dim == 96) return launch_decode_t<float, 96>(p, waves, trace, s);
-    if (head_dim == 128) return launch_decode_t<float, 128>(p, waves, trace, s);
+    if (head_dim == 64) return launch_decode_t<float, 64>(p, waves, trace, s, ev);
+    if (head_dim == 96) return launch_decode_t<float, 96>(p, waves, trace, s, ev);
+    if (head_dim == 128) return launch_decode_t<float, 128>(p, waves, trace, s, ev);
   } else {
-    if (head_dim == 64) return launch_decode_t<bf16, 64>(p, waves, trace, s);
-    if (head_dim == 96) return launch_decode_t<bf16, 96>(p, waves, trace, s);
-    if (head_dim == 128) return launch_decode_t<bf16, 128>(p, waves, trace, s);
+    if (head_dim == 64) return launch_decode_t<bf16, 64>(p, waves, trace, s, ev);
+    if (head_dim == 96) return launch_decode_t<bf16, 96>(p, waves, trace, s, ev);
+    if (head_dim == 128) return launch_decode_t<bf16, 128>(p, waves, trace, s, ev);
   }
   return hipErrorInvalidValue;
 }

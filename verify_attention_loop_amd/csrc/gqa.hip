@@ -25,6 +25,7 @@
 
 #include "attn_common.hpp"
 #include "device.hpp"
+#include "launch.hpp"
 #include "params.hpp"
 
 namespace lkv {
@@ -244,43 +245,43 @@ __global__ __launch_bounds__(WAVES * 64) void gqa_decode_kernel(const PlainParam
 }
 
 template <typename T, int D, int G>
-static void launch_gqa_g(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+static void launch_gqa_g(const PlainParams& p, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   dim3 grid(p.n_splits, p.hkv, p.n_rows);
   if (waves == 1) {
-    if (trace) hipLaunchKernelGGL((gqa_decode_kernel<T, D, 1, true, G>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((gqa_decode_kernel<T, D, 1, false, G>), grid, dim3(64), 0, s, p);
+    if (trace) launch_k((gqa_decode_kernel<T, D, 1, true, G>), grid, dim3(64), s, ev, p);
+    else launch_k((gqa_decode_kernel<T, D, 1, false, G>), grid, dim3(64), s, ev, p);
   } else if (waves == 2) {
-    if (trace) hipLaunchKernelGGL((gqa_decode_kernel<T, D, 2, true, G>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((gqa_decode_kernel<T, D, 2, false, G>), grid, dim3(128), 0, s, p);
+    if (trace) launch_k((gqa_decode_kernel<T, D, 2, true, G>), grid, dim3(128), s, ev, p);
+    else launch_k((gqa_decode_kernel<T, D, 2, false, G>), grid, dim3(128), s, ev, p);
   } else {
-    if (trace) hipLaunchKernelGGL((gqa_decode_kernel<T, D, 4, true, G>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((gqa_decode_kernel<T, D, 4, false, G>), grid, dim3(256), 0, s, p);
+    if (trace) launch_k((gqa_decode_kernel<T, D, 4, true, G>), grid, dim3(256), s, ev, p);
+    else launch_k((gqa_decode_kernel<T, D, 4, false, G>), grid, dim3(256), s, ev, p);
   }
 }
 
 template <typename T, int D>
-static hipError_t launch_gqa_t(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+static hipError_t launch_gqa_t(const PlainParams& p, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   switch (p.hq / p.hkv) {
-    case 2: launch_gqa_g<T, D, 2>(p, waves, trace, s); break;
-    case 4: launch_gqa_g<T, D, 4>(p, waves, trace, s); break;
-    case 8: launch_gqa_g<T, D, 8>(p, waves, trace, s); break;
+    case 2: launch_gqa_g<T, D, 2>(p, waves, trace, s, ev); break;
+    case 4: launch_gqa_g<T, D, 4>(p, waves, trace, s, ev); break;
+    case 8: launch_gqa_g<T, D, 8>(p, waves, trace, s, ev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 // Grouped-query decode (group 2, 4 or 8; q = 1, no draft block).
-hipError_t launch_gqa_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s) {
+hipError_t launch_gqa_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   if (p.q_len != 1 || p.draft_len != 0 || p.hkv < 1 || p.hq % p.hkv != 0) return hipErrorInvalidValue;
   if (waves != 1 && waves != 2) waves = 4;
   if (dtype == 0) {
-    if (head_dim == 64) return launch_gqa_t<float, 64>(p, waves, trace, s);
-    if (head_dim == 96) return launch_gqa_t<float, 96>(p, waves, trace, s);
-    if (head_dim == 128) return launch_gqa_t<float, 128>(p, waves, trace, s);
+    if (head_dim == 64) return launch_gqa_t<float, 64>(p, waves, trace, s, ev);
+    if (head_dim == 96) return launch_gqa_t<float, 96>(p, waves, trace, s, ev);
+    if (head_dim == 128) return launch_gqa_t<float, 128>(p, waves, trace, s, ev);
   } else {
-    if (head_dim == 64) return launch_gqa_t<bf16, 64>(p, waves, trace, s);
-    if (head_dim == 96) return launch_gqa_t<bf16, 96>(p, waves, trace, s);
-    if (head_dim == 128) return launch_gqa_t<bf16, 128>(p, waves, trace, s);
+    if (head_dim == 64) return launch_gqa_t<bf16, 64>(p, waves, trace, s, ev);
+    if (head_dim == 96) return launch_gqa_t<bf16, 96>(p, waves, trace, s, ev);
+    if (head_dim == 128) return launch_gqa_t<bf16, 128>(p, waves, trace, s, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
+#include "launch.hpp"
 #include "params.hpp"
 
 namespace lkv {
@@ -243,17 +244,17 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
 }
 
 template <typename T, int D, int G>
-static void launch_verify_g(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+static void launch_verify_g(const PlainParams& p, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   dim3 grid(p.n_splits, p.hq / G, p.n_rows);
   if (waves == 1) {
-    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 1, true, G>), grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL((verify_kernel<T, D, 1, false, G>), grid, dim3(64), 0, s, p);
+    if (trace) launch_k((verify_kernel<T, D, 1, true, G>), grid, dim3(64), s, ev, p);
+    else launch_k((verify_kernel<T, D, 1, false, G>), grid, dim3(64), s, ev, p);
   } else if (waves == 2) {
-    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 2, true, G>), grid, dim3(128), 0, s, p);
-    else hipLaunchKernelGGL((verify_kernel<T, D, 2, false, G>), grid, dim3(128), 0, s, p);
+    if (trace) launch_k((verify_kernel<T, D, 2, true, G>), grid, dim3(128), s, ev, p);
+    else launch_k((verify_kernel<T, D, 2, false, G>), grid, dim3(128), s, ev, p);
   } else {
-    if (trace) hipLaunchKernelGGL((verify_kernel<T, D, 4, true, G>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((verify_kernel<T, D, 4, false, G>), grid, dim3(256), 0, s, p);
+    if (trace) launch_k((verify_kernel<T, D, 4, true, G>), grid, dim3(256), s, ev, p);
+    else launch_k((verify_kernel<T, D, 4, false, G>), grid, dim3(256), s, ev, p);
   }
 }
 
@@ -265,28 +266,28 @@ int verify_heads_per_wg(int hq, int hkv, int q_len) {
 }
 
 template <typename T, int D>
-static hipError_t launch_verify_t(const PlainParams& p, int waves, bool trace, hipStream_t s) {
+static hipError_t launch_verify_t(const PlainParams& p, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   switch (verify_heads_per_wg(p.hq, p.hkv, p.q_len)) {
-    case 2: launch_verify_g<T, D, 2>(p, waves, trace, s); break;
-    case 4: launch_verify_g<T, D, 4>(p, waves, trace, s); break;
-    case 8: launch_verify_g<T, D, 8>(p, waves, trace, s); break;
-    default: launch_verify_g<T, D, 1>(p, waves, trace, s); break;
+    case 2: launch_verify_g<T, D, 2>(p, waves, trace, s, ev); break;
+    case 4: launch_verify_g<T, D, 4>(p, waves, trace, s, ev); break;
+    case 8: launch_verify_g<T, D, 8>(p, waves, trace, s, ev); break;
+    default: launch_verify_g<T, D, 1>(p, waves, trace, s, ev); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s) {
+hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   if (p.q_len < 1 || p.q_len > kMaxBlock || p.draft_len != 0) return hipErrorInvalidValue;
   if (p.hkv < 1 || p.hq % p.hkv != 0) return hipErrorInvalidValue;
   if (waves != 1 && waves != 2) waves = 4;
   if (dtype == 0) {
-    if (head_dim == 64) return launch_verify_t<float, 64>(p, waves, trace, s);
-    if (head_dim == 96) return launch_verify_t<float, 96>(p, waves, trace, s);
-    if (head_dim == 128) return launch_verify_t<float, 128>(p, waves, trace, s);
+    if (head_dim == 64) return launch_verify_t<float, 64>(p, waves, trace, s, ev);
+    if (head_dim == 96) return launch_verify_t<float, 96>(p, waves, trace, s, ev);
+    if (head_dim == 128) return launch_verify_t<float, 128>(p, waves, trace, s, ev);
   } else {
-    if (head_dim == 64) return launch_verify_t<bf16, 64>(p, waves, trace, s);
-    if (head_dim == 96) return launch_verify_t<bf16, 96>(p, waves, trace, s);
-    if (head_dim == 128) return launch_verify_t<bf16, 128>(p, waves, trace, s);
+    if (head_dim == 64) return launch_verify_t<bf16, 64>(p, waves, trace, s, ev);
+    if (head_dim == 96) return launch_verify_t<bf16, 96>(p, waves, trace, s, ev);
+    if (head_dim == 128) return launch_verify_t<bf16, 128>(p, waves, trace, s, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -241,7 +241,7 @@ def build_cells(w: synth.Workload, *, lengths=None, layers=(0,), loops=None, pla
     for L in lengths:
         n_far = L - w.sink - w.tail
         n_cp = (n_far + 31) // 32
-        near_pages = len({0} | set(range((L - w.tail) // 16, (L - 1) // 16 + 1)))
+        near_pages = len(set(range((w.sink - 1) // 16 + 1)) | set(range((L - w.tail) // 16, (L - 1) // 16 + 1)))
         for (layer, r) in needed:
             n_near += near_pages
             if plan[layer, r] == synth.CELL_INT4:

@@ -84,7 +84,7 @@ typedef struct {
   int32_t max_len;      /* longest sequence, positions */
   int32_t max_block;    /* longest verify block (q_len), 1..16 */
   int32_t quant;        /* 0: plain planes; 1: LoopKV-style cells (bf16, FULL) */
-  int32_t sink;         /* quant: exact sink positions [0, sink) */
+  int32_t sink;         /* quant: exact sink positions [0, sink), 1..64 (the page's rule uses 32) */
   int32_t tail;         /* quant: exact tail positions [L - tail, L) */
   int32_t poison;       /* 1: fill pages with NaN when handed out (debug) */
   uint64_t shuffle_seed;/* 0: free pages handed out in address order; else a seeded permutation */

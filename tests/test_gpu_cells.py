@@ -206,3 +206,43 @@ def test_running_rule_hot_set_within_fixed_rule_when_tau_ln2_below_offset(tau):
                     strict += int(np.sum(f & ~r))
     assert strict > 0
     bc.cache.close()
+
+
+@pytest.mark.parametrize("rule,tau", [("fixed", 0.0), ("running", 14.0), ("running", 3.0)])
+def test_cells_32_sink_keys(rule, tau):
+    """The LoopKV page seeds its hot test with the largest of 32 sink scores (App. E); sink 32 spans two plain
+    pages.  Lengths 161 (= 32 + 128 + 1: one far token), 420 and 1000; fixed rule (offset 4) and the running
+    rule (tau 14 and 3) vs the oracle with the same far partition: outputs within 2e-2, hot masks bit-exact
+    outside a 1e-4 band around each token's threshold."""
+    w = synth.Workload("cells32", 3, 1, 4, 2, 128, 1000, synth.DT_BF16, "full", 0, 1, 16, synth.MODE_PLAIN,
+                       1.0, quant=True, sink=32, tail=128)
+    lengths = [161, 420, 1000]
+    bc = harness.build_cells(w, lengths=lengths, layers=(0,), plan=PLAN[:1])
+    band_hits = 0
+    for loop in range(4):
+        for split_k in (1, 3):
+            if rule == "fixed":
+                out, _, mask = _attend_cells(bc, 0, loop, 4.0, split_k)
+            else:
+                out, _, mask = _attend_cells(bc, 0, loop, 4.0, split_k, v_rule=vla.VRULE_RUNNING, v_tau=tau)
+            S = min(split_k, max((L - w.sink - w.tail + 31) // 32 for L in lengths))
+            for b, L in enumerate(lengths):
+                n_far = L - w.sink - w.tail
+                for h in range(w.n_heads):
+                    a = harness.cell_inputs(bc, b, 0, loop, h)
+                    if rule == "fixed":
+                        want, _, hot, s_far, thr = harness.cell_oracle_row(bc, b, 0, loop, h, 4.0)
+                        thr = np.full(n_far, thr)
+                    else:
+                        want, _, hot, _, thr = oracle.cell_row_running(
+                            a["q"], a["k_near"], a["v_near"], a["kc"], a["ks"], a["kz"], a["vc"], a["vs"], a["vz"],
+                            a["sink"], a["tail"], a["kind"], tau, S)
+                        g = np.arange(n_far) // 32
+                        s_far = (a["kz"][g] + a["ks"][g] * a["kc"]) @ a["q"] / math.sqrt(w.head_dim)
+                    assert np.abs(out[b, 0, h] - want).max() <= TOL, (loop, split_k, b, h)
+                    got = _bits(mask[b, h], n_far)
+                    near = (np.abs(s_far - thr) <= BAND) if a["kind"] != oracle.CELL_INT2 else np.zeros(n_far, bool)
+                    assert np.array_equal(got[~near], hot[~near]), (loop, split_k, b, h)
+                    band_hits += int(near.sum())
+    assert band_hits < 5
+    bc.cache.close()

@@ -211,6 +211,19 @@ def test_config_validation(lib):
         vla.LoopCache.sizes(cfg)
 
 
+def test_sink_range(lib):
+    """Quantised cells take 1..64 exact sink positions (the LoopKV page's own rule seeds m0 from 32)."""
+    def cfg(sink):
+        return vla.LoopCache.config(n_layers=1, n_loops=2, n_heads_q=4, n_heads_kv=4, head_dim=128,
+                                    kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=2,
+                                    max_len=400, max_block=1, quant=1, sink=sink, tail=128)
+    for ok in (1, 4, 32, 64):
+        vla.LoopCache.sizes(cfg(ok))
+    for bad in (0, 65, -1):
+        with pytest.raises(vla.LkvError):
+            vla.LoopCache.sizes(cfg(bad))
+
+
 def test_plan_rules(lib):
     cfg = vla.LoopCache.config(n_layers=2, n_loops=4, n_heads_q=16, n_heads_kv=16, head_dim=128,
                                kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=2,

@@ -154,7 +154,7 @@ lkv_status check_config(const lkv_config* c, std::string* why) {
   if (c->quant) {
     if (c->kv_dtype != LKV_DTYPE_BF16) return bad("quantised cells keep bf16 sink and tail");
     if (c->policy != LKV_POLICY_FULL) return bad("quantised cells use the full-cache policy");
-    if (c->sink < 1 || c->sink > kPage || c->tail < 0) return bad("quantised cells need 1 <= sink <= 16, tail >= 0");
+    if (c->sink < 1 || c->sink > 4 * kPage || c->tail < 0) return bad("quantised cells need 1 <= sink <= 64, tail >= 0");
     if (c->head_dim % 32) return bad("quantised cells need head_dim % 32 == 0");
     if (c->head_dim != 128) return bad("quantised cells are built for head_dim 128");
   }

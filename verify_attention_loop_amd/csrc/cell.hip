@@ -406,12 +406,12 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
     // ---------------- far block
     // seed m0: largest exact sink score (natural-log units)
     float m0 = -INFINITY;
-    {
-      const uint8_t* base = p.pool + (uint64_t)tab_near[0] * p.page_bytes;
+    for (int sp = 0; sp * kPage < p.sink; ++sp) {  // sink pages (the page's own rule uses 32 sink keys)
+      const uint8_t* base = p.pool + (uint64_t)tab_near[sp] * p.page_bytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 4 * g + i;
-        if (j < p.sink) {  // uniform per DPP row
+        if (sp * kPage + j < p.sink) {  // uniform per DPP row
           Raw<16> kr;
           load_raw<16>(kr, base + koff + (uint64_t)j * (D * 2));
           float s = 0.f;
@@ -420,9 +420,9 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
           m0 = fmaxf(m0, row_sum16(s) * p.scale);
         }
       }
-      m0 = fmaxf(m0, __shfl_xor(m0, 16));
-      m0 = fmaxf(m0, __shfl_xor(m0, 32));
     }
+    m0 = fmaxf(m0, __shfl_xor(m0, 16));
+    m0 = fmaxf(m0, __shfl_xor(m0, 32));
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
     const int n_cp = (n_far + kCodePage - 1) / kCodePage;
@@ -695,7 +695,7 @@ static void launch_cell_t(const CellParams& p, int waves, bool trace, dim3 grid,
 }
 
 hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s, const LaunchEvents& ev) {
-  if (head_dim != 128 || p.sink > kPage || (p.bits != 4 && p.bits != 2) || p.masked != (p.bits == 4 ? 1 : 0) ||
+  if (head_dim != 128 || p.sink < 1 || p.sink > 4 * kPage || (p.bits != 4 && p.bits != 2) || p.masked != (p.bits == 4 ? 1 : 0) ||
       (p.rule != 0 && p.rule != 1))
     return hipErrorInvalidValue;
   dim3 grid(p.n_splits + 1, p.hq, p.n_rows);

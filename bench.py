@@ -38,10 +38,11 @@ KERNEL_SOURCES = {
     "huginn_verify": [_CSRC + "verify.hip"] + _COMMON,
     "loopkv_cells": [_CSRC + "cell.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "raven_ripe": [_CSRC + "gqa.hip", _CSRC + "attn_common.hpp"] + _COMMON,
+    "dory_lastloop": [_CSRC + "gqa.hip", _CSRC + "attn_common.hpp"] + _COMMON,
 }
 # The timed attention kernel of each workload (rocprofv3 kernel name prefix).
 KERNEL_NAME = {"huginn_ripe": "decode_kernel", "ouro_splitk": "decode_kernel", "huginn_verify": "verify_kernel",
-               "loopkv_cells": "cell_kernel", "raven_ripe": "gqa_decode_kernel"}
+               "loopkv_cells": "cell_kernel", "raven_ripe": "gqa_decode_kernel", "dory_lastloop": "gqa_decode_kernel"}
 
 
 def kernel_hash(workload: str) -> str:
@@ -58,7 +59,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="huginn_ripe",
-                    choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "loopkv_cells", "raven_ripe"])
+                    choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "loopkv_cells", "raven_ripe",
+                             "dory_lastloop"])
     ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers held in HBM (0: all)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -75,7 +75,7 @@ typedef struct {
   int32_t n_loops;      /* R */
   int32_t n_heads_q;    /* query heads */
   int32_t n_heads_kv;   /* KV heads; n_heads_q % n_heads_kv == 0 */
-  int32_t head_dim;     /* 64, 96 or 128 */
+  int32_t head_dim;     /* 64, 96, 128, or 256 (bf16 caches, plain planes) */
   int32_t page_size;    /* tokens per plain page: must be LKV_PAGE_TOKENS */
   int32_t kv_dtype;     /* LKV_DTYPE_F32 or LKV_DTYPE_BF16 (also the q / out dtype) */
   int32_t policy;       /* LKV_POLICY_FULL or LKV_POLICY_RIPE */

@@ -308,6 +308,12 @@ WORKLOADS = {
     # by groups of 4 query heads (32 query heads), L=1024, W=64, batch 64.
     "raven_ripe": Workload("raven_ripe", 64, 6, 32, 32, 64, 1024, DT_BF16, "ripe", 64, 1, 16, MODE_RIPEN, 1.0,
                            split_k=0, n_kv_heads=8),
+    # Dory-shaped grouped-query decode in the model's trained last-loop mode: every loop reads the final
+    # loop's KV for the history (the deepest-plane cache, RIPE with W = 0) and its own plane only for the
+    # current token.  5 recurrent full-attention layers x 4 loops, 4 KV heads x 256 shared by groups of 4
+    # query heads (16 query heads), L = 16384, batch 32.
+    "dory_lastloop": Workload("dory_lastloop", 32, 5, 4, 16, 256, 16384, DT_BF16, "ripe", 0, 1, 16, MODE_PLAIN,
+                              1.0, split_k=0, n_kv_heads=4),
     # split_k 0: the library chooses the number of far splits.
     "loopkv_cells": Workload("loopkv_cells", 16, 24, 4, 16, 128, 16384, DT_BF16, "full", 0, 1, 16,
                              MODE_PLAIN, 1.0, split_k=0, quant=True, sink=4, tail=128),

@@ -70,7 +70,7 @@ def _ragged(D, mode=synth.MODE_RIPEN):
     return synth.Workload("ragged", 6, 2, 5, 3, D, 257, synth.DT_BF16, "ripe", 20, 1, 16, mode, 1.0)
 
 
-@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("D", [64, 96, 128, 256])
 @pytest.mark.parametrize("policy", [vla.POLICY_FULL, vla.POLICY_RIPE])
 def test_ragged_lengths_bf16(D, policy):
     """Ragged batch (lengths 1, 15, 16, 17, 100, 257: empty window, page edges, partial pages), shuffled

@@ -42,7 +42,8 @@ def _attend(built, layer, loop, q, split_k, mode=vla.MODE_DECODE, trace_len=0, *
 
 @pytest.mark.parametrize("kernel", ["tile", "valu"])
 @pytest.mark.parametrize("G", [2, 4, 8])
-@pytest.mark.parametrize("D,dt,tol", [(64, synth.DT_F32, 1e-5), (128, synth.DT_BF16, 2e-2), (96, synth.DT_BF16, 2e-2)])
+@pytest.mark.parametrize("D,dt,tol", [(64, synth.DT_F32, 1e-5), (128, synth.DT_BF16, 2e-2), (96, synth.DT_BF16, 2e-2),
+                                      (256, synth.DT_BF16, 2e-2)])
 @pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 20)])
 def test_gqa_decode_every_row(G, D, dt, tol, policy, W, kernel, monkeypatch):
     monkeypatch.setenv("LKV_GQA_VALU", "1" if kernel == "valu" else "0")
@@ -66,11 +67,12 @@ def test_gqa_decode_every_row(G, D, dt, tol, policy, W, kernel, monkeypatch):
     built.cache.close()
 
 
-@pytest.mark.parametrize("G,k", [(2, 8), (4, 8), (4, 4), (8, 2), (8, 1), (2, 5)])
-def test_gqa_verify_every_row(G, k):
+@pytest.mark.parametrize("G,k,D", [(2, 8, 64), (4, 8, 64), (4, 4, 64), (8, 2, 64), (8, 1, 64), (2, 5, 64),
+                                   (4, 4, 256), (4, 8, 256)])
+def test_gqa_verify_every_row(G, k, D):
     """Verify tiles on a GQA cache (each query head reads its group's KV head): k G <= 16 puts the block's rows
     of all G heads in one tile, k G > 16 (4 x 8) takes one head per tile; RIPE window 20 >= k - 1."""
-    w = _wl(64, G, q_len=k)
+    w = _wl(D, G, q_len=k)
     lengths = [k, 40, 300]
     built = harness.build_plain(w, lengths=lengths, policy=vla.POLICY_RIPE, window=20, q_len=k, shuffle=True,
                                 poison=True)
@@ -92,11 +94,11 @@ def test_gqa_verify_every_row(G, k):
     built.cache.close()
 
 
-@pytest.mark.parametrize("G", [2, 8])
-def test_gqa_draft_step(G):
+@pytest.mark.parametrize("G,D", [(2, 128), (8, 128), (4, 256)])
+def test_gqa_draft_step(G, D):
     """Draft step on a GQA cache: cached positions through the policy, the block from scratch keys/values of the
     KV heads."""
-    w = _wl(128, G)
+    w = _wl(D, G)
     n_cached = [30, 200]
     dl = 3
     built = harness.build_plain(w, lengths=n_cached, policy=vla.POLICY_RIPE, window=12, q_len=1, shuffle=True,
@@ -138,6 +140,24 @@ def test_raven_ripe_full_size_sampled():
     built = harness.build_plain(w, layers=(0,))
     rows = harness.sample_rows(w.batch, 1, w.n_heads, 24, seed=5)
     for loop in (0, 31):
+        q = harness.gpu_queries(built, 0, loop, 1)
+        o, _, _ = _attend(built, 0, loop, q, 0)
+        assert np.isfinite(o).all()
+        want, _ = harness.oracle_rows(w, rows, 0, loop, built.lengths, 1, vla.POLICY_RIPE, w.window)
+        got = np.array([o[b, i, h] for (b, i, h) in rows])
+        assert np.abs(got - want).max() <= 2e-2
+    built.cache.close()
+
+
+@pytest.mark.slow
+def test_dory_lastloop_full_size_sampled():
+    """Dory-shaped decode in the last-loop mode at full size for one layer (32 sequences, 16 query heads over
+    4 KV heads x 256, L = 16384, W = 0: the history from the final loop's plane, the current token from the
+    loop's own): sampled rows vs the oracle, in the launch configuration the benchmark times."""
+    w = synth.WORKLOADS["dory_lastloop"]
+    built = harness.build_plain(w, layers=(0,))
+    rows = harness.sample_rows(w.batch, 1, w.n_heads, 16, seed=6)
+    for loop in (0, 3):
         q = harness.gpu_queries(built, 0, loop, 1)
         o, _, _ = _attend(built, 0, loop, q, 0)
         assert np.isfinite(o).all()

@@ -39,7 +39,7 @@ def _wl(D, dt=synth.DT_BF16, scale=1.0, R=5, H=3):
     return synth.Workload("verify", 4, 2, R, H, D, 300, dt, "ripe", 20, 8, 16, synth.MODE_RIPEN, scale)
 
 
-@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("D", [64, 96, 128, 256])
 @pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 0), (vla.POLICY_RIPE, 7),
                                       (vla.POLICY_RIPE, 20)])
 def test_verify_bf16_every_row(D, policy, W):
@@ -144,7 +144,7 @@ def _draft_inputs(w, n_seqs, layer, loop, n_cached, dl, rows):
 
 
 @pytest.mark.parametrize("policy,W", [(vla.POLICY_RIPE, 0), (vla.POLICY_RIPE, 12), (vla.POLICY_FULL, 0)])
-@pytest.mark.parametrize("D", [96, 128])
+@pytest.mark.parametrize("D", [96, 128, 256])
 def test_draft_step(policy, W, D):
     """RIPE page, Alg. 1 draft: the query (last draft token) reads cached positions through the policy
     (W = 0: the deepest plane) and the draft block's own keys/values from scratch."""

@@ -143,7 +143,9 @@ lkv_status check_config(const lkv_config* c, std::string* why) {
   if (!c) return bad("config is NULL");
   if (c->n_layers < 1 || c->n_loops < 1) return bad("n_layers and n_loops must be >= 1");
   if (c->n_heads_q < 1 || c->n_heads_kv < 1 || c->n_heads_q % c->n_heads_kv) return bad("bad head counts");
-  if (c->head_dim != 64 && c->head_dim != 96 && c->head_dim != 128) return bad("head_dim must be 64, 96 or 128");
+  if (c->head_dim != 64 && c->head_dim != 96 && c->head_dim != 128 && c->head_dim != 256)
+    return bad("head_dim must be 64, 96, 128 or 256");
+  if (c->head_dim == 256 && c->kv_dtype != LKV_DTYPE_BF16) return bad("head_dim 256 is built for bf16 caches");
   if (c->page_size != LKV_PAGE_TOKENS) return bad("page_size must be 16");
   if (c->kv_dtype != LKV_DTYPE_F32 && c->kv_dtype != LKV_DTYPE_BF16) return bad("bad kv_dtype");
   if (c->policy != LKV_POLICY_FULL && c->policy != LKV_POLICY_RIPE) return bad("bad policy");

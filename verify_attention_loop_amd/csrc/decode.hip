@@ -101,7 +101,10 @@ __global__ __launch_bounds__(WAVES * 64, (G == 1 && D == 96 && sizeof(T) == 2) ?
       const int j = pos + 4 * i + g;
       const bool own = (j < n_cached) ? (j >= own_lo) : any_own;
       const uint8_t* bp = own ? base_own : base_deep;
-      load_stream<KB>(kr[i], bp + koff + (uint64_t)(4 * i + g) * (D * ES));
+      // a lane's K run is one 16-byte piece of a token row: nontemporal when the wave
+      // instruction covers whole lines (KB <= 16), plain loads for longer runs
+      if constexpr (KB <= 16) load_stream<KB>(kr[i], bp + koff + (uint64_t)(4 * i + g) * (D * ES));
+      else load_raw<KB>(kr[i], bp + koff + (uint64_t)(4 * i + g) * (D * ES));
     }
     Raw<VB> vr;
     load_vquad<T, D>(vr, (any_own ? base_own : base_deep) + voff);
@@ -310,6 +313,7 @@ hipError_t launch_decode(const PlainParams& p, int dtype, int head_dim, int wave
     if (head_dim == 64) return launch_decode_t<bf16, 64>(p, waves, trace, s, ev);
     if (head_dim == 96) return launch_decode_t<bf16, 96>(p, waves, trace, s, ev);
     if (head_dim == 128) return launch_decode_t<bf16, 128>(p, waves, trace, s, ev);
+    if (head_dim == 256) return launch_decode_t<bf16, 256>(p, waves, trace, s, ev);
   }
   return hipErrorInvalidValue;
 }
@@ -324,7 +328,8 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream
   } else {
     if (head_dim == 64) hipLaunchKernelGGL((merge_kernel<bf16, 64>), grid, dim3(256), 0, s, p);
     else if (head_dim == 96) hipLaunchKernelGGL((merge_kernel<bf16, 96>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((merge_kernel<bf16, 128>), grid, dim3(256), 0, s, p);
+    else if (head_dim == 128) hipLaunchKernelGGL((merge_kernel<bf16, 128>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((merge_kernel<bf16, 256>), grid, dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }

@@ -17,8 +17,8 @@
 // their plane, and a page that straddles the window edge loads both V quads and
 // blends them per token.
 //
-// Each wave walks its pages with two register buffers: the loads of its next page
-// are in flight while it computes the current one.  V is read with nontemporal
+// Each wave walks its pages with two register buffers (d <= 128): the loads of its
+// next page are in flight while it computes the current one.  V is read with nontemporal
 // loads (whole lines per instruction); K rows are 64-byte pieces of 128-256-byte
 // token rows, so they use plain loads, which L2 merges.
 #include <hip/hip_runtime.h>
@@ -57,7 +57,7 @@ struct PageRegs {
 }  // namespace
 
 template <typename T, int D, int WAVES, bool TRACE, int G>
-__global__ __launch_bounds__(WAVES * 64) void gqa_decode_kernel(const PlainParams p) {
+__global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kernel(const PlainParams p) {
   using Tl = DecodeTile<T, D>;
   using PR = PageRegs<T, D>;
   constexpr bool F32 = sizeof(T) == 4;
@@ -188,15 +188,25 @@ __global__ __launch_bounds__(WAVES * 64) void gqa_decode_kernel(const PlainParam
     }
   };
 
-  // The wave's pages are p0 + w, p0 + w + WAVES, ...; buffer a holds the even ones, b the odd.
-  PR ra, rb;
-  if (p0 + w < p1) load_page(p0 + w, ra);
-  for (int pa = p0 + w; pa < p1; pa += 2 * WAVES) {
-    const int pb = pa + WAVES, pc = pb + WAVES;
-    if (pb < p1) load_page(pb, rb);
-    compute_page(pa, ra);
-    if (pc < p1) load_page(pc, ra);
-    if (pb < p1) compute_page(pb, rb);
+  // The wave's pages are p0 + w, p0 + w + WAVES, ...  Up to d = 128 two register buffers
+  // (a: even pages, b: odd) keep the next page's loads in flight; at d = 256 one page's
+  // operands are 64 VGPRs, and a single buffer keeps two waves per SIMD.
+  if constexpr (D <= 128) {
+    PR ra, rb;
+    if (p0 + w < p1) load_page(p0 + w, ra);
+    for (int pa = p0 + w; pa < p1; pa += 2 * WAVES) {
+      const int pb = pa + WAVES, pc = pb + WAVES;
+      if (pb < p1) load_page(pb, rb);
+      compute_page(pa, ra);
+      if (pc < p1) load_page(pc, ra);
+      if (pb < p1) compute_page(pb, rb);
+    }
+  } else {
+    for (int pa = p0 + w; pa < p1; pa += WAVES) {
+      PR ra;
+      load_page(pa, ra);
+      compute_page(pa, ra);
+    }
   }
   lsum = col_sum(lsum);
 
@@ -282,6 +292,7 @@ hipError_t launch_gqa_decode(const PlainParams& p, int dtype, int head_dim, int 
     if (head_dim == 64) return launch_gqa_t<bf16, 64>(p, waves, trace, s, ev);
     if (head_dim == 96) return launch_gqa_t<bf16, 96>(p, waves, trace, s, ev);
     if (head_dim == 128) return launch_gqa_t<bf16, 128>(p, waves, trace, s, ev);
+    if (head_dim == 256) return launch_gqa_t<bf16, 256>(p, waves, trace, s, ev);
   }
   return hipErrorInvalidValue;
 }

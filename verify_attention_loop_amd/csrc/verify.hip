@@ -288,6 +288,7 @@ hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int wave
     if (head_dim == 64) return launch_verify_t<bf16, 64>(p, waves, trace, s, ev);
     if (head_dim == 96) return launch_verify_t<bf16, 96>(p, waves, trace, s, ev);
     if (head_dim == 128) return launch_verify_t<bf16, 128>(p, waves, trace, s, ev);
+    if (head_dim == 256) return launch_verify_t<bf16, 256>(p, waves, trace, s, ev);
   }
   return hipErrorInvalidValue;
 }

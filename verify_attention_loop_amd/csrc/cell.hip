@@ -302,6 +302,9 @@ __device__ __forceinline__ void nibbles_f32(uint32_t code, float* f) {
 // (x & m) | c in one VALU op.  The compiler splits it in two when both constants are
 // literals (a VOP3 op takes neither literals nor a second scalar here), so the mask
 // comes in a VGPR and the constant in an SGPR.
+// Inline asm is opaque to the compiler's hazard checks: this helper and ubyte_f32 only
+// take operands made by bitwise ops or loads, never by a transcendental op (v_exp and
+// the like), whose result a dependent VALU op on gfx950 may read only after a wait state.
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m_vgpr, uint32_t c_sgpr) {
   uint32_t d;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "v"(m_vgpr), "s"(c_sgpr));
@@ -579,9 +582,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
       float wgt[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        wgt[i] = x[i] * f16_to_f32(vm.w[i] & 0xFFFFu);
-        const float zc = x[i] * f16_to_f32(vm.w[i] >> 16);
-        zacc += (masked && !hot[i]) ? fmaf(1.5f, wgt[i], zc) : zc;
+        // fma with a zero addend (not a product) so that the f16 operand folds into one
+        // v_fma_mix_f32; p sigma >= 0, so the sign of a zero result does not matter
+        wgt[i] = fmaf(x[i], f16_to_f32(vm.w[i] & 0xFFFFu), 0.f);  // p sigma
+        zacc = fmaf(x[i], f16_to_f32(vm.w[i] >> 16), zacc);        // + p z
+        if (masked) zacc = fmaf(1.5f, hot[i] ? 0.f : wgt[i], zacc);  // cold: bucket midpoint
       }
       // V codes: INT4 hot 4 hi + lo, cold 4 hi (the bucket midpoint's 1.5 is in zacc); INT2 the code
 #pragma unroll

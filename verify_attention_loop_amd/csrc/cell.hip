@@ -449,7 +449,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
     __shared__ uint32_t sm_qp[WAVES][3][D / 2];  // per wave: hi, mid, lo bf16 parts of q'
     constexpr uint32_t kOne = 0x3F803F80u;        // bf16 pair (1, 1)
     const uint32_t mask_a = BITS == 4 ? 0x00780078u : 0x00180018u;  // code bits at mantissa bits 3..
-    auto far_keys = [&](int cp, const uint8_t*& hb, float* x2, bool* valid, Raw<16>& vh, Raw<32>& vm) {
+    auto far_keys = [&](int cp, const uint8_t*& hb, float* x2, Raw<16>& vh, Raw<32>& vm) {
       hb = p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes;
       // Issue the page's loads together: K meta of channels 2 lane, 2 lane + 1, K codes,
       // V hi (or INT2 V codes), V meta.
@@ -525,32 +525,33 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ii = 4 * tb + i;
-          valid[ii] = cp * kCodePage + g + 4 * ii < n_far;
-          x2[ii] = valid[ii] ? fmaf(acc[tb][i], c16, cb) : -INFINITY;
-        }
-      // Past the sequence (last page only) the V meta is cleared, so that those tokens'
-      // zero weights meet finite scales whatever the page holds there.
+        for (int i = 0; i < 4; ++i) x2[4 * tb + i] = fmaf(acc[tb][i], c16, cb);
+      // Past the sequence (last page only): score -inf and V meta cleared, so that those
+      // tokens get zero weight against finite scales whatever the page holds there.
       if (cp * kCodePage + kCodePage > n_far) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (!valid[i]) vm.w[i] = 0u;
+          if (cp * kCodePage + g + 4 * i >= n_far) {
+            x2[i] = -INFINITY;
+            vm.w[i] = 0u;
+          }
       }
     };
 
     // Value phase: hot test against thr2 (base-2 units), online softmax, V lo of hot tokens,
     // V dequant folded into the weights, accumulation.
-    auto far_values = [&](int cp, const uint8_t* hb, float* x2, const bool* valid, float thr2, const Raw<16>& vh,
-                          const Raw<32>& vm) {
+    auto far_values = [&](int cp, const uint8_t* hb, float* x2, float thr2, const Raw<16>& vh, const Raw<32>& vm) {
+      // A finite threshold keeps tokens past the sequence (score -inf) cold under any rule,
+      // and leaves every finite score hot when the rule's threshold is -inf.
+      thr2 = fmaxf(thr2, -3.402823466e38f);  // -FLT_MAX
       float x[8];
       bool hot[8];
       uint32_t hotbits = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        hot[i] = valid[i] && (!masked || x2[i] >= thr2);
-        x[i] = x2[i];  // -inf past the sequence
-        if (hot[i]) hotbits |= 1u << (g + 4 * i);
+        hot[i] = masked ? x2[i] >= thr2 : x2[i] > -INFINITY;
+        x[i] = x2[i];
+        if (TRACE && hot[i]) hotbits |= 1u << (g + 4 * i);
       }
       // online softmax of this row (x[] becomes p_j)
       float mn = st.m;
@@ -612,11 +613,10 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
       for (int cp = c0 + w; cp < c1; cp += WAVES) {
         const uint8_t* hb;
         float x2[8];
-        bool valid[8];
         Raw<16> vh;
         Raw<32> vm;
-        far_keys(cp, hb, x2, valid, vh, vm);
-        far_values(cp, hb, x2, valid, thr2, vh, vm);
+        far_keys(cp, hb, x2, vh, vm);
+        far_values(cp, hb, x2, thr2, vh, vm);
       }
     } else {
       // The LoopKV page's rule (App. E Algorithm 1): this far block walks its pages in order
@@ -633,12 +633,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
         const bool active = cp < c1;  // uniform per wave
         const uint8_t* hb = nullptr;
         float x2[8];
-        bool valid[8];
         Raw<16> vh;
         Raw<32> vm;
         float pm = -INFINITY;
         if (active) {
-          far_keys(cp, hb, x2, valid, vh, vm);
+          far_keys(cp, hb, x2, vh, vm);
 #pragma unroll
           for (int i = 0; i < 8; ++i)
             pm = fmaxf(pm, x2[i]);  // -inf past the sequence
@@ -654,7 +653,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
           if (v <= w) m_page = fmaxf(m_page, pv);
           m_run = fmaxf(m_run, pv);
         }
-        if (active) far_values(cp, hb, x2, valid, fmaxf(m_page, m0_2) - p.v_tau, vh, vm);
+        if (active) far_values(cp, hb, x2, fmaxf(m_page, m0_2) - p.v_tau, vh, vm);
       }
     }
   }

@@ -209,6 +209,16 @@ def test_config_validation(lib):
     cfg.max_block = 17
     with pytest.raises(vla.LkvError):
         vla.LoopCache.sizes(cfg)
+    cfg.max_block = 1
+    cfg.head_dim = 256  # bf16 plain planes take head dim 256 (the Dory shape) ...
+    assert vla.LoopCache.sizes(cfg).page_bytes == 2 * 2 * 16 * 256 * 2
+    cfg.kv_dtype = vla.DTYPE_F32  # ... fp32 caches do not
+    with pytest.raises(vla.LkvError):
+        vla.LoopCache.sizes(cfg)
+    cfg.kv_dtype = vla.DTYPE_BF16
+    cfg.quant, cfg.sink, cfg.tail = 1, 4, 8  # nor do quantised cells
+    with pytest.raises(vla.LkvError):
+        vla.LoopCache.sizes(cfg)
 
 
 def test_sink_range(lib):

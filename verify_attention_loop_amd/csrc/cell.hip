@@ -4,33 +4,24 @@
 // head_dim 128).  Per head, INT4 (40 * D bytes = 160 B per token-head: 4-bit K and
 // V codes plus fp16 scale/zero per 32 elements, LoopKV page App. C):
 //   [0,    4D)  K meta   [channel][scale, zero] fp16, per channel over the page
-//   [4D,  20D)  K codes  4-bit, MFMA operand order: [token block][lane][k-step][8 nibbles]
+//   [4D,  20D)  K codes  4-bit, lane-major: [half][g][li][4 tokens][8 nibbles]
 //   [20D, 28D)  V hi     2-bit hi = c >> 2, lane-major: [g][li][8 tokens][16 bits]
 //   [28D, 36D)  V lo     2-bit lo = c & 3, token-major: [token][li][16 bits]
 //   [36D, 40D)  V meta   [g][group][8 tokens][scale, zero] fp16, per token and 32 channels
-// INT2 (24 * D bytes): K meta [0,4D), K codes [4D,12D) in MFMA operand order
-// [lane][token block][k-step pair][16 crumbs], V codes [12D,20D) as V hi, V meta
-// [20D,24D).
+// INT2 (24 * D bytes): K meta [0,4D), K codes [4D,12D) as V hi, V codes [12D,20D)
+// as V hi, V meta [20D,24D).  Lane (g, li) of a DPP row owns channels 8li..8li+7
+// and tokens g, g+4, ..., g+28 of the page, so its K codes, V hi and V meta are
+// contiguous 16-32 B runs; V lo is token-major so that a cold token's 32-byte lo
+// row (one token-head) is never requested at all (LoopKV page, Sec. 3.3).
 //
-// K codes are the A operand of 16x16x32 bf16 MFMAs (scores, see cell_kernel): lane
-// l = 16 g + m holds, for token block tb (tokens 16 tb ..) and k-step s, row m =
-// token kc_token(tb, m) and channels 32 s + 8 g + e, e = 0..7.  An INT4 word holds
-// channel e at nibble (e >> 1) + 4 (e & 1), so channels 2j and 2j + 1 are nibbles j
-// and j + 4 and one shift and one mask turn them into a bf16 pair.  An INT2 word
-// holds the k-steps 2 s2 and 2 s2 + 1 of one token block: channel e of k-step s at
-// crumb 8 (e & 1) + (e >> 1) + 4 (s & 1).  Each load instruction of the kernel reads
-// 1 KB of whole lines.
-//
-// V: lane (g, li) of a DPP row owns channels 8li..8li+7 and tokens g, g+4, ...,
-// g+28 of the page, so its V hi and V meta are contiguous 16-32 B runs; V lo is
-// token-major so that a cold token's 32-byte lo row (one token-head) is never
-// requested at all (LoopKV page, Sec. 3.3).  Bit order inside a lane's 16-bit word
-// of 2-bit values (its 8 channels c): hi crumbs sit at crumb 2c + 1 (c < 4) or
-// 2(c - 4) (c >= 4), lo and INT2 V crumbs at crumb 2c (c < 4) or 2(c - 4) + 1
-// (c >= 4).  Then x | x << 18 puts hi_c at bits 2-3 of nibble c and y | y << 14 puts
-// lo_c at bits 0-1 of nibble c, so one bitfield insert yields the eight 4-bit codes
-// 4 hi + lo of a hot token, and byte conversions turn nibbles into floats: about 3
-// VALU instructions per code instead of 6 for separate hi and lo planes.
+// Bit order inside a lane's 16-bit word of 2-bit values (its 8 channels c):
+// hi crumbs sit at crumb 2c + 1 (c < 4) or 2(c - 4) (c >= 4), lo and INT2 crumbs
+// at crumb 2c (c < 4) or 2(c - 4) + 1 (c >= 4).  Then x | x << 18 puts hi_c at
+// bits 2-3 of nibble c and y | y << 14 puts lo_c at bits 0-1 of nibble c, so one
+// bitfield insert yields the eight 4-bit codes 4 hi + lo of a hot token, and
+// byte conversions turn nibbles into floats: about 3 VALU instructions per code
+// instead of 6 for separate hi and lo planes.  K codes are plain nibbles (nibble c
+// = channel c).
 #include <hip/hip_runtime.h>
 
 #include "attn_common.hpp"
@@ -48,22 +39,6 @@ uint64_t code_page_bytes(int hkv, int head_dim, int bits) {
 __host__ __device__ __forceinline__ int hi_crumb(int c) { return c < 4 ? 2 * c + 1 : 2 * (c - 4); }
 __host__ __device__ __forceinline__ int lo_crumb(int c) { return c < 4 ? 2 * c : 2 * (c - 4) + 1; }
 
-// K code operand order: token of MFMA row m in token block tb, and the row of token t
-// (its block is t >> 4).  Row 4 g + i of block tb is token g + 4 (4 tb + i), so the
-// score rows a lane receives are the tokens g + 4 i' (i' = 4 tb + i) whose V it holds.
-__host__ __device__ __forceinline__ int kc_token(int tb, int m) { return (m >> 2) + 16 * tb + 4 * (m & 3); }
-__host__ __device__ __forceinline__ int kc_row(int t) { return 4 * (t & 3) + ((t & 15) >> 2); }
-
-// Byte offset (inside a head slice) of the 32-bit K code word that holds channels
-// 8 cg .. 8 cg + 7 of token t, and the bit of channel e (0..7) of that group in it.
-__host__ __device__ __forceinline__ int kc_word(int bits, int t, int cg) {
-  const int tb = t >> 4, lane = 16 * (cg & 3) + kc_row(t), s = cg >> 2;
-  return bits == 4 ? 4 * 128 + tb * 1024 + lane * 16 + s * 4 : 4 * 128 + lane * 16 + (tb * 2 + (s >> 1)) * 4;
-}
-__host__ __device__ __forceinline__ int kc_bit(int bits, int cg, int e) {
-  return bits == 4 ? 4 * ((e >> 1) + 4 * (e & 1)) : 2 * (8 * (e & 1) + (e >> 1) + 4 * ((cg >> 2) & 1));
-}
-
 // Byte offsets inside one head's slice of a code page (d = 128).
 __host__ __device__ constexpr uint64_t code_head_bytes(int bits) { return (uint64_t)(bits == 4 ? 40 : 24) * 128; }
 __host__ __device__ constexpr uint64_t vcode_offset(int bits) { return (bits == 4 ? 20 : 12) * 128; }
@@ -76,27 +51,24 @@ __device__ __forceinline__ void pack_item(uint8_t* hb, int bits, int tok, int li
                                           const uint8_t* vin, const uint16_t* vm_src, const uint16_t* km_src) {
   constexpr int D = 128;
   const int g = tok & 3, i = tok >> 2;
-  uint8_t* kword = hb + kc_word(bits, tok, li);
   if (bits == 4) {
     uint32_t kw = 0, vhi = 0, vlo = 0;
     for (int c = 0; c < 8; ++c) {
-      kw |= (uint32_t)(kin[c] & 15u) << kc_bit(4, li, c);
+      kw |= (uint32_t)(kin[c] & 15u) << (4 * c);
       vhi |= (uint32_t)((vin[c] >> 2) & 3u) << (2 * hi_crumb(c));
       vlo |= (uint32_t)(vin[c] & 3u) << (2 * lo_crumb(c));
     }
-    *reinterpret_cast<uint32_t*>(kword) = kw;
+    const int hh = i >> 2, ii = i & 3;
+    *reinterpret_cast<uint32_t*>(hb + 4 * D + hh * 1024 + (g * 16 + li) * 16 + ii * 4) = kw;
     *reinterpret_cast<uint16_t*>(hb + 20 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)vhi;
     *reinterpret_cast<uint16_t*>(hb + 28 * D + tok * 32 + li * 2) = (uint16_t)vlo;
   } else {
-    // the group's 8 crumbs fill one byte in each 16-bit half of the word
     uint32_t kw = 0, vw = 0;
     for (int c = 0; c < 8; ++c) {
-      kw |= (uint32_t)(kin[c] & 3u) << kc_bit(2, li, c);
+      kw |= (uint32_t)(kin[c] & 3u) << (2 * lo_crumb(c));
       vw |= (uint32_t)(vin[c] & 3u) << (2 * lo_crumb(c));
     }
-    const int sh = 8 * ((li >> 2) & 1);
-    kword[sh / 8] = (uint8_t)(kw >> sh);
-    kword[2 + sh / 8] = (uint8_t)(kw >> (16 + sh));
+    *reinterpret_cast<uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)kw;
     *reinterpret_cast<uint16_t*>(hb + 12 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)vw;
   }
   if (li < 4) {
@@ -116,18 +88,20 @@ __device__ __forceinline__ void unpack_item(const uint8_t* hb, int bits, int tok
                                             uint8_t* vout, uint16_t* vm_dst, uint16_t* km_dst) {
   constexpr int D = 128;
   const int g = tok & 3, i = tok >> 2;
-  const uint32_t kw = *reinterpret_cast<const uint32_t*>(hb + kc_word(bits, tok, li));
   if (bits == 4) {
+    const int hh = i >> 2, ii = i & 3;
+    const uint32_t kw = *reinterpret_cast<const uint32_t*>(hb + 4 * D + hh * 1024 + (g * 16 + li) * 16 + ii * 4);
     const uint32_t vhi = *reinterpret_cast<const uint16_t*>(hb + 20 * D + (g * 16 + li) * 16 + i * 2);
     const uint32_t vlo = *reinterpret_cast<const uint16_t*>(hb + 28 * D + tok * 32 + li * 2);
     for (int c = 0; c < 8; ++c) {
-      kout[c] = (uint8_t)((kw >> kc_bit(4, li, c)) & 15u);
+      kout[c] = (uint8_t)((kw >> (4 * c)) & 15u);
       vout[c] = (uint8_t)((((vhi >> (2 * hi_crumb(c))) & 3u) << 2) | ((vlo >> (2 * lo_crumb(c))) & 3u));
     }
   } else {
+    const uint32_t kw = *reinterpret_cast<const uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + i * 2);
     const uint32_t vw = *reinterpret_cast<const uint16_t*>(hb + 12 * D + (g * 16 + li) * 16 + i * 2);
     for (int c = 0; c < 8; ++c) {
-      kout[c] = (uint8_t)((kw >> kc_bit(2, li, c)) & 3u);
+      kout[c] = (uint8_t)((kw >> (2 * lo_crumb(c))) & 3u);
       vout[c] = (uint8_t)((vw >> (2 * lo_crumb(c))) & 3u);
     }
   }
@@ -299,18 +273,9 @@ __device__ __forceinline__ void nibbles_f32(uint32_t code, float* f) {
   f[7] = ubyte_f32<3>(od);
 }
 
-// (x & m) | c in one VALU op.  The compiler splits it in two when both constants are
-// literals (a VOP3 op takes neither literals nor a second scalar here), so the mask
-// comes in a VGPR and the constant in an SGPR.
-// Inline asm is opaque to the compiler's hazard checks: this helper and ubyte_f32 only
-// take operands made by bitwise ops or loads, never by a transcendental op (v_exp and
-// the like), whose result a dependent VALU op on gfx950 may read only after a wait state.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m_vgpr, uint32_t c_sgpr) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "v"(m_vgpr), "s"(c_sgpr));
-  return d;
-}
-
+// Inline asm is opaque to the compiler's hazard checks: ubyte_f32 only takes operands
+// made by bitwise ops, never by a transcendental op (v_exp and the like), whose result
+// a dependent VALU op on gfx950 may read only after a wait state.
 __device__ __forceinline__ uint32_t or4(uint32_t v) {
   v |= (uint32_t)__shfl_xor((int)v, 16);
   v |= (uint32_t)__shfl_xor((int)v, 32);
@@ -323,8 +288,7 @@ __device__ __forceinline__ uint32_t or4(uint32_t v) {
 //     stay the cell's own and exact);
 //   far block c: its share of the code pages of the cell's source (own codes, or
 //     the final loop's for a shared cell).  Per page the K scale is folded into q
-//     and q.z into a bias (LoopKV page, App. E), so a score is bias + sum q'_c c_jc;
-//     the sums run on MFMA (the key phase below), the rest on the VALU.
+//     and q.z into a bias (LoopKV page, App. E), so a score is bias + sum q'_c c_jc.
 //     The seed m0 is the largest sink score, recomputed by every far block from
 //     the sink keys (no wait on another block).  Hot test of a far token: the fixed
 //     rule s_j >= m0 - offset, or the page's own rule s_j >= max(m, m0) - tau ln 2
@@ -335,10 +299,10 @@ __device__ __forceinline__ uint32_t or4(uint32_t v) {
 // Each DPP row keeps its own online softmax; partials go to the workspace and
 // the LSE merge kernel combines them.
 template <int WAVES, bool TRACE, int BITS, bool RUNNING>
-// The kernel is VALU-bound; five waves per SIMD fit the fixed rule in 96 VGPRs without spills
+// The kernel is VALU-bound; six waves per SIMD fit the fixed rule in 80 VGPRs without spills
 // (the running rule keeps a page's scores across a barrier and takes four; the traced
 // variants, for tests, are left unconstrained).
-__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cell_kernel(const CellParams p) {
+__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 6)) void cell_kernel(const CellParams p) {
   constexpr int D = 128, E = 8;
   constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -350,20 +314,18 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
   const int n_far = L - p.sink - p.tail;
   const int tail_lo = L - p.tail;
 
-  // q: channels 8 li .. 8 li + 7 as bf16 pairs (near block, sink seed), and channels
-  // 2 lane, 2 lane + 1 as floats (far block: folded with the K meta of those channels).
+  // q: this lane's channels 8 li .. 8 li + 7, as bf16 pairs (dot2) and as floats
+  float qf[E];
   uint32_t qw[E / 2];
-  float q2[2];
   {
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(p.q) + ((int64_t)b * p.hq + h) * D * 2;
     Raw<16> r;
-    load_raw<16>(r, qrow + li * E * 2);
+    load_raw<16>(r, reinterpret_cast<const uint8_t*>(p.q) + (((int64_t)b * p.hq + h) * D + li * E) * 2);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) qw[x] = r.w[x];
-    Raw<4> r2;
-    load_raw<4>(r2, qrow + lane * 4);
-    q2[0] = bf_lo(r2.w[0]);
-    q2[1] = bf_hi(r2.w[0]);
+    for (int x = 0; x < 4; ++x) {
+      qw[x] = r.w[x];
+      qf[2 * x] = bf_lo(r.w[x]);
+      qf[2 * x + 1] = bf_hi(r.w[x]);
+    }
   }
   const int32_t* tab_near = p.tab_near + (int64_t)slot * p.ring_near;
   const uint64_t koff = (uint64_t)hk * HEADB + (uint64_t)li * 16;
@@ -436,96 +398,42 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 4 : 5)) void cel
     constexpr uint64_t vcode_off = BITS == 4 ? 20 * D : 12 * D;
     constexpr uint64_t vmeta_off = BITS == 4 ? 36 * D : 20 * D;
 
-    // Key phase of code page cp: loads, scores of tokens g + 4i in base-2 units (x2; -inf
-    // past the sequence), validity; the V codes and V meta are loaded here too.
-    // Scores on MFMA (LoopKV page, App. E: the K scale folds into the query, the zero
-    // into a per-page bias): s_j = sum_c q_c z_c + sum_c q'_c c_jc with q' = q sigma,
-    // exact in fp32 (bf16 x fp16) and split exactly into three bf16 parts that go
-    // through LDS into the B operand, replicated over all 16 columns.  A code c enters
-    // the A operand as the bf16 1 + c / 16 (exact), so the MFMA sums give
-    // C_j = sum_c q'_c (1 + c_jc / 16) and s_j = 16 C_j + sum_c (q_c z_c - 16 q'_c).
-    // Every column of C holds the scores, so lane (g, n) has rows 4 g + i of each token
-    // block: the tokens g + 4 (4 tb + i) whose values it reads.
-    __shared__ uint32_t sm_qp[WAVES][3][D / 2];  // per wave: hi, mid, lo bf16 parts of q'
-    constexpr uint32_t kOne = 0x3F803F80u;        // bf16 pair (1, 1)
-    const uint32_t mask_a = BITS == 4 ? 0x00780078u : 0x00180018u;  // code bits at mantissa bits 3..
+    // Key phase of code page cp: loads, K dequant folded into q (LoopKV page, App. E: the
+    // per-channel scale multiplies the query, the zero becomes a bias), scores of tokens
+    // g + 4i in base-2 units (x2; -inf past the sequence); the V codes and V meta are
+    // loaded here too.  A score is bias + sum_c q'_c c_jc over the lane's 8 channels,
+    // then a 16-lane DPP sum.
     auto far_keys = [&](int cp, const uint8_t*& hb, float* x2, Raw<16>& vh, Raw<32>& vm) {
       hb = p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes;
-      // Issue the page's loads together: K meta of channels 2 lane, 2 lane + 1, K codes,
-      // V hi (or INT2 V codes), V meta.
-      Raw<8> km;
-      load_raw<8>(km, hb + lane * 8);
-      Raw<16> kc[BITS == 4 ? 2 : 1];
-      load_stream<16>(kc[0], hb + 4 * D + lane * 16);
-      if constexpr (BITS == 4) load_stream<16>(kc[1], hb + 4 * D + 1024 + lane * 16);
+      // Issue the page's loads together: K meta of the lane's 8 channels, K codes, V hi
+      // (or INT2 V codes), V meta.
+      Raw<32> km;
+      load_raw<32>(km, hb + li * 32);
+      Raw<16> k0, k1;
+      load_stream<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
+      if constexpr (BITS == 4) load_stream<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
       load_stream<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
       load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
-      // q' of the lane's two channels, its exact bf16 parts, and the lane's share of the bias
-      float qp[2], bl = 0.f;
-      uint32_t part[3][2];
+      // q' = q sigma and bias = q . z; fma with a zero addend so the fp16 operand folds into
+      // v_fma_mix_f32 (q sigma is exact in fp32: bf16 x fp16)
+      float qs[E], bias = 0.f;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        qp[x] = q2[x] * f16_to_f32(km.w[x] & 0xFFFFu);
-        bl = fmaf(q2[x], f16_to_f32(km.w[x] >> 16), bl);
-        const uint32_t hi = __float_as_uint(qp[x]) & 0xFFFF0000u;
-        const float r = qp[x] - __uint_as_float(hi);
-        const uint32_t mid = __float_as_uint(r) & 0xFFFF0000u;
-        const uint32_t lo = __float_as_uint(r - __uint_as_float(mid));  // at most 3 significant bits
-        part[0][x] = hi;
-        part[1][x] = mid;
-        part[2][x] = lo;
+      for (int c = 0; c < E; ++c) {
+        qs[c] = fmaf(qf[c], f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
+        bias = fmaf(qf[c], f16_to_f32(km.w[c] >> 16), bias);
       }
-      bl = fmaf(-16.f, qp[0] + qp[1], bl);
-      __builtin_amdgcn_wave_barrier();  // the previous page's operand reads are issued
 #pragma unroll
-      for (int k = 0; k < 3; ++k) sm_qp[w][k][lane] = (part[k][0] >> 16) | (part[k][1] & 0xFFFF0000u);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float bias = row_sum16(bl);
-      bias += __shfl_xor(bias, 16);
-      bias += __shfl_xor(bias, 32);
-      f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      for (int i = 0; i < 8; ++i) {
+        uint32_t code;
+        if constexpr (BITS == 4) code = i < 4 ? k0.w[i] : k1.w[i - 4];
+        else code = lo_nibbles((k0.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        float f[E];
+        nibbles_f32(code, f);
+        float sc = bias;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        // B: parts of q' for channels 32 ks + 8 g .. + 7 (the same for every column n)
-        uint32_t bq[3][4];
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          const uint4 v = *reinterpret_cast<const uint4*>(&sm_qp[w][k][16 * ks + 4 * g]);
-          bq[k][0] = v.x;
-          bq[k][1] = v.y;
-          bq[k][2] = v.z;
-          bq[k][3] = v.w;
-        }
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          // A: codes of row m = n, channels 32 ks + 8 g + e, as bf16 1 + c / 16
-          uint32_t a[4];
-          if constexpr (BITS == 4) {
-            const uint32_t wd = kc[tb].w[ks];
-            a[0] = and_or(wd << 3, mask_a, kOne);
-            a[1] = and_or(wd >> 1, mask_a, kOne);
-            a[2] = and_or(wd >> 5, mask_a, kOne);
-            a[3] = and_or(wd >> 9, mask_a, kOne);
-          } else {
-            const uint32_t wd = kc[0].w[tb * 2 + (ks >> 1)] >> (8 * (ks & 1));
-            a[0] = and_or(wd << 3, mask_a, kOne);
-            a[1] = and_or(wd << 1, mask_a, kOne);
-            a[2] = and_or(wd >> 1, mask_a, kOne);
-            a[3] = and_or(wd >> 3, mask_a, kOne);
-          }
-#pragma unroll
-          for (int k = 0; k < 3; ++k)
-            acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                              __builtin_bit_cast(bf16x8_t, bq[k]), acc[tb], 0, 0, 0);
-        }
+        for (int c = 0; c < E; ++c) sc = fmaf(qs[c], f[c], sc);
+        x2[i] = row_sum16(sc) * p.scale_log2;
       }
-      const float c16 = 16.f * p.scale_log2, cb = bias * p.scale_log2;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x2[4 * tb + i] = fmaf(acc[tb][i], c16, cb);
       // Past the sequence (last page only): score -inf and V meta cleared, so that those
       // tokens get zero weight against finite scales whatever the page holds there.
       if (cp * kCodePage + kCodePage > n_far) {

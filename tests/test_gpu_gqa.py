@@ -67,13 +67,16 @@ def test_gqa_decode_every_row(G, D, dt, tol, policy, W, kernel, monkeypatch):
     built.cache.close()
 
 
-@pytest.mark.parametrize("G,k,D", [(2, 8, 64), (4, 8, 64), (4, 4, 64), (8, 2, 64), (8, 1, 64), (2, 5, 64),
+@pytest.mark.parametrize("G,k,D", [(2, 8, 64), (4, 4, 64), (8, 2, 64), (8, 1, 64), (2, 5, 64),
+                                   (4, 8, 64), (8, 4, 64), (4, 5, 96), (2, 16, 128), (8, 3, 128),
                                    (4, 4, 256), (4, 8, 256)])
 def test_gqa_verify_every_row(G, k, D):
     """Verify tiles on a GQA cache (each query head reads its group's KV head): k G <= 16 puts the block's rows
-    of all G heads in one tile, k G > 16 (4 x 8) takes one head per tile; RIPE window 20 >= k - 1."""
+    of all G heads in one tile; 16 < k G <= 32 takes two tiles sharing the page's K/V registers (head dim <= 128);
+    larger blocks, and k G > 16 at head dim 256, take one query head per tile.  RIPE window 20 >= k - 1."""
     w = _wl(D, G, q_len=k)
     lengths = [k, 40, 300]
+    assert k <= 16
     built = harness.build_plain(w, lengths=lengths, policy=vla.POLICY_RIPE, window=20, q_len=k, shuffle=True,
                                 poison=True)
     rows = [(b, i, h) for b in range(3) for i in range(k) for h in range(w.n_heads)]

@@ -27,7 +27,7 @@ hipError_t launch_decode(const PlainParams& p, int dtype, int head_dim, int wave
                          const LaunchEvents& ev);
 hipError_t launch_verify(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s,
                          const LaunchEvents& ev);
-int verify_heads_per_wg(int hq, int hkv, int q_len);
+int verify_heads_per_wg(int hq, int hkv, int q_len, int head_dim);
 hipError_t launch_gqa_decode(const PlainParams& p, int dtype, int head_dim, int waves, bool trace, hipStream_t s,
                              const LaunchEvents& ev);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, hipStream_t s);
@@ -732,13 +732,14 @@ LaunchEvents launch_events(const lkv_attend_args* a, bool first, bool last) {
 
 // Splits of a plain-cache call: enough workgroups to fill the chip.  Decode and draft
 // workgroups serve all query heads of one KV head; verify workgroups the query heads of
-// one KV head when the block fits the tile's 16 columns, else one query head.
+// one KV head when the block's rows fit one or two 16-column tiles, else one query head.
 // Grouped-query decode aims at two workgroups per CU rather than eight: its kernel time
 // hardly depends on the split count (measured on MI355X), and a call without splits
 // skips the merge kernel.
 int auto_splits(const lkv_cache* c, int n_seqs, int mode, int q_len, int max_pages) {
   const int hq = c->cfg.n_heads_q, hkv = c->cfg.n_heads_kv;
-  const int rows = n_seqs * (mode == LKV_MODE_VERIFY ? hq / verify_heads_per_wg(hq, hkv, std::max(1, q_len)) : hkv);
+  const int rows =
+      n_seqs * (mode == LKV_MODE_VERIFY ? hq / verify_heads_per_wg(hq, hkv, std::max(1, q_len), c->cfg.head_dim) : hkv);
   const bool gqa = mode == LKV_MODE_DECODE && hq > hkv;
   const int target = gqa ? env_int("LKV_GQA_TARGET_WGS", 512) : env_int("LKV_TARGET_WGS", 2048);
   int s = (target + rows - 1) / rows;

@@ -19,10 +19,9 @@
 // rows, so they use plain loads, which L2 merges.
 //
 // Grouped-query attention: with G > 1 a workgroup serves the G query heads of one
-// KV head and column n is (block row n / G, head n % G), so every K/V page is read
-// once for all G heads and the softmax work per page does not grow with G.  The
-// q = 1 decode of a grouped cache runs here too (k = 1, G columns): its scores and
-// weighted sums are the same contractions with G columns instead of one.
+// KV head and column c is (block row c / G, head c % G), so every K/V page is read
+// once for all G heads.  Blocks of up to 32 such columns (head dim <= 128) take two
+// tiles that share the page's K and V registers.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -43,7 +42,7 @@ __device__ __forceinline__ float xsum4(float v) {
   return v;
 }
 
-template <typename T, int D, int WAVES, bool TRACE, int G>
+template <typename T, int D, int WAVES, bool TRACE, int G, int NCT>
 __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p) {
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int ES = F32 ? 4 : 2;
@@ -53,28 +52,33 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
   // f32:  D/16 K loads of 4 channels (4 MFMAs each); D/16 V loads of one channel x 4 tokens.
   constexpr int NB = F32 ? D / 16 : D / 32;
   constexpr int NACC = F32 ? D / 16 : D / 16;  // 16-channel output blocks
+  constexpr int NCOL = 16 * NCT;               // columns of the workgroup's tiles
 
-  // blockIdx.y: the query head (G = 1) or the KV head whose G query heads share the tile.
+  // blockIdx.y: the query head (G = 1) or the KV head whose G query heads share the tiles.
+  // Column c = 16 t + n (tile t, lane column n) is block row c / G of query head c % G.
   const int split = blockIdx.x, b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int g = lane >> 4, n = lane & 15;
   const int hk = G == 1 ? blockIdx.y / (p.hq / p.hkv) : blockIdx.y;
-  const int qi = n / G;                 // block row of column n
-  const int h = blockIdx.y * G + n % G;  // query head of column n
   const int slot = p.slot[b];
   const int L = p.len[b];
   const int k = p.q_len;
   const int t0 = L - k;
-  const bool qv = qi < k;
-  const int tq = t0 + qi;
-  const int own_n = p.ripe ? max(0, min(t0, tq - p.window)) : 0;
   const int own_min = p.ripe ? max(0, min(t0, t0 - p.window)) : 0;
   const int own_max = p.ripe ? max(0, min(t0, t0 + k - 1 - p.window)) : 0;
 
-  // Q^T operand (query n), zero for padding columns.
-  uint32_t qb[NB][4];
-  {
-    const int64_t qrow = (((int64_t)b * k + (qv ? qi : 0)) * p.hq + h) * D;
+  int qi[NCT], h[NCT], tq[NCT], own_n[NCT];
+  bool qv[NCT];
+  uint32_t qb[NCT][NB][4];  // Q^T operands, zero for padding columns
+#pragma unroll
+  for (int t = 0; t < NCT; ++t) {
+    const int col = 16 * t + n;
+    qi[t] = col / G;
+    h[t] = blockIdx.y * G + col % G;
+    qv[t] = qi[t] < k;
+    tq[t] = t0 + qi[t];
+    own_n[t] = p.ripe ? max(0, min(t0, tq[t] - p.window)) : 0;
+    const int64_t qrow = (((int64_t)b * k + (qv[t] ? qi[t] : 0)) * p.hq + h[t]) * D;
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) + qrow * ES;
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -82,14 +86,19 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
       if constexpr (F32) load_raw<16>(r, qp + (16 * s + 4 * g) * 4);
       else load_raw<16>(r, qp + (32 * s + 8 * g) * 2);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) qb[s][x] = qv ? r.w[x] : 0u;
+      for (int x = 0; x < 4; ++x) qb[t][s][x] = qv[t] ? r.w[x] : 0u;
     }
   }
 
-  f32x4_t acc[NACC];
+  f32x4_t acc[NCT][NACC];
+  float m[NCT], lsum[NCT];
 #pragma unroll
-  for (int a = 0; a < NACC; ++a) acc[a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  for (int t = 0; t < NCT; ++t) {
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) acc[t][a] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m[t] = -INFINITY;
+    lsum[t] = 0.f;
+  }
 
   const int n_pages = (L + kPage - 1) / kPage;
   const int p0 = (int)((int64_t)split * n_pages / p.n_splits);
@@ -121,100 +130,110 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
       for (int s = 0; s < NB; ++s) load_raw<16>(kr[s], base + koff + s * KSTEP);
 #pragma unroll
       for (int s = 0; s < NB; ++s) load_stream<16>(vr[s], base + voff + s * VSTEP);
-
-      // ---- S^T = K Q^T
-      f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < NB; ++s) {
-        if constexpr (F32) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kr[s].w[e]), __uint_as_float(qb[s][e]), sc,
-                                                      0, 0, 0);
-        } else {
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[s].w),
-                                                       __builtin_bit_cast(bf16x8_t, qb[s]), sc, 0, 0, 0);
-        }
-      }
-
-      // ---- mask, online softmax for query n (S^T element i is token 4i + g)
-      float x[4];
+      // V of tokens this pass does not own is cleared (unused or poisoned slots may hold
+      // NaN, and 0 * NaN is NaN); the same for every column
       bool keep[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = pos + 4 * i + g;
-        const bool plane_ok = own ? (j >= own_n) : (j < own_n);
-        const bool vis = qv && j <= tq && plane_ok;
-        x[i] = vis ? sc[i] * p.scale_log2 : -INFINITY;
         keep[i] = j < L && (own ? j >= own_min : j < own_max);
-        if constexpr (TRACE) {
-          if (h == 0 && vis && j < p.trace_len) {  // column of head 0 only
-            int32_t* tr = p.trace + (((int64_t)b * k + qi) * p.trace_len + j) * 2;
-            tr[0] = own ? p.loop : p.deepest;
-            tr[1] = phys * kPage + (j % kPage);
-          }
-        }
       }
-      float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mx = xmax4(mx);
-      const float mn = fmaxf(m, mx);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(m - mu);
-      m = mn;
-      float pe[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pe[i] = fast_exp2(x[i] - mu);
-#pragma unroll
-      for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
 
-      // ---- O^T += V^T P^T; V of tokens this pass does not own is cleared (unused or
-      // poisoned slots may hold NaN, and 0 * NaN is NaN)
-      if constexpr (F32) {
-        lsum = fmaf(lsum, alpha, (pe[0] + pe[1]) + (pe[2] + pe[3]));
 #pragma unroll
-        for (int s = 0; s < NB; ++s)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = __uint_as_float(keep[e] ? vr[s].w[e] : 0u);
-            acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pe[e], acc[s], 0, 0, 0);
-          }
-      } else {
-        // P in bf16 for the MFMA; the row sum uses the same rounded weights.
-        const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
-        lsum = fmaf(lsum, alpha, (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23)));
-        const uint32_t pw[2] = {p01, p23};
-        const uint32_t k01 = (keep[0] ? 0x0000FFFFu : 0u) | (keep[1] ? 0xFFFF0000u : 0u);
-        const uint32_t k23 = (keep[2] ? 0x0000FFFFu : 0u) | (keep[3] ? 0xFFFF0000u : 0u);
+      for (int t = 0; t < NCT; ++t) {
+        // ---- S^T = K Q^T
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
-          const uint32_t a0[2] = {vr[s].w[0] & k01, vr[s].w[1] & k23};
-          const uint32_t a1[2] = {vr[s].w[2] & k01, vr[s].w[3] & k23};
-          acc[2 * s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, a0),
-                                                                 __builtin_bit_cast(bf16x4_t, pw), acc[2 * s], 0, 0, 0);
-          acc[2 * s + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(bf16x4_t, a1), __builtin_bit_cast(bf16x4_t, pw), acc[2 * s + 1], 0, 0, 0);
+          if constexpr (F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kr[s].w[e]), __uint_as_float(qb[t][s][e]),
+                                                        sc, 0, 0, 0);
+          } else {
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[s].w),
+                                                         __builtin_bit_cast(bf16x8_t, qb[t][s]), sc, 0, 0, 0);
+          }
+        }
+
+        // ---- mask, online softmax for the lane's column (S^T element i is token 4i + g)
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = pos + 4 * i + g;
+          const bool plane_ok = own ? (j >= own_n[t]) : (j < own_n[t]);
+          const bool vis = qv[t] && j <= tq[t] && plane_ok;
+          x[i] = vis ? sc[i] * p.scale_log2 : -INFINITY;
+          if constexpr (TRACE) {
+            if (h[t] == 0 && vis && j < p.trace_len) {  // columns of head 0 only
+              int32_t* tr = p.trace + (((int64_t)b * k + qi[t]) * p.trace_len + j) * 2;
+              tr[0] = own ? p.loop : p.deepest;
+              tr[1] = phys * kPage + (j % kPage);
+            }
+          }
+        }
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = xmax4(mx);
+        const float mn = fmaxf(m[t], mx);
+        const float mu = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = fast_exp2(m[t] - mu);
+        m[t] = mn;
+        float pe[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pe[i] = fast_exp2(x[i] - mu);
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[t][a] *= alpha;
+
+        // ---- O^T += V^T P^T
+        if constexpr (F32) {
+          lsum[t] = fmaf(lsum[t], alpha, (pe[0] + pe[1]) + (pe[2] + pe[3]));
+#pragma unroll
+          for (int s = 0; s < NB; ++s)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float v = __uint_as_float(keep[e] ? vr[s].w[e] : 0u);
+              acc[t][s] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, pe[e], acc[t][s], 0, 0, 0);
+            }
+        } else {
+          // P in bf16 for the MFMA; the row sum uses the same rounded weights.
+          const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
+          lsum[t] = fmaf(lsum[t], alpha, (bf_lo(p01) + bf_hi(p01)) + (bf_lo(p23) + bf_hi(p23)));
+          const uint32_t pw[2] = {p01, p23};
+          const uint32_t k01 = (keep[0] ? 0x0000FFFFu : 0u) | (keep[1] ? 0xFFFF0000u : 0u);
+          const uint32_t k23 = (keep[2] ? 0x0000FFFFu : 0u) | (keep[3] ? 0xFFFF0000u : 0u);
+#pragma unroll
+          for (int s = 0; s < NB; ++s) {
+            const uint32_t a0[2] = {vr[s].w[0] & k01, vr[s].w[1] & k23};
+            const uint32_t a1[2] = {vr[s].w[2] & k01, vr[s].w[3] & k23};
+            acc[t][2 * s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(bf16x4_t, a0), __builtin_bit_cast(bf16x4_t, pw), acc[t][2 * s], 0, 0, 0);
+            acc[t][2 * s + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(bf16x4_t, a1), __builtin_bit_cast(bf16x4_t, pw), acc[t][2 * s + 1], 0, 0, 0);
+          }
         }
       }
     }
   }
 
-  lsum = xsum4(lsum);
-
   // ---- merge the waves of this workgroup through LDS
-  __shared__ float sm_o[WAVES][kMaxBlock][D + 1];
-  __shared__ float sm_m[WAVES][kMaxBlock], sm_l[WAVES][kMaxBlock];
+  __shared__ float sm_o[WAVES][NCOL][D + 1];
+  __shared__ float sm_m[WAVES][NCOL], sm_l[WAVES][NCOL];
 #pragma unroll
-  for (int a = 0; a < NACC; ++a)
+  for (int t = 0; t < NCT; ++t) {
+    const float ls = xsum4(lsum[t]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int ch;
-      if constexpr (F32) ch = 16 * a + 4 * g + i;
-      else ch = 32 * (a >> 1) + 2 * (4 * g + i) + (a & 1);
-      sm_o[w][n][ch] = acc[a][i];
+    for (int a = 0; a < NACC; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int ch;
+        if constexpr (F32) ch = 16 * a + 4 * g + i;
+        else ch = 32 * (a >> 1) + 2 * (4 * g + i) + (a & 1);
+        sm_o[w][16 * t + n][ch] = acc[t][a][i];
+      }
+    if (g == 0) {
+      sm_m[w][16 * t + n] = m[t];
+      sm_l[w][16 * t + n] = ls;
     }
-  if (g == 0) {
-    sm_m[w][n] = m;
-    sm_l[w][n] = lsum;
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < k * G * D; idx += WAVES * 64) {
@@ -243,35 +262,48 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
   }
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int NCT>
 static void launch_verify_g(const PlainParams& p, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
   dim3 grid(p.n_splits, p.hq / G, p.n_rows);
   if (waves == 1) {
-    if (trace) launch_k((verify_kernel<T, D, 1, true, G>), grid, dim3(64), s, ev, p);
-    else launch_k((verify_kernel<T, D, 1, false, G>), grid, dim3(64), s, ev, p);
+    if (trace) launch_k((verify_kernel<T, D, 1, true, G, NCT>), grid, dim3(64), s, ev, p);
+    else launch_k((verify_kernel<T, D, 1, false, G, NCT>), grid, dim3(64), s, ev, p);
   } else if (waves == 2) {
-    if (trace) launch_k((verify_kernel<T, D, 2, true, G>), grid, dim3(128), s, ev, p);
-    else launch_k((verify_kernel<T, D, 2, false, G>), grid, dim3(128), s, ev, p);
+    if (trace) launch_k((verify_kernel<T, D, 2, true, G, NCT>), grid, dim3(128), s, ev, p);
+    else launch_k((verify_kernel<T, D, 2, false, G, NCT>), grid, dim3(128), s, ev, p);
   } else {
-    if (trace) launch_k((verify_kernel<T, D, 4, true, G>), grid, dim3(256), s, ev, p);
-    else launch_k((verify_kernel<T, D, 4, false, G>), grid, dim3(256), s, ev, p);
+    if (trace) launch_k((verify_kernel<T, D, 4, true, G, NCT>), grid, dim3(256), s, ev, p);
+    else launch_k((verify_kernel<T, D, 4, false, G, NCT>), grid, dim3(256), s, ev, p);
   }
 }
 
 // Query heads per workgroup: the whole group of a KV head when its block rows fit the
-// 16 columns of the tile, else one.
-int verify_heads_per_wg(int hq, int hkv, int q_len) {
+// 16 columns of one tile, or (head dim <= 128) two tiles; else one query head.
+int verify_heads_per_wg(int hq, int hkv, int q_len, int head_dim) {
   const int group = hq / hkv;
-  return (group == 2 || group == 4 || group == 8) && q_len * group <= kMaxBlock ? group : 1;
+  if (group != 2 && group != 4 && group != 8) return 1;
+  return q_len * group <= kMaxBlock || (head_dim <= 128 && q_len * group <= 2 * kMaxBlock) ? group : 1;
 }
 
 template <typename T, int D>
 static hipError_t launch_verify_t(const PlainParams& p, int waves, bool trace, hipStream_t s, const LaunchEvents& ev) {
-  switch (verify_heads_per_wg(p.hq, p.hkv, p.q_len)) {
-    case 2: launch_verify_g<T, D, 2>(p, waves, trace, s, ev); break;
-    case 4: launch_verify_g<T, D, 4>(p, waves, trace, s, ev); break;
-    case 8: launch_verify_g<T, D, 8>(p, waves, trace, s, ev); break;
-    default: launch_verify_g<T, D, 1>(p, waves, trace, s, ev); break;
+  const int G = verify_heads_per_wg(p.hq, p.hkv, p.q_len, D);
+  const bool two = p.q_len * G > kMaxBlock;
+  if constexpr (D <= 128) {
+    if (two) {
+      switch (G) {
+        case 2: launch_verify_g<T, D, 2, 2>(p, waves, trace, s, ev); return hipGetLastError();
+        case 4: launch_verify_g<T, D, 4, 2>(p, waves, trace, s, ev); return hipGetLastError();
+        case 8: launch_verify_g<T, D, 8, 2>(p, waves, trace, s, ev); return hipGetLastError();
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
+  switch (G) {
+    case 2: launch_verify_g<T, D, 2, 1>(p, waves, trace, s, ev); break;
+    case 4: launch_verify_g<T, D, 4, 1>(p, waves, trace, s, ev); break;
+    case 8: launch_verify_g<T, D, 8, 1>(p, waves, trace, s, ev); break;
+    default: launch_verify_g<T, D, 1, 1>(p, waves, trace, s, ev); break;
   }
   return hipGetLastError();
 }

@@ -83,6 +83,20 @@ def build_workload(w, args):
     return built, layers
 
 
+def host_info() -> str:
+    """The host CPU the oracle ran on: model name and logical CPUs visible to this process."""
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return f"{model}; {len(os.sched_getaffinity(0))} logical CPUs available"
+
+
 def cpu_baseline(w, seconds: float):
     """The fp64 oracle, as it stands, on a bounded sample of the workload: rows of (seq, layer 0, loop,
     head) with their own and deepest planes regenerated on the host; the sample repeats until `seconds`
@@ -124,7 +138,7 @@ def cpu_baseline(w, seconds: float):
     rows_per_s = done / elapsed
     rows_per_token = w.n_layers * w.n_heads  # one loop-query token = every layer and head of one (seq, loop)
     return {"value": rows_per_s / rows_per_token, "unit": "loop-query tokens/s", "cores": oracle.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "host": host_info(),
             "sample": f"{done} rows ({n_rows} distinct (seq, layer 0, loop, head) rows of the {w.name} workload, "
                       f"L={L}, d={w.head_dim}, repeated) in {elapsed:.1f} s of fp64 oracle time; "
                       f"{rows_per_token} rows = 1 loop-query token"}
@@ -173,6 +187,7 @@ def cpu_baseline_cells(bc, seconds: float):
             done += 1
     rows_per_token = w.n_layers * w.n_heads
     return {"value": done / elapsed / rows_per_token, "unit": "loop-query tokens/s", "cores": 1, "kind": "oracle",
+            "host": host_info(),
             "sample": f"{done} cell rows ({len(rows)} distinct (seq, layer 0, loop, head) rows of the {w.name} "
                       f"workload, L={w.length}, repeated) in {elapsed:.1f} s of fp64 oracle time on one thread; "
                       f"{rows_per_token} rows = 1 loop-query token"}

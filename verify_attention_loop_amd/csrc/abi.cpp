@@ -839,11 +839,12 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
   const int group = hq / cfg.n_heads_kv;
   const bool gqa = a->mode == LKV_MODE_DECODE && (group == 2 || group == 4 || group == 8) &&
                    env_int("LKV_GQA_VALU", 0) == 0;
-  // Waves per workgroup: 4 for q = 1 rows, 2 for verify tiles (measured best on MI355X
-  // at the workloads' shapes; the environment can override for experiments).
+  // Waves per workgroup (measured best on MI355X at the workloads' shapes; the environment
+  // can override for experiments): 8 for multi-head q = 1 rows, 4 for grouped-query rows
+  // (and the grouped VALU kernel, whose registers grow with G), 2 for verify tiles.
   const int waves = a->mode == LKV_MODE_VERIFY ? env_int("LKV_VERIFY_WAVES", 2)
                     : gqa                     ? env_int("LKV_GQA_WAVES", 4)
-                                              : env_int("LKV_WAVES", 4);
+                                              : env_int("LKV_WAVES", group == 1 ? 8 : 4);
   const int64_t qrow = (int64_t)a->q_len * hq * D;
   for (int b0 = 0; b0 < a->n_seqs; b0 += kMaxRows) {
     const int nb = std::min(kMaxRows, a->n_seqs - b0);

@@ -195,3 +195,25 @@ def test_ouro_full_size_sampled():
         got_lse = lse.cpu().numpy()
         assert np.abs(np.array([got_lse[b, i, h] for (b, i, h) in rows]) - want_lse).max() <= 1e-3
     built.cache.close()
+
+
+def test_timing_events_stamp_the_launch_and_change_nothing():
+    """lkv_attend's optional event pair is stamped by the attention launch itself: the elapsed time is positive and
+    the outputs equal those of the same call without events, bit for bit (decode with splits and the merge)."""
+    w = _ragged(96)
+    lengths = [100, 257, 40]
+    built = harness.build_plain(w, lengths=lengths, layers=(1,), policy=vla.POLICY_RIPE, window=20)
+    q = harness.gpu_queries(built, 1, 2, 1)
+    a, _, _ = _attend(built, 1, 2, q, 3)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    ev1.record()  # torch creates the HIP events on first record
+    out = torch.empty_like(q)
+    ws = torch.empty(max(4, built.cache.lkv_workspace_bytes(1, 2, built.seqs, split_k=3)), dtype=torch.uint8,
+                     device="cuda")
+    built.cache.lkv_attend(1, 2, built.seqs, q, out, split_k=3, workspace=ws, ev_begin=ev0.cuda_event,
+                           ev_end=ev1.cuda_event)
+    torch.cuda.synchronize()
+    assert ev0.elapsed_time(ev1) > 0
+    assert torch.equal(out, a)
+    built.cache.close()

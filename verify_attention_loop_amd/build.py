@@ -1,7 +1,10 @@
 """Build libloopattn.so (gfx950) in-tree with hipcc.
 
 Every HIP source is compiled with packed-fp32 instructions disabled
-(``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``) and with MFMA results kept in
+ordinary VGPRs (``-mllvm -amdgpu-mfma-vgpr-form``): the attention kernels rescale
+their MFMA accumulators during the online softmax, which in AGPRs costs a copy out and
+back per element, and the AGPR form also took more registers in total.
 """
 from __future__ import annotations
 
@@ -29,7 +32,8 @@ def hipcc() -> str:
 
 def flags() -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fhip-fp32-correctly-rounded-divide-sqrt",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
+            "-fhip-fp32-correctly-rounded-divide-sqrt",
             "-Wno-unused-command-line-argument"]
 
 

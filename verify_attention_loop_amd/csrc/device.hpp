@@ -60,6 +60,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Online softmax with a lazy reference maximum, for accumulators that live in MFMA
+// result registers (AGPRs), where a rescale costs a read, a multiply and a write per
+// element: a column's reference maximum m moves only when a score passes it by more
+// than kLazyLog2 (base-2 units).  Weights 2^(x - m) then stay below 2^kLazyLog2, the
+// row sum and the accumulators keep using one m, so the softmax is the same, and once
+// the first page has set m a wave almost never rescales (lazy_any skips it).
+constexpr float kLazyLog2 = 8.f;
+
+__device__ __forceinline__ bool lazy_any(bool grow) { return __builtin_amdgcn_ballot_w64(grow) != 0; }
+
 // Raw dword loads of N bytes (N in {8, 12, 16, 32, 48, 64}); addresses are 4-byte aligned.
 template <int NB>
 struct Raw {

@@ -100,7 +100,8 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kerne
   const uint64_t koff = (uint64_t)hk * HEAD + (uint64_t)krow * D * ES + 16 * g;
   const uint64_t voff = (uint64_t)p.hkv * HEAD + (uint64_t)hk * HEAD + (uint64_t)g * (kQuad * D * ES) + 16 * n;
 
-  // Issue the loads of page pg.
+  // Issue the loads of page pg (no waits: the page's per-token plane choice for V waits
+  // until compute_page).
   auto load_page = [&](int pg, PR& r) {
     const int pos = pg * kPage;
     const bool any_own = min(pos + kPage, L) - 1 >= own_lo;
@@ -115,23 +116,31 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kerne
 #pragma unroll
     for (int s = 0; s < NB; ++s) load_raw<16>(r.k[s], kb + 64 * s);
     load_vquad<T, D>(r.v, (any_own ? base_own : base_deep) + voff);
-    if (pos + kPage > L || (any_own && any_deep)) {  // last page or window edge: per-token plane, validity
-      Raw<Tl::VB> vd;
-      if (any_own && any_deep) load_vquad<T, D>(vd, base_deep + voff);
-      bool take_deep[4], zero[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = pos + 4 * i + g;
-        take_deep[i] = any_own && any_deep && j < own_lo;
-        zero[i] = j >= L;
-      }
-      blend_quad<T, D>(r.v, vd, take_deep, zero);
-    }
   };
 
   // Scores, online softmax and weighted sum of one loaded page.
   auto compute_page = [&](int pg, const PR& r) {
     const int pos = pg * kPage;
+    // V: at the last page and the window edge the plane is chosen per token (the edge's
+    // plane-R quad is loaded here, once, since the case is rare) and tokens past the
+    // sequence are cleared
+    Raw<Tl::VB> v = r.v;
+    {
+      const bool any_own = min(pos + kPage, L) - 1 >= own_lo;
+      const bool any_deep = pos < own_lo;
+      if (pos + kPage > L || (any_own && any_deep)) {  // last page or window edge: per-token plane, validity
+        Raw<Tl::VB> vd;
+        if (any_own && any_deep) load_vquad<T, D>(vd, p.pool + (uint64_t)r.phys_deep * p.page_bytes + voff);
+        bool take_deep[4], zero[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = pos + 4 * i + g;
+          take_deep[i] = any_own && any_deep && j < own_lo;
+          zero[i] = j >= L;
+        }
+        blend_quad<T, D>(v, vd, take_deep, zero);
+      }
+    }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
@@ -148,22 +157,27 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kerne
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = pos + 4 * i + g < L ? sc[i] * p.scale_log2 : -INFINITY;
-    const float mn = fmaxf(m, col_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]))));
-    const float mu = (mn == -INFINITY) ? 0.f : mn;
-    const float alpha = fast_exp2(m - mu);
-    m = mn;
+    // lazy reference maximum (m moves only when the column's maximum passes it by more than
+    // kLazyLog2; from -inf any finite score moves it, with alpha = 0)
+    const float mx = col_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+    const bool grow = mx > m + kLazyLog2;
+    const float alpha = grow ? fast_exp2(m - mx) : 1.f;
+    if (grow) m = mx;
+    const float mu = (m == -INFINITY) ? 0.f : m;
     float pe[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pe[i] = fast_exp2(x[i] - mu);
+    if (lazy_any(grow)) {
 #pragma unroll
-    for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+      for (int a = 0; a < NACC; ++a) acc[a] *= alpha;
+    }
     if constexpr (F32) {
       lsum = fmaf(lsum, alpha, (pe[0] + pe[1]) + (pe[2] + pe[3]));
 #pragma unroll
       for (int s = 0; s < NACC; ++s)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(r.v.w[4 * s + e]), pe[e], acc[s], 0, 0, 0);
+          acc[s] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(v.w[4 * s + e]), pe[e], acc[s], 0, 0, 0);
     } else {
       // P in bf16 for the MFMA; the row sum uses the same rounded weights.
       const uint32_t p01 = pack_bf16x2(pe[0], pe[1]), p23 = pack_bf16x2(pe[2], pe[3]);
@@ -171,7 +185,7 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kerne
       const uint32_t pw[2] = {p01, p23};
 #pragma unroll
       for (int a = 0; a < NACC; ++a) {
-        const uint32_t vw[2] = {r.v.w[2 * a], r.v.w[2 * a + 1]};
+        const uint32_t vw[2] = {v.w[2 * a], v.w[2 * a + 1]};
         acc[a] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, vw),
                                                            __builtin_bit_cast(bf16x4_t, pw), acc[a], 0, 0, 0);
       }
@@ -190,16 +204,32 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kerne
 
   // The wave's pages are p0 + w, p0 + w + WAVES, ...  Up to d = 128 two register buffers
   // (a: even pages, b: odd) keep the next page's loads in flight; at d = 256 one page's
-  // operands are 64 VGPRs, and a single buffer keeps two waves per SIMD.
+  // operands are 64 VGPRs, and a single buffer keeps two waves per SIMD.  No prefetch
+  // sits inside a branch that rejoins before the compute it overlaps (the run's last
+  // page leaves the loop instead): the compiler's wait before a page then counts only
+  // the loads issued before it, where a conditional prefetch made it wait for all.
   if constexpr (D <= 128) {
-    PR ra, rb;
-    if (p0 + w < p1) load_page(p0 + w, ra);
-    for (int pa = p0 + w; pa < p1; pa += 2 * WAVES) {
-      const int pb = pa + WAVES, pc = pb + WAVES;
-      if (pb < p1) load_page(pb, rb);
-      compute_page(pa, ra);
-      if (pc < p1) load_page(pc, ra);
-      if (pb < p1) compute_page(pb, rb);
+    int pa = p0 + w;
+    if (pa < p1) {
+      PR ra, rb;
+      load_page(pa, ra);
+      while (true) {
+        const int pb = pa + WAVES;
+        if (pb >= p1) {
+          compute_page(pa, ra);
+          break;
+        }
+        load_page(pb, rb);
+        compute_page(pa, ra);
+        const int pc = pb + WAVES;
+        if (pc >= p1) {
+          compute_page(pb, rb);
+          break;
+        }
+        load_page(pc, ra);
+        compute_page(pb, rb);
+        pa = pc;
+      }
     }
   } else {
     for (int pa = p0 + w; pa < p1; pa += WAVES) {

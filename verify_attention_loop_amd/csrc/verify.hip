@@ -172,17 +172,21 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
             }
           }
         }
+        // (lazy reference maximum: m moves only when the column's maximum passes it by more
+        // than kLazyLog2; from -inf any finite score moves it, with alpha = 0)
         float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mx = xmax4(mx);
-        const float mn = fmaxf(m[t], mx);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = fast_exp2(m[t] - mu);
-        m[t] = mn;
+        const bool grow = mx > m[t] + kLazyLog2;
+        const float alpha = grow ? fast_exp2(m[t] - mx) : 1.f;
+        if (grow) m[t] = mx;
+        const float mu = (m[t] == -INFINITY) ? 0.f : m[t];
         float pe[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pe[i] = fast_exp2(x[i] - mu);
+        if (lazy_any(grow)) {
 #pragma unroll
-        for (int a = 0; a < NACC; ++a) acc[t][a] *= alpha;
+          for (int a = 0; a < NACC; ++a) acc[t][a] *= alpha;
+        }
 
         // ---- O^T += V^T P^T
         if constexpr (F32) {

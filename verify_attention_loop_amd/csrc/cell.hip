@@ -273,6 +273,22 @@ __device__ __forceinline__ void nibbles_f32(uint32_t code, float* f) {
   f[7] = ubyte_f32<3>(od);
 }
 
+// The eight nibbles of a code word as floats with the odd ones scaled by 16:
+// f[c] = nibble c (c even) or 16 nibble c (c odd), one mask per parity instead of a
+// shift and a mask.  The scale is a power of two, so a product or sum that carries it
+// rounds exactly as the unscaled one and dividing by 16 at the end restores it bit for bit.
+__device__ __forceinline__ void nibbles16_f32(uint32_t code, float* f) {
+  const uint32_t ev = code & 0x0F0F0F0Fu, od = code & 0xF0F0F0F0u;
+  f[0] = ubyte_f32<0>(ev);
+  f[1] = ubyte_f32<0>(od);
+  f[2] = ubyte_f32<1>(ev);
+  f[3] = ubyte_f32<1>(od);
+  f[4] = ubyte_f32<2>(ev);
+  f[5] = ubyte_f32<2>(od);
+  f[6] = ubyte_f32<3>(ev);
+  f[7] = ubyte_f32<3>(od);
+}
+
 // Inline asm is opaque to the compiler's hazard checks: ubyte_f32 only takes operands
 // made by bitwise ops, never by a transcendental op (v_exp and the like), whose result
 // a dependent VALU op on gfx950 may read only after a wait state.
@@ -422,6 +438,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
         qs[c] = fmaf(qf[c], f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
         bias = fmaf(qf[c], f16_to_f32(km.w[c] >> 16), bias);
       }
+      float sc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t code;
@@ -429,11 +446,15 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
         else code = lo_nibbles((k0.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
         float f[E];
         nibbles_f32(code, f);
-        float sc = bias;
+        sc[i] = bias;
 #pragma unroll
-        for (int c = 0; c < E; ++c) sc = fmaf(qs[c], f[c], sc);
-        x2[i] = row_sum16(sc) * p.scale_log2;
+        for (int c = 0; c < E; ++c) sc[i] = fmaf(qs[c], f[c], sc[i]);
       }
+      // the eight 16-lane sums step by step across tokens, so that consecutive DPP ops
+      // are independent
+      row_sum16_n<8>(sc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x2[i] = sc[i] * p.scale_log2;
       // Past the sequence (last page only): score -inf and V meta cleared, so that those
       // tokens get zero weight against finite scales whatever the page holds there.
       if (cp * kCodePage + kCodePage > n_far) {
@@ -505,7 +526,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
         if constexpr (BITS == 4) code = hi_nibbles(hw) | lo_nibbles(lo16[i]);
         else code = lo_nibbles(hw);
         float f[E];
-        nibbles_f32(code, f);
+        nibbles16_f32(code, f);  // odd channels accumulate 16 times their value
 #pragma unroll
         for (int c = 0; c < E; ++c) o[c] = fmaf(wgt[i], f[c], o[c]);
       }
@@ -564,6 +585,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
         if (active) far_values(cp, hb, x2, fmaxf(m_page, m0_2) - p.v_tau, vh, vm);
       }
     }
+  }
+
+  if (part != p.n_splits) {
+#pragma unroll
+    for (int e = 1; e < E; e += 2) o[e] *= 0.0625f;  // undo the odd channels' scale of 16 (exact)
   }
 
   // merge the 4 * WAVES row states

@@ -48,6 +48,20 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
+// row_sum16 of N values, one reduction step at a time across them (the DPP ops of a
+// step are independent, so no wait states sit between them).
+template <int N>
+__device__ __forceinline__ void row_sum16_n(float* x) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp<0xB1>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp<0x4E>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp<0x141>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += dpp<0x140>(x[i]);
+}
+
 __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp<0xB1>(x));
   x = fmaxf(x, dpp<0x4E>(x));

@@ -315,10 +315,10 @@ __device__ __forceinline__ uint32_t or4(uint32_t v) {
 // Each DPP row keeps its own online softmax; partials go to the workspace and
 // the LSE merge kernel combines them.
 template <int WAVES, bool TRACE, int BITS, bool RUNNING>
-// The kernel is VALU-bound; six waves per SIMD fit the fixed rule in 80 VGPRs without spills
-// (the running rule keeps a page's scores across a barrier and takes five; the traced
-// variants, for tests, are left unconstrained).
-__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cell_kernel(const CellParams p) {
+// The kernel is VALU-bound; six waves per SIMD fit the fixed rule in 80 VGPRs and INT2
+// cells (no hot test) seven in 72 (the running rule keeps a page's scores across a barrier
+// and takes five; the traced variants, for tests, are left unconstrained).
+__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ? 7 : 6))) void cell_kernel(const CellParams p) {
   constexpr int D = 128, E = 8;
   constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;

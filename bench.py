@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "loop-query tokens/s + achieved HBM GB/s (% of MI355X peak), looped-KV attention"
 # Sources of each workload's timed attention kernel (with the shared device headers): the
-# counter summary in profiles/ holds their hash and is ignored once any of them changes.
+# counter summary in profiles/ holds their hash, together with the compiler flags, and is
+# ignored once any of them changes.
 _CSRC = "verify_attention_loop_amd/csrc/"
 _COMMON = [_CSRC + "device.hpp", _CSRC + "params.hpp"]
 KERNEL_SOURCES = {
@@ -50,6 +51,9 @@ def kernel_hash(workload: str) -> str:
     for f in KERNEL_SOURCES[workload]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
+    from verify_attention_loop_amd import build as _build  # flags only; compiles nothing
+    flags = [f for f in _build.flags() if f != "-I" and not os.path.isabs(f)]  # no include paths
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 

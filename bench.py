@@ -67,6 +67,8 @@ def parse():
                              "dory_lastloop"])
     ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers held in HBM (0: all)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="sequences per call (0: the workload's); other batches report no traffic figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record HIP events around one launch in this many (rotating over the calls, so every "
@@ -213,6 +215,9 @@ def main():
     vla.load()
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
+    if args.batch > 0:
+        import dataclasses
+        w = dataclasses.replace(w, batch=args.batch)
     t_setup = time.perf_counter()
     R, B, q_len = w.n_loops, w.batch, w.q_len
     split = w.split_k if args.split_k < 0 else args.split_k
@@ -303,7 +308,7 @@ def main():
     # achieved = algorithmic bytes of the sampled launches / their summed duration
     achieved = float(sum(call_bytes[n] for (_, n) in sampled)) / (kern.sum() / 1e3) / 1e9
     khash = kernel_hash(args.workload)
-    traffic = read_traffic(args.workload, khash)
+    traffic = read_traffic(args.workload, khash) if args.batch <= 0 else None  # counters: the workload's batch
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

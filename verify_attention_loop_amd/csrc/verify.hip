@@ -15,8 +15,10 @@
 // of the PV product, and exactly the four tokens of V quad g, whose
 // [channel][4 tokens] layout is the V^T operand (four tokens of one channel per
 // lane).  Columns beyond the block are padding.  V is read with nontemporal loads
-// (whole lines per instruction); K rows are 64-byte pieces of 128-256-byte token
-// rows, so they use plain loads, which L2 merges.
+// (whole lines per instruction); so is K, as the page's contiguous K slice of the KV
+// head, staged through LDS, from which each lane reads its operand pieces (16 bytes of
+// a token row): read straight from memory those would be 64-byte pieces of 128-512-byte
+// rows, partial lines that nontemporal loads serve badly.
 //
 // Grouped-query attention: with G > 1 a workgroup serves the G query heads of one
 // KV head and column c is (block row c / G, head c % G), so every K/V page is read
@@ -114,6 +116,13 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
                         (uint64_t)(F32 ? n * kQuad * 4 : 2 * n * kQuad * 2);
   constexpr int KSTEP = F32 ? 16 * 4 : 32 * 2;              // bytes between a lane's K loads
   constexpr int VSTEP = F32 ? 16 * kQuad * 4 : 32 * kQuad * 2;  // bytes between a lane's V loads
+  // K goes through LDS: the wave reads the page's K slice of its KV head (HEAD bytes,
+  // contiguous) with whole-line streaming loads, lane l taking bytes 16 l + 1024 s, and
+  // then reads its MFMA operands (row tokens, 16-byte channel pieces) from LDS.
+  static_assert(HEAD == NB * 64 * 16, "one 16-byte piece per lane and load");
+  __shared__ __attribute__((aligned(16))) uint8_t sm_k[WAVES][HEAD];
+  const uint64_t kslice = (uint64_t)hk * HEAD;
+  const int kl = (int)(koff - kslice);  // the lane's operand offset inside the slice
 
   for (int pg = p0 + w; pg < p1; pg += WAVES) {
     const int pos = pg * kPage;
@@ -124,12 +133,23 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
       const bool own = pass == 0;
       const int phys = own ? tab_own[pg % p.ring_own] : tab_deep[pg];
       const uint8_t* base = p.pool + (uint64_t)phys * p.page_bytes;
-      // Issue every load of the page first: K rows (plain loads) and V quads (streaming).
-      Raw<16> kr[NB], vr[NB];
+      // Issue every load of the page first: the K slice and the V quads (streaming).
+      Raw<16> kr[NB], vr[NB], kst[NB];
 #pragma unroll
-      for (int s = 0; s < NB; ++s) load_raw<16>(kr[s], base + koff + s * KSTEP);
+      for (int s = 0; s < NB; ++s) load_stream<16>(kst[s], base + kslice + (s * 64 + lane) * 16);
 #pragma unroll
       for (int s = 0; s < NB; ++s) load_stream<16>(vr[s], base + voff + s * VSTEP);
+#pragma unroll
+      for (int s = 0; s < NB; ++s)
+        *reinterpret_cast<u32x4_t*>(&sm_k[w][(s * 64 + lane) * 16]) = u32x4_t{kst[s].w[0], kst[s].w[1], kst[s].w[2], kst[s].w[3]};
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&sm_k[w][kl + s * KSTEP]);
+        kr[s].w[0] = v.x;
+        kr[s].w[1] = v.y;
+        kr[s].w[2] = v.z;
+        kr[s].w[3] = v.w;
+      }
       // V of tokens this pass does not own is cleared (unused or poisoned slots may hold
       // NaN, and 0 * NaN is NaN); the same for every column
       bool keep[4];

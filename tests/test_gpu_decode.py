@@ -217,3 +217,30 @@ def test_timing_events_stamp_the_launch_and_change_nothing():
     assert ev0.elapsed_time(ev1) > 0
     assert torch.equal(out, a)
     built.cache.close()
+
+
+def test_binding_refuses_undersized_buffers_before_any_launch():
+    """A q, out, lse or append buffer smaller than the call's documented shape, or of the wrong element type, raises
+    ValueError in the binding (the library takes bare addresses); the cache stays usable and a correct call after
+    the refusals still matches the earlier result."""
+    w = _ragged(96)
+    built = harness.build_plain(w, lengths=[100, 40], layers=(1,), policy=vla.POLICY_RIPE, window=20)
+    q = harness.gpu_queries(built, 1, 2, 1)
+    a, _, _ = _attend(built, 1, 2, q, 1)
+    out = torch.empty_like(q)
+    with pytest.raises(ValueError, match=r"^out holds"):
+        built.cache.lkv_attend(1, 2, built.seqs, q, out[:1], split_k=1)
+    with pytest.raises(ValueError, match=r"^q has element type"):
+        built.cache.lkv_attend(1, 2, built.seqs, q.float(), out, split_k=1)
+    with pytest.raises(ValueError, match=r"^lse holds"):
+        built.cache.lkv_attend(1, 2, built.seqs, q, out, split_k=1,
+                               lse=torch.empty(1, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match=r"^out must be contiguous"):
+        built.cache.lkv_attend(1, 2, built.seqs, q, out.transpose(2, 3), split_k=1)
+    kv = torch.empty((4, w.hkv, w.head_dim), dtype=q.dtype, device="cuda")
+    with pytest.raises(ValueError, match=r"^v holds"):
+        built.cache.lkv_append_plane(built.seqs[0], 1, w.n_loops - 1, 100, kv, kv[:2])
+    built.cache.lkv_attend(1, 2, built.seqs, q, out, split_k=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, a)
+    built.cache.close()

@@ -321,3 +321,40 @@ def test_speculative_steps_keep_exactly_the_ripe_pages(lib, gamma, W):
                     plane, phys, slot = c.lkv_debug_resolve(s, 1, loop, t, t, j)
                     assert plane == oracle.oracle_plane(oracle.RIPE, loop, R, t, t, j, W)
                     assert phys >= 0 and slot == j % 16
+
+
+def test_binding_rejects_host_noncontiguous_and_undersized_tensors():
+    """The binding hands the library bare addresses, so it checks tensor arguments first: a host tensor, a
+    non-contiguous view, a wrong element type or too few elements raise ValueError; None and int addresses pass."""
+    torch = pytest.importorskip("torch")
+    need = vla._need
+    need(None, "x", 10, 4)
+    need(1234, "x", 10, 4)
+    with pytest.raises(ValueError, match="device tensor"):
+        need(torch.zeros(16), "x", 10, 4)
+
+    class FakeDev:  # a stand-in with the tensor attributes the check reads (no GPU here)
+        is_cuda = True
+
+        def __init__(self, n, es, dtype, contiguous=True):
+            self.n, self.es, self.dtype, self.c = n, es, dtype, contiguous
+
+        def is_contiguous(self):
+            return self.c
+
+        def element_size(self):
+            return self.es
+
+        def numel(self):
+            return self.n
+
+    need(FakeDev(10, 2, torch.bfloat16), "q", 10, 2, (torch.bfloat16,))
+    with pytest.raises(ValueError, match="contiguous"):
+        need(FakeDev(10, 2, torch.bfloat16, contiguous=False), "q", 10, 2, (torch.bfloat16,))
+    with pytest.raises(ValueError, match="element type"):
+        need(FakeDev(10, 2, torch.float16), "q", 10, 2, (torch.bfloat16,))
+    with pytest.raises(ValueError, match="element type"):
+        need(FakeDev(10, 4, torch.float32), "q", 10, 2, (torch.bfloat16,))
+    with pytest.raises(ValueError, match="needs 11"):
+        need(FakeDev(10, 2, torch.bfloat16), "q", 11, 2, (torch.bfloat16,))
+    need(FakeDev(3, 8, torch.float64), "workspace", 0, None)

@@ -126,6 +126,23 @@ def _ptr(x) -> int:
     return x.data_ptr()
 
 
+def _need(t, name: str, n_elems: int, elem_bytes: int, dtypes=None):
+    """A tensor argument must be a contiguous device tensor of the documented element type holding at
+    least n_elems elements: the library takes bare addresses and sizes its kernels from the call's
+    arguments, so a smaller buffer would be read or written past its end.  None and int addresses pass
+    through (the caller vouches for them)."""
+    if t is None or isinstance(t, int):
+        return
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if elem_bytes is not None and (t.element_size() != elem_bytes or (dtypes is not None and t.dtype not in dtypes)):
+        raise ValueError(f"{name} has element type {t.dtype}, expected {elem_bytes}-byte {dtypes or ''}")
+    if t.numel() < n_elems:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {n_elems}")
+
+
 def _stream(stream) -> int:
     if stream is None:
         import torch
@@ -208,8 +225,16 @@ class LoopCache:
     def lkv_reserve(self, seq: int, layer: int, plane: int, pos0: int, n_tok: int):
         self._check(self.lib.lkv_reserve(self.h, seq, layer, plane, pos0, n_tok), "lkv_reserve")
 
+    def _kv_types(self):
+        import torch
+        return (4, (torch.float32,)) if self.cfg.kv_dtype == DTYPE_F32 else (2, (torch.bfloat16,))
+
     def lkv_append_plane(self, seq: int, layer: int, plane: int, pos0: int, k, v, stream=None):
         n_tok = k.shape[0]
+        row = self.cfg.n_heads_kv * self.cfg.head_dim
+        eb, dt = self._kv_types()
+        _need(k, "k", n_tok * row, eb, dt)
+        _need(v, "v", n_tok * row, eb, dt)
         self._check(self.lib.lkv_append_plane(self.h, seq, layer, plane, pos0, n_tok, _ptr(k), _ptr(v),
                                               _stream(stream)), "lkv_append_plane")
 
@@ -224,18 +249,32 @@ class LoopCache:
         a = np.ascontiguousarray(kinds, dtype=np.int8)
         self._check(self.lib.lkv_set_plan(self.h, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int8))), "lkv_set_plan")
 
+    def _coded_args(self, n_pages, k_codes, k_meta, v_codes, v_meta):
+        hkv, d = self.cfg.n_heads_kv, self.cfg.head_dim
+        _need(k_codes, "k_codes", n_pages * CODE_PAGE_TOKENS * hkv * d, 1)
+        _need(k_meta, "k_meta", n_pages * hkv * d * 2, 2)
+        _need(v_codes, "v_codes", n_pages * CODE_PAGE_TOKENS * hkv * d, 1)
+        _need(v_meta, "v_meta", n_pages * CODE_PAGE_TOKENS * hkv * (d // 32) * 2, 2)
+
     def lkv_append_coded(self, seq: int, layer: int, loop: int, page0: int, n_pages: int, k_codes, k_meta, v_codes,
                          v_meta, stream=None):
+        self._coded_args(n_pages, k_codes, k_meta, v_codes, v_meta)
         self._check(self.lib.lkv_append_coded(self.h, seq, layer, loop, page0, n_pages, _ptr(k_codes), _ptr(k_meta),
                                               _ptr(v_codes), _ptr(v_meta), _stream(stream)), "lkv_append_coded")
 
     def lkv_encode_pages(self, seq: int, layer: int, loop: int, page0: int, n_pages: int, n_valid_last: int, k, v,
                          stream=None):
+        import torch
+        n_tok = max(0, (n_pages - 1) * CODE_PAGE_TOKENS + n_valid_last)
+        row = self.cfg.n_heads_kv * self.cfg.head_dim
+        _need(k, "k", n_tok * row, 2, (torch.bfloat16,))
+        _need(v, "v", n_tok * row, 2, (torch.bfloat16,))
         self._check(self.lib.lkv_encode_pages(self.h, seq, layer, loop, page0, n_pages, n_valid_last, _ptr(k), _ptr(v),
                                               _stream(stream)), "lkv_encode_pages")
 
     def lkv_read_coded(self, seq: int, layer: int, loop: int, page0: int, n_pages: int, k_codes, k_meta, v_codes,
                        v_meta, stream=None):
+        self._coded_args(n_pages, k_codes, k_meta, v_codes, v_meta)
         self._check(self.lib.lkv_read_coded(self.h, seq, layer, loop, page0, n_pages, _ptr(k_codes), _ptr(k_meta),
                                             _ptr(v_codes), _ptr(v_meta), _stream(stream)), "lkv_read_coded")
 
@@ -263,8 +302,30 @@ class LoopCache:
         self._check(self.lib.lkv_workspace_bytes(self.h, ctypes.byref(a), ctypes.byref(n)), "lkv_workspace_bytes")
         return n.value
 
+    def _attend_buffers(self, a, q, out, kw):
+        """Sizes of the call's tensors, from the same arguments the library sizes its kernels by."""
+        import torch
+        c = self.cfg
+        n, k, hq, hkv, d = a.n_seqs, max(1, a.q_len), c.n_heads_q, c.n_heads_kv, c.head_dim
+        eb, dt = self._kv_types()
+        _need(q, "q", n * k * hq * d, eb, dt)
+        _need(out, "out", n * k * hq * d, eb, dt)
+        _need(kw.get("lse"), "lse", n * k * hq, 4, (torch.float32,))
+        _need(kw.get("workspace"), "workspace", 0, None)  # its size in bytes is passed and checked by the library
+        if a.draft_len > 0:
+            _need(kw.get("draft_k"), "draft_k", n * a.draft_len * hkv * d, eb, dt)
+            _need(kw.get("draft_v"), "draft_v", n * a.draft_len * hkv * d, eb, dt)
+        if a.trace_len > 0:
+            _need(kw.get("index_trace"), "index_trace", n * k * a.trace_len * 2, 4, (torch.int32,))
+        if kw.get("mask_trace") is not None and c.quant:
+            far = max(max(0, self.lkv_seq_info(a.seq_ids[b])[0] - c.sink - c.tail) for b in range(n))
+            _need(kw.get("mask_trace"), "mask_trace", n * hq * ((far + 31) // 32), 4)
+
     def lkv_attend(self, layer, loop, seq_ids, q, out, stream=None, **kw):
         a, _ids = self._args(layer, loop, seq_ids, q, out, **kw)
+        if not 1 <= a.n_seqs <= self.cfg.max_seqs:
+            raise ValueError(f"n_seqs {a.n_seqs} outside [1, {self.cfg.max_seqs}]")
+        self._attend_buffers(a, q, out, kw)
         self._check(self.lib.lkv_attend(self.h, ctypes.byref(a), _stream(stream)), "lkv_attend")
 
     def lkv_mem_stats(self) -> dict:

@@ -37,12 +37,14 @@ KERNEL_SOURCES = {
     "huginn_ripe": [_CSRC + "decode.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "ouro_splitk": [_CSRC + "decode.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "huginn_verify": [_CSRC + "verify.hip"] + _COMMON,
+    "huginn_draft": [_CSRC + "decode.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "loopkv_cells": [_CSRC + "cell.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "raven_ripe": [_CSRC + "gqa.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "dory_lastloop": [_CSRC + "gqa.hip", _CSRC + "attn_common.hpp"] + _COMMON,
 }
 # The timed attention kernel of each workload (rocprofv3 kernel name prefix).
 KERNEL_NAME = {"huginn_ripe": "decode_kernel", "ouro_splitk": "decode_kernel", "huginn_verify": "verify_kernel",
+               "huginn_draft": "decode_kernel",
                "loopkv_cells": "cell_kernel", "raven_ripe": "gqa_decode_kernel", "dory_lastloop": "gqa_decode_kernel"}
 
 
@@ -63,8 +65,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="huginn_ripe",
-                    choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "loopkv_cells", "raven_ripe",
-                             "dory_lastloop"])
+                    choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "huginn_draft", "loopkv_cells",
+                             "raven_ripe", "dory_lastloop"])
     ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers held in HBM (0: all)")
     ap.add_argument("--batch", type=int, default=0,
@@ -85,7 +87,9 @@ def parse():
 def build_workload(w, args):
     import harness
     layers = list(range(w.n_layers if args.layers <= 0 else min(args.layers, w.n_layers)))
-    built = harness.build_plain(w, layers=layers)
+    # the draft workload's cache takes blocks of draft_passes + 1 tokens (the verify block)
+    max_block = w.extra["draft_passes"] + 1 if "draft_passes" in w.extra else None
+    built = harness.build_plain(w, layers=layers, max_block=max_block)
     return built, layers
 
 
@@ -117,13 +121,19 @@ def cpu_baseline(w, seconds: float):
     pol = oracle.RIPE if w.policy == "ripe" else oracle.FULL
     rng = np.random.default_rng(0)
     n_rows = 24
-    L = w.length
+    draft = "draft_passes" in w.extra
+    # a draft row (the middle pass, 4 draft tokens): cached positions through the draft window, the block from
+    # the draft streams
+    dl = 4 if draft else 0
+    window = w.extra["draft_window"] if draft else w.window
+    L = w.length + dl
     q = np.empty((n_rows, w.head_dim))
     ko = np.empty((n_rows, L, w.head_dim))
     vo, kd, vd = np.empty_like(ko), np.empty_like(ko), np.empty_like(ko)
     loops = np.empty(n_rows, dtype=np.int32)
     for i in range(n_rows):
-        b, h, r = int(rng.integers(w.batch)), int(rng.integers(w.n_heads)), int(rng.integers(R))
+        b, h = int(rng.integers(w.batch)), int(rng.integers(w.n_heads))
+        r = int(rng.integers(w.extra["draft_loops"] if draft else R))
         hk = h // (w.n_heads // w.hkv)  # the query head's KV head
         loops[i] = r
         ko[i] = harness.cpu_values(w, synth.T_K, b, 0, r, hk, L)
@@ -133,12 +143,16 @@ def cpu_baseline(w, seconds: float):
             vd[i] = harness.cpu_values(w, synth.T_V, b, 0, R - 1, hk, L)
         else:
             kd[i], vd[i] = ko[i], vo[i]
+        if draft:
+            ko[i, w.length:] = harness.cpu_draft_values(w, synth.T_DRAFTK, b, 0, r, hk, w.length, dl)
+            vo[i, w.length:] = harness.cpu_draft_values(w, synth.T_DRAFTV, b, 0, r, hk, w.length, dl)
         q[i] = harness.cpu_query(w, b, 0, r, h, L - 1)
     t = np.full(n_rows, L - 1, dtype=np.int32)
+    t0 = np.full(n_rows, L - 1 - (dl - 1 if draft else 0), dtype=np.int32)
     done, elapsed = 0, 0.0
     while elapsed < seconds:
         t1 = time.perf_counter()
-        oracle.attend_rows(q, ko, vo, kd, vd, t, t, loops, pol, R, w.window)
+        oracle.attend_rows(q, ko, vo, kd, vd, t, t0, loops, pol, R, window)
         elapsed += time.perf_counter() - t1
         done += n_rows
     rows_per_s = done / elapsed
@@ -222,22 +236,37 @@ def main():
     R, B, q_len = w.n_loops, w.batch, w.q_len
     split = w.split_k if args.split_k < 0 else args.split_k
     layers = list(range(w.n_layers if args.layers <= 0 else min(args.layers, w.n_layers)))
+    draft = "draft_passes" in w.extra
     if w.quant:
         built = harness.build_cells(w, layers=layers)
         mode = vla.MODE_DECODE
     else:
         built, layers = build_workload(w, args)
-        mode = vla.MODE_VERIFY if q_len > 1 else vla.MODE_DECODE
+        mode = vla.MODE_DRAFT if draft else (vla.MODE_VERIFY if q_len > 1 else vla.MODE_DECODE)
     kernel = KERNEL_NAME[w.name]
     cache = built.cache
     n_layers_step = w.n_layers
-    # Queries and outputs of every (layer, loop) call of a step, resident in HBM.
-    calls = [(layer, loop) for loop in range(R) for layer in range(n_layers_step)]
-    qs, outs = {}, {}
-    for (layer, loop) in calls:
+    # Every call of a step, (layer, loop, g), in the model's order: every core layer at every loop, loop-major;
+    # the draft workload repeats that over its first loops for passes g = 1 .. draft_passes (draft block of g
+    # tokens).  Queries, outputs and draft scratch of every call are resident in HBM.
+    if draft:
+        passes, d_loops = w.extra["draft_passes"], w.extra["draft_loops"]
+        calls = [(layer, loop, g) for g in range(1, passes + 1) for loop in range(d_loops)
+                 for layer in range(n_layers_step)]
+    else:
+        calls = [(layer, loop, 0) for loop in range(R) for layer in range(n_layers_step)]
+    qs, outs, call_kw = {}, {}, {}
+    for c in calls:
+        layer, loop, g = c
         src_layer = layers[layer % len(layers)]
-        qs[(layer, loop)] = harness.gpu_queries(built, src_layer, loop, q_len)
-        outs[(layer, loop)] = torch.empty_like(qs[(layer, loop)])
+        if draft:
+            qs[c] = harness.gpu_queries(built, src_layer, loop, 1, t0s=[L + g - 1 for L in built.lengths])
+            dk, dv = harness.gpu_draft_kv(w, built.rows, src_layer, loop, built.lengths, g)
+            call_kw[c] = dict(window=w.extra["draft_window"], draft_k=dk, draft_v=dv, draft_len=g)
+        else:
+            qs[c] = harness.gpu_queries(built, src_layer, loop, q_len)
+            call_kw[c] = {}
+        outs[c] = torch.empty_like(qs[c])
     ws_bytes = cache.lkv_workspace_bytes(0, 0, built.seqs, q_len=q_len, mode=mode, split_k=split)
     ws = torch.empty(max(4, ws_bytes), dtype=torch.uint8, device="cuda")
     extra = {}
@@ -256,14 +285,17 @@ def main():
         for b, nf in enumerate(n_far):
             valid[b, 0, :nf] = True
         call_bytes = []
-        for (layer, loop) in calls:
+        for c in calls:
+            layer, loop, _ = c
             src_layer = layers[layer % len(layers)]
-            cache.lkv_attend(src_layer, loop, built.seqs, qs[(layer, loop)], outs[(layer, loop)], split_k=split,
-                             workspace=ws, mask_trace=mask, **extra)
+            cache.lkv_attend(src_layer, loop, built.seqs, qs[c], outs[c], split_k=split, workspace=ws,
+                             mask_trace=mask, **extra)
             bits = np.unpackbits(mask.cpu().numpy().view(np.uint8), bitorder="little").reshape(
                 len(built.seqs), w.n_heads, words * 32).astype(bool)
             n_cold = int((~bits & valid.numpy()).sum())
             call_bytes.append(harness.cell_bytes_per_call(built, src_layer, loop, n_cold))
+    elif draft:  # the cached positions and the g draft tokens, once per (seq, KV head)
+        call_bytes = [harness.algorithmic_bytes_per_call(w, [L + g for L in built.lengths], 1) for (_, _, g) in calls]
     else:
         call_bytes = [harness.algorithmic_bytes_per_call(w, built.lengths, q_len)] * len(calls)
     torch.cuda.synchronize()
@@ -272,12 +304,13 @@ def main():
     every = max(1, args.event_every)
 
     def step(events=None, k=0):
-        for n, (layer, loop) in enumerate(calls):
-            kw = dict(extra)
+        for n, c in enumerate(calls):
+            layer, loop, _ = c
+            kw = dict(extra, **call_kw[c])
             if events is not None and (n + k) % every == 0:
                 kw.update(ev_begin=events[2 * n].cuda_event, ev_end=events[2 * n + 1].cuda_event)
-            cache.lkv_attend(layers[layer % len(layers)], loop, built.seqs, qs[(layer, loop)], outs[(layer, loop)],
-                             q_len=q_len, mode=mode, split_k=split, workspace=ws, **kw)
+            cache.lkv_attend(layers[layer % len(layers)], loop, built.seqs, qs[c], outs[c], q_len=q_len, mode=mode,
+                             split_k=split, workspace=ws, **kw)
 
     for _ in range(args.warmup):
         step()
@@ -302,7 +335,7 @@ def main():
     for o in outs.values():
         assert torch.isfinite(o.float()).all(), "non-finite attention output"
 
-    tokens_per_step = B * q_len * R
+    tokens_per_step = B * passes * d_loops if draft else B * q_len * R
     value = tokens_per_step / (ms_per_step / 1e3)
     alg_bytes = float(np.mean(call_bytes))
     # achieved = algorithmic bytes of the sampled launches / their summed duration
@@ -337,6 +370,9 @@ def main():
            "page_tokens": 32 if w.quant else 16, "split_k": split, "calls_per_step": len(calls),
            "layers_resident": len(layers), "kernel_ms_per_step": round(mean_launch_ms * len(calls), 4),
            "setup_s": round(setup_s, 1)}
+    if draft:
+        cfg.update(draft_passes=passes, draft_loops=d_loops, draft_window=w.extra["draft_window"],
+                   draft_block="1..%d tokens from scratch" % passes)
     if w.quant:
         cfg.update(sink=w.sink, tail=w.tail,
                    v_thresh="m0 - 4.0" if args.v_rule == "fixed" else f"max(m, m0) - {args.v_tau} ln 2 (running)",

@@ -122,6 +122,30 @@ def gpu_queries(built: Built, layer: int, loop: int, q_len: int, t0s=None, seed=
     return out
 
 
+def gpu_draft_kv(w: synth.Workload, rows, layer: int, loop: int, n_cached, dl: int, seed=None):
+    """Scratch keys and values of a draft block, device [n_seqs][dl][n_kv_heads][d]: positions n_cached[b] ..
+    n_cached[b] + dl - 1 of the draft streams of each sequence's row."""
+    import torch
+    dt = torch_dtype(w.dtype)
+    dk = torch.empty((len(rows), dl, w.hkv, w.head_dim), dtype=dt, device="cuda")
+    dv = torch.empty_like(dk)
+    st = torch.cuda.current_stream().cuda_stream
+    seed = w.seed if seed is None else seed
+    for b, r in enumerate(rows):
+        for t, buf in ((synth.T_DRAFTK, dk), (synth.T_DRAFTV, dv)):
+            synth.gpu_kv(buf[b].data_ptr(), w.dtype, seed, t, r, layer, loop, w.hkv, w.head_dim, n_cached[b], dl,
+                         synth.MODE_PLAIN, w.n_loops, w.scale, st)
+    return dk, dv
+
+
+def cpu_draft_values(w: synth.Workload, tensor: int, b: int, layer: int, loop: int, head: int, n_cached: int, dl: int,
+                     seed=None):
+    """fp64 values [dl][d] of one KV head of a draft block (the host side of gpu_draft_kv)."""
+    x = synth.kv(w.dtype, w.seed if seed is None else seed, tensor, b, layer, loop, w.hkv, w.head_dim, n_cached, dl,
+                 synth.MODE_PLAIN, w.n_loops, w.scale, heads=[head])[:, 0, :]
+    return to_f64(x, w.dtype)
+
+
 def cpu_values(w: synth.Workload, tensor: int, b: int, layer: int, plane: int, head: int, n_pos: int, seed=None):
     """fp64 values [n_pos][d] of one (tensor, row, layer, plane, KV head), as the cache holds them."""
     x = synth.kv(w.dtype, w.seed if seed is None else seed, tensor, b, layer, plane, w.hkv, w.head_dim, 0,

@@ -300,6 +300,12 @@ WORKLOADS = {
     # Self-speculative verify on the Huginn shape: 800 cached + block of 8, batch 16.
     "huginn_verify": Workload("huginn_verify", 16, 4, 32, 55, 96, 808, DT_BF16, "ripe", 64, 8, 16,
                               MODE_RIPEN, 1.0, extra={"draft_loops": 4}),
+    # The draft passes of the same self-speculative step: 7 single-token passes (draft block growing from 1 to 7
+    # tokens) through the first 4 loops of every layer, 16 seqs with 800 cached positions (length counts the
+    # cached positions here) that the draft reads from the deepest plane (draft window 0); the block's own keys
+    # and values come from scratch.
+    "huginn_draft": Workload("huginn_draft", 16, 4, 32, 55, 96, 800, DT_BF16, "ripe", 64, 1, 16, MODE_RIPEN, 1.0,
+                             extra={"draft_passes": 7, "draft_loops": 4, "draft_window": 0}),
     # Ouro-shaped paged decode: 24 layers x 4 loops, 16 heads x 128, L=8192, batch 32, 8 splits.
     "ouro_splitk": Workload("ouro_splitk", 32, 24, 4, 16, 128, 8192, DT_BF16, "full", 0, 1, 16,
                             MODE_PLAIN, 1.0, split_k=8, shuffle=True),

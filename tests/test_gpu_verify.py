@@ -197,3 +197,36 @@ def test_huginn_verify_full_size_sampled(policy):
         got = np.array([o[b, i, h] for (b, i, h) in rows])
         assert np.abs(got - want).max() <= TOL_BF16
     built.cache.close()
+
+
+@pytest.mark.slow
+def test_huginn_draft_full_size_sampled():
+    """The draft passes at the Huginn shape, in the launch configuration the benchmark times: 16 sequences with
+    800 cached positions, 55 heads x 96, draft window 0 (cached positions from the deepest plane), draft blocks of
+    1, 4 and 7 tokens from scratch; layer 0, loops 0 and 3; sampled heads of every sequence against the oracle."""
+    w = synth.WORKLOADS["huginn_draft"]
+    R = w.n_loops
+    built = harness.build_plain(w, layers=(0,), planes=[0, 3], max_block=w.extra["draft_passes"] + 1)
+    rng = np.random.default_rng(5)
+    for loop in (0, 3):
+        for g in (1, 4, 7):
+            dk, dv = harness.gpu_draft_kv(w, built.rows, 0, loop, built.lengths, g)
+            q = harness.gpu_queries(built, 0, loop, 1, t0s=[L + g - 1 for L in built.lengths])
+            out = torch.empty_like(q)
+            built.cache.lkv_attend(0, loop, built.seqs, q, out, mode=vla.MODE_DRAFT, window=0, split_k=1,
+                                   draft_k=dk, draft_v=dv, draft_len=g)
+            torch.cuda.synchronize()
+            o = harness.out_f64(out)
+            assert np.isfinite(o).all()
+            for b, n in enumerate(built.lengths):
+                h = int(rng.integers(w.n_heads))
+                L = n + g
+                kd = harness.cpu_values(w, synth.T_K, b, 0, R - 1, h, L)
+                vd = harness.cpu_values(w, synth.T_V, b, 0, R - 1, h, L)
+                ko, vo = kd.copy(), vd.copy()  # cached positions come from the deepest plane at window 0
+                ko[n:] = harness.cpu_draft_values(w, synth.T_DRAFTK, b, 0, loop, h, n, g)
+                vo[n:] = harness.cpu_draft_values(w, synth.T_DRAFTV, b, 0, loop, h, n, g)
+                qq = harness.cpu_query(w, b, 0, loop, h, L - 1)
+                want, _ = oracle.attend_row(qq, ko, vo, kd, vd, L - 1, n, vla.POLICY_RIPE, loop, R, 0)
+                assert np.abs(o[b, 0, h] - want).max() <= TOL_BF16, (loop, g, b, h)
+    built.cache.close()

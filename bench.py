@@ -34,6 +34,7 @@ METRIC = "loop-query tokens/s + achieved HBM GB/s (% of MI355X peak), looped-KV 
 _CSRC = "verify_attention_loop_amd/csrc/"
 _COMMON = [_CSRC + "device.hpp", _CSRC + "params.hpp"]
 KERNEL_SOURCES = {
+    "tiny": [_CSRC + "decode.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "huginn_ripe": [_CSRC + "decode.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "ouro_splitk": [_CSRC + "decode.hip", _CSRC + "attn_common.hpp"] + _COMMON,
     "huginn_verify": [_CSRC + "verify.hip"] + _COMMON,
@@ -43,7 +44,7 @@ KERNEL_SOURCES = {
     "dory_lastloop": [_CSRC + "gqa.hip", _CSRC + "attn_common.hpp"] + _COMMON,
 }
 # The timed attention kernel of each workload (rocprofv3 kernel name prefix).
-KERNEL_NAME = {"huginn_ripe": "decode_kernel", "ouro_splitk": "decode_kernel", "huginn_verify": "verify_kernel",
+KERNEL_NAME = {"tiny": "decode_kernel", "huginn_ripe": "decode_kernel", "ouro_splitk": "decode_kernel", "huginn_verify": "verify_kernel",
                "huginn_draft": "decode_kernel",
                "loopkv_cells": "cell_kernel", "raven_ripe": "gqa_decode_kernel", "dory_lastloop": "gqa_decode_kernel"}
 
@@ -66,7 +67,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="huginn_ripe",
                     choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "huginn_draft", "loopkv_cells",
-                             "raven_ripe", "dory_lastloop"])
+                             "raven_ripe", "dory_lastloop", "tiny"])
     ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers held in HBM (0: all)")
     ap.add_argument("--batch", type=int, default=0,

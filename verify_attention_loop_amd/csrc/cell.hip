@@ -313,7 +313,10 @@ __device__ __forceinline__ uint32_t or4(uint32_t v) {
 //     the bucket midpoint 4 hi + 1.5; the per-token V scale and zero fold into the
 //     weight p_j (LoopKV page, Sec. 3.3, App. E Alg. 1).
 // Each DPP row keeps its own online softmax; partials go to the workspace and
-// the LSE merge kernel combines them.
+// the LSE merge kernel combines them.  In the far blocks a page's eight token scores
+// of a row are summed transposed, so that lanes 2t and 2t + 1 hold token t's score:
+// each lane takes one exponential, and the weights and hot bits reach the whole row
+// by lane broadcasts.
 template <int WAVES, bool TRACE, int BITS, bool RUNNING>
 // The kernel is VALU-bound; six waves per SIMD fit the fixed rule in 80 VGPRs and INT2
 // cells (no hot test) seven in 72 (the running rule keeps a page's scores across a barrier
@@ -415,11 +418,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
     constexpr uint64_t vmeta_off = BITS == 4 ? 36 * D : 20 * D;
 
     // Key phase of code page cp: loads, K dequant folded into q (LoopKV page, App. E: the
-    // per-channel scale multiplies the query, the zero becomes a bias), scores of tokens
-    // g + 4i in base-2 units (x2; -inf past the sequence); the V codes and V meta are
-    // loaded here too.  A score is bias + sum_c q'_c c_jc over the lane's 8 channels,
-    // then a 16-lane DPP sum.
-    auto far_keys = [&](int cp, const uint8_t*& hb, float* x2, Raw<16>& vh, Raw<32>& vm) {
+    // per-channel scale multiplies the query, the zero becomes a bias), and the score of
+    // the lane's token g + 4 (li / 2) in base-2 units (xs; -inf past the sequence); the V
+    // codes and V meta are loaded here too.  A score is bias + sum_c q'_c c_jc over the
+    // lane's 8 channels for each of its 8 tokens, then the transposed 16-lane sum.
+    auto far_keys = [&](int cp, const uint8_t*& hb, float& xs, Raw<16>& vh, Raw<32>& vm) {
       hb = p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes;
       // Issue the page's loads together: K meta of the lane's 8 channels, K codes, V hi
       // (or INT2 V codes), V meta.
@@ -450,52 +453,61 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
 #pragma unroll
         for (int c = 0; c < E; ++c) sc[i] = fmaf(qs[c], f[c], sc[i]);
       }
-      // the eight 16-lane sums step by step across tokens, so that consecutive DPP ops
-      // are independent
-      row_sum16_n<8>(sc);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x2[i] = sc[i] * p.scale_log2;
+      // the row sums of the eight tokens, transposed: this lane keeps the score of its own
+      // token li / 2 (base-2 units)
+      xs = row_sum16_t8(sc, li) * p.scale_log2;
       // Past the sequence (last page only): score -inf and V meta cleared, so that those
       // tokens get zero weight against finite scales whatever the page holds there.
       if (cp * kCodePage + kCodePage > n_far) {
+        if (cp * kCodePage + g + 4 * (li >> 1) >= n_far) xs = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (cp * kCodePage + g + 4 * i >= n_far) {
-            x2[i] = -INFINITY;
-            vm.w[i] = 0u;
-          }
+          if (cp * kCodePage + g + 4 * i >= n_far) vm.w[i] = 0u;
       }
     };
 
     // Value phase: hot test against thr2 (base-2 units), online softmax, V lo of hot tokens,
     // V dequant folded into the weights, accumulation.
-    auto far_values = [&](int cp, const uint8_t* hb, float* x2, float thr2, const Raw<16>& vh, const Raw<32>& vm) {
+    auto far_values = [&](int cp, const uint8_t* hb, float xs, float thr2, const Raw<16>& vh, const Raw<32>& vm) {
       // A finite threshold keeps tokens past the sequence (score -inf) cold under any rule,
       // and leaves every finite score hot when the rule's threshold is -inf.
       thr2 = fmaxf(thr2, -3.402823466e38f);  // -FLT_MAX
+      const bool hot_own = masked ? xs >= thr2 : xs > -INFINITY;
+      // online softmax of this row, one token per lane pair: the page maximum over the row,
+      // the lane's own weight, and st.l summing the lane's own weights (the row's sum is
+      // half the sum over its lanes)
+      float mx = fmaxf(xs, dpp<0x4E>(xs));  // lanes 2t and 2t + 1 hold the same token
+      mx = fmaxf(mx, dpp<0x141>(mx));
+      mx = fmaxf(mx, dpp<0x140>(mx));
+      const float mn = fmaxf(st.m, mx);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(st.m - mu);
+      const float p_own = fast_exp2(xs - mu);
+      st.l = fmaf(st.l, alpha, p_own);
+      st.m = mn;
+      // every lane needs the eight weights and hot bits: broadcast from lane 2i of the row,
+      // the hot bit riding in the sign (a cold or absent token, p = 0 included, has it set)
+      const float ps = hot_own ? p_own : -p_own;
       float x[8];
       bool hot[8];
       uint32_t hotbits = 0;
+      {
+        float pb[8];
+        pb[0] = row_bcast<0>(ps);
+        pb[1] = row_bcast<2>(ps);
+        pb[2] = row_bcast<4>(ps);
+        pb[3] = row_bcast<6>(ps);
+        pb[4] = row_bcast<8>(ps);
+        pb[5] = row_bcast<10>(ps);
+        pb[6] = row_bcast<12>(ps);
+        pb[7] = row_bcast<14>(ps);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hot[i] = masked ? x2[i] >= thr2 : x2[i] > -INFINITY;
-        x[i] = x2[i];
-        if (TRACE && hot[i]) hotbits |= 1u << (g + 4 * i);
+        for (int i = 0; i < 8; ++i) {
+          hot[i] = (int32_t)__float_as_uint(pb[i]) >= 0;
+          x[i] = fabsf(pb[i]);
+          if (TRACE && hot[i]) hotbits |= 1u << (g + 4 * i);
+        }
       }
-      // online softmax of this row (x[] becomes p_j)
-      float mn = st.m;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mn = fmaxf(mn, x[i]);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(st.m - mu);
-      float add = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[i] = fast_exp2(x[i] - mu);
-        add += x[i];
-      }
-      st.l = fmaf(st.l, alpha, add);
-      st.m = mn;
 #pragma unroll
       for (int c = 0; c < E; ++c) o[c] *= alpha;
       zacc *= alpha;
@@ -541,11 +553,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
       const float thr2 = (m0 - p.thr_offset) * kLog2e;
       for (int cp = c0 + w; cp < c1; cp += WAVES) {
         const uint8_t* hb;
-        float x2[8];
+        float xs;
         Raw<16> vh;
         Raw<32> vm;
-        far_keys(cp, hb, x2, vh, vm);
-        far_values(cp, hb, x2, thr2, vh, vm);
+        far_keys(cp, hb, xs, vh, vm);
+        far_values(cp, hb, xs, thr2, vh, vm);
       }
     } else {
       // The LoopKV page's rule (App. E Algorithm 1): this far block walks its pages in order
@@ -561,15 +573,15 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
         const int cp = base + w;
         const bool active = cp < c1;  // uniform per wave
         const uint8_t* hb = nullptr;
-        float x2[8];
+        float xs = -INFINITY;
         Raw<16> vh;
         Raw<32> vm;
         float pm = -INFINITY;
         if (active) {
-          far_keys(cp, hb, x2, vh, vm);
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            pm = fmaxf(pm, x2[i]);  // -inf past the sequence
+          far_keys(cp, hb, xs, vh, vm);
+          pm = fmaxf(xs, dpp<0x4E>(xs));  // -inf past the sequence
+          pm = fmaxf(pm, dpp<0x141>(pm));
+          pm = fmaxf(pm, dpp<0x140>(pm));
           pm = fmaxf(pm, __shfl_xor(pm, 16));
           pm = fmaxf(pm, __shfl_xor(pm, 32));
         }
@@ -582,7 +594,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
           if (v <= w) m_page = fmaxf(m_page, pv);
           m_run = fmaxf(m_run, pv);
         }
-        if (active) far_values(cp, hb, x2, fmaxf(m_page, m0_2) - p.v_tau, vh, vm);
+        if (active) far_values(cp, hb, xs, fmaxf(m_page, m0_2) - p.v_tau, vh, vm);
       }
     }
   }
@@ -590,6 +602,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
   if (part != p.n_splits) {
 #pragma unroll
     for (int e = 1; e < E; e += 2) o[e] *= 0.0625f;  // undo the odd channels' scale of 16 (exact)
+    st.l = 0.5f * row_sum16(st.l);  // lanes 2t and 2t + 1 hold equal sums, so this is exact
   }
 
   // merge the 4 * WAVES row states

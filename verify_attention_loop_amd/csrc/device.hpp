@@ -48,18 +48,25 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// row_sum16 of N values, one reduction step at a time across them (the DPP ops of a
-// step are independent, so no wait states sit between them).
+// Eight 16-lane row sums at once, transposed: lane l of a DPP row ends with the row sum of
+// v[l >> 1] (each sum held by two neighbouring lanes).  Each step pairs a lane with one whose
+// index differs in one bit (mirror: bit 3, half mirror: bit 2, xor 2, xor 1), keeps half of
+// its values and adds the partner's other half: 22 VALU ops for the eight sums instead of 32.
+__device__ __forceinline__ float row_sum16_t8(const float* v, int li) {
+  const bool b3 = li & 8, b2 = li & 4, b1 = li & 2;
+  float a[4], c[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) a[k] = (b3 ? v[k + 4] : v[k]) + dpp<0x140>(b3 ? v[k] : v[k + 4]);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) c[k] = (b2 ? a[k + 2] : a[k]) + dpp<0x141>(b2 ? a[k] : a[k + 2]);
+  const float e = (b1 ? c[1] : c[0]) + dpp<0x4E>(b1 ? c[0] : c[1]);
+  return e + dpp<0xB1>(e);
+}
+
+// Value of lane n of the lane's DPP row (row_newbcast).
 template <int N>
-__device__ __forceinline__ void row_sum16_n(float* x) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp<0xB1>(x[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp<0x4E>(x[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp<0x141>(x[i]);
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] += dpp<0x140>(x[i]);
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp<0x150 + N>(x);
 }
 
 __device__ __forceinline__ float row_max16(float x) {

@@ -20,7 +20,7 @@
 //   * each DPP row keeps its own online softmax (m, l, o); rows and waves merge
 //     through LDS at the end, splits through the LSE merge kernel.
 // The plane of a key is chosen per token by address, so a RIPE boundary inside a
-// page costs one extra V quad load on that page only.
+// page costs one extra V quad load and accumulation pass on that page only.
 #include <hip/hip_runtime.h>
 
 #include "attn_common.hpp"
@@ -30,7 +30,28 @@
 
 namespace lkv {
 
-// Seven waves per SIMD fit the multi-head bf16 d = 96 kernel in 72 VGPRs; the hint keeps
+// Clears token k of a quad block where zero[k] (slots whose values must not reach the
+// sum: they may hold NaN, so they are cleared by select, never by a zero weight).
+template <typename T, int D>
+__device__ __forceinline__ void clear_quad(Raw<DecodeTile<T, D>::VB>& a, const bool* zero) {
+  constexpr int E = D / 16;
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a.w[4 * e + k] = zero[k] ? 0u : a.w[4 * e + k];
+  } else {
+    const uint32_t keep01 = (zero[0] ? 0u : 0x0000FFFFu) | (zero[1] ? 0u : 0xFFFF0000u);
+    const uint32_t keep23 = (zero[2] ? 0u : 0x0000FFFFu) | (zero[3] ? 0u : 0xFFFF0000u);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      a.w[2 * e + 0] &= keep01;
+      a.w[2 * e + 1] &= keep23;
+    }
+  }
+}
+
+// Seven waves per SIMD fit the multi-head bf16 d = 96 kernel in 66 VGPRs; the hint keeps
 // the register allocator there.
 template <typename T, int D, int WAVES, bool TRACE, int G>
 __global__ __launch_bounds__(WAVES * 64, (G == 1 && D == 96 && sizeof(T) == 2) ? 7 : 1) void decode_kernel(const PlainParams p) {
@@ -106,32 +127,43 @@ __global__ __launch_bounds__(WAVES * 64, (G == 1 && D == 96 && sizeof(T) == 2) ?
       if constexpr (KB <= 16) load_stream<KB>(kr[i], bp + koff + (uint64_t)(4 * i + g) * (D * ES));
       else load_raw<KB>(kr[i], bp + koff + (uint64_t)(4 * i + g) * (D * ES));
     }
+    // A page that straddles the RIPE window edge (rare, wave-uniform) is accumulated in
+    // two passes over one V register block: the own plane's tokens first, then the
+    // deepest plane's quad loaded into the same registers, so the common path's
+    // register budget carries no second quad.
+    const bool edge = any_own && any_deep;
+    bool take_deep[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) take_deep[k] = edge && pos + 4 * k + g < own_lo;
     Raw<VB> vr;
     load_vquad<T, D>(vr, (any_own ? base_own : base_deep) + voff);
-    if (!full || (any_own && any_deep)) {  // boundary or last page: per-token plane and validity
-      Raw<VB> vd;
-      if (any_own && any_deep) load_vquad<T, D>(vd, base_deep + voff);
-      bool take_deep[4], zero[4];
+    if (!full || edge) {  // edge or last page: clear the tokens this quad does not supply
+      bool zero[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int j = pos + 4 * k + g;
-        take_deep[k] = any_own && any_deep && j < own_lo;
-        zero[k] = j >= n_cached;
-      }
-      blend_quad<T, D>(vr, vd, take_deep, zero);
+      for (int k = 0; k < 4; ++k) zero[k] = take_deep[k] || pos + 4 * k + g >= n_cached;
+      clear_quad<T, D>(vr, zero);
     }
 
+    float x[G][4];
 #pragma unroll
     for (int gq = 0; gq < G; ++gq) {
-      float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = pos + 4 * i + g;
         const float s = row_sum16(partial_dot<T, D>(kr[i], qf[gq], qw[gq])) * p.scale_log2;
-        x[i] = (j < n_cached) ? s : -INFINITY;
+        x[gq][i] = (j < n_cached) ? s : -INFINITY;
       }
-      softmax_step<E, 4>(st[gq], o[gq], x);
-      accum_quad<T, D>(o[gq], vr, x);
+      softmax_step<E, 4>(st[gq], o[gq], x[gq]);
+      accum_quad<T, D>(o[gq], vr, x[gq]);
+    }
+    if (edge) {
+      load_vquad<T, D>(vr, base_deep + voff);
+      bool zero[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) zero[k] = !take_deep[k];
+      clear_quad<T, D>(vr, zero);
+#pragma unroll
+      for (int gq = 0; gq < G; ++gq) accum_quad<T, D>(o[gq], vr, x[gq]);
     }
 
     if constexpr (TRACE) {

@@ -73,6 +73,7 @@ def parse():
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences per call (0: the workload's); other batches report no traffic figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the streaming-read probe")
     ap.add_argument("--event-every", type=int, default=8,
                     help="record HIP events around one launch in this many (rotating over the calls, so every "
                          "(layer, loop) call is sampled); event markers on every launch add ~7%% to the step time")
@@ -163,6 +164,35 @@ def cpu_baseline(w, seconds: float):
             "sample": f"{done} rows ({n_rows} distinct (seq, layer 0, loop, head) rows of the {w.name} workload, "
                       f"L={L}, d={w.head_dim}, repeated) in {elapsed:.1f} s of fp64 oracle time; "
                       f"{rows_per_token} rows = 1 loop-query token"}
+
+
+def read_probe(nbytes: int, reps: int = 10):
+    """Achievable HBM read rate for a launch of nbytes: the library's streaming-read probe (lkv_probe_read:
+    16-byte nontemporal loads, as the page streams use), timed with the same launch-stamped events as the
+    sampled attention launches.  Launch i reads region i mod m of m regions of one buffer, with m regions
+    spanning at least 768 MB, so no launch finds its bytes in the 256 MB Infinity Cache.  Returns
+    (bytes per launch, GB/s)."""
+    import numpy as np
+    import torch
+
+    import verify_attention_loop_amd as vla
+
+    n = max(vla.PROBE_CHUNK, nbytes // vla.PROBE_CHUNK * vla.PROBE_CHUNK)
+    m = max(2, -(-(768 << 20) // n))
+    buf = torch.empty(m * n, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()  # torch creates the underlying HIP event on its first record
+        b.record()
+    for i in range(2):
+        vla.lkv_probe_read(buf[i % m * n:], n, sink)
+    for i, (a, b) in enumerate(evs):
+        vla.lkv_probe_read(buf[(i + 2) % m * n:], n, sink, a.cuda_event, b.cuda_event)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    del buf
+    return n, n / (ms / 1e3) / 1e9
 
 
 def read_traffic(workload: str, khash: str):
@@ -354,6 +384,13 @@ def main():
             torch.mul(af, 1.0, out=bf)  # elementwise kernel: reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
 
+    probe = None
+    if not args.no_probe:
+        pb, pr = read_probe(int(alg_bytes))
+        probe = {"bytes": pb, "GBps": round(pr, 1), "frac": round(achieved / pr, 4)}
+        pb4, pr4 = read_probe(4 << 30)
+        probe.update(GBps_4GiB=round(pr4, 1))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_cells(built, args.cpu_seconds) if w.quant else cpu_baseline(w, args.cpu_seconds)
@@ -402,6 +439,7 @@ def main():
             "algorithmic_bytes_per_launch": int(alg_bytes), "mean_launch_us": round(mean_launch_ms * 1e3, 2),
             "launches_timed": len(sampled),
             "kernel_hash": khash,
+            "read_probe": probe,
         },
         "cpu_baseline": cpu,
     }

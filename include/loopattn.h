@@ -259,6 +259,20 @@ lkv_status lkv_debug_resolve(const lkv_cache* c, int32_t seq, int32_t layer, int
 /* Length and committed length of a sequence. */
 lkv_status lkv_seq_info(const lkv_cache* c, int32_t seq, int32_t* len, int32_t* committed);
 
+/* Measurement aid, not a step of the attention path: one streaming read of
+   `bytes` bytes of device memory at `buf` with the load form the page streams
+   use (16-byte nontemporal loads, each wave instruction covering a whole 1 KB
+   run), on `stream`.  Its rate is the achievable HBM read bandwidth that the
+   attention kernels are compared with.  `bytes` must be a positive multiple of
+   LKV_PROBE_CHUNK (below 2^31 chunks); `sink` is one caller-owned device word
+   that the kernel may overwrite.  ev_begin / ev_end (hipEvent_t, may be NULL)
+   are stamped with the start and end of the kernel's own dispatch, as the
+   attend call's timing events are.  No handle is involved.  Errors: EINVAL
+   (NULL pointer or bad size), EDEVICE (launch failed). */
+#define LKV_PROBE_CHUNK 16384
+lkv_status lkv_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* ev_begin, void* ev_end,
+                          void* stream);
+
 const char* lkv_last_error(const lkv_cache* c);
 const char* lkv_status_str(lkv_status s);
 

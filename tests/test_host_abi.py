@@ -31,6 +31,18 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_probe_read_checks_arguments_before_any_launch(lib):
+    """The read probe refuses NULL pointers and sizes that are not a positive multiple of its chunk, on
+    the host (no device call is made for these)."""
+    assert vla.PROBE_CHUNK == 16384
+    buf, sink = 1 << 40, 1 << 41  # never dereferenced
+    for nbytes in (0, 100, vla.PROBE_CHUNK - 16, vla.PROBE_CHUNK + 16, 3 * vla.PROBE_CHUNK // 2):
+        assert lib.lkv_probe_read(buf, nbytes, sink, 0, 0, 0) == vla.LKV_EINVAL, nbytes
+    assert lib.lkv_probe_read(0, vla.PROBE_CHUNK, sink, 0, 0, 0) == vla.LKV_EINVAL
+    assert lib.lkv_probe_read(buf, vla.PROBE_CHUNK, 0, 0, 0, 0) == vla.LKV_EINVAL
+    assert lib.lkv_probe_read(buf, vla.PROBE_CHUNK << 31, sink, 0, 0, 0) == vla.LKV_EINVAL
+
+
 class HostArenas:
     """Fake device arenas: host buffers whose addresses the host-only calls never read."""
 

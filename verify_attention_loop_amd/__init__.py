@@ -27,7 +27,7 @@ EXPORTS = [
     "lkv_sizes", "lkv_create", "lkv_destroy", "lkv_add_seq", "lkv_free_seq", "lkv_reserve", "lkv_append_plane",
     "lkv_commit", "lkv_truncate", "lkv_set_plan", "lkv_append_coded", "lkv_encode_pages", "lkv_read_coded",
     "lkv_workspace_bytes", "lkv_attend",
-    "lkv_mem_stats", "lkv_debug_resolve", "lkv_seq_info", "lkv_last_error", "lkv_status_str",
+    "lkv_mem_stats", "lkv_debug_resolve", "lkv_seq_info", "lkv_last_error", "lkv_status_str", "lkv_probe_read",
 ]
 
 
@@ -104,6 +104,7 @@ def load():
         "lkv_mem_stats": [vp, P(lkv_mem_info)],
         "lkv_debug_resolve": [vp, i32, i32, i32, i32, i32, i32, i32, P(i32), P(i32), P(i32)],
         "lkv_seq_info": [vp, i32, P(i32), P(i32)],
+        "lkv_probe_read": [vp, ctypes.c_size_t, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -148,6 +149,23 @@ def _stream(stream) -> int:
         import torch
         return torch.cuda.current_stream().cuda_stream
     return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+PROBE_CHUNK = 16384  # LKV_PROBE_CHUNK
+
+
+def lkv_probe_read(buf, nbytes: int, sink, ev_begin=0, ev_end=0, stream=None):
+    """One streaming read of the first nbytes of device tensor buf (a positive multiple of PROBE_CHUNK)
+    on the stream: the achievable HBM read rate that the attention kernels are compared with.  sink is
+    a device tensor of at least one 4-byte word; ev_begin / ev_end are HIP event handles (or 0) that the
+    launch stamps with its own start and end."""
+    _need(buf, "buf", nbytes, None)
+    if buf is not None and not isinstance(buf, int) and buf.numel() * buf.element_size() < nbytes:
+        raise ValueError(f"buf holds {buf.numel() * buf.element_size()} bytes, the call reads {nbytes}")
+    _need(sink, "sink", 1, 4)
+    rc = load().lkv_probe_read(_ptr(buf), nbytes, _ptr(sink), ev_begin or 0, ev_end or 0, _stream(stream))
+    if rc != 0:
+        raise LkvError(rc, f"lkv_probe_read: {load().lkv_status_str(rc).decode()}")
 
 
 class LoopCache:

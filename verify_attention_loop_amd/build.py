@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libloopattn.so")
-SOURCES = ["abi.cpp", "decode.hip", "gqa.hip", "verify.hip", "cell.hip", "copy.hip"]
+SOURCES = ["abi.cpp", "decode.hip", "gqa.hip", "verify.hip", "cell.hip", "copy.hip", "probe.hip"]
 ARCH = os.environ.get("LKV_ARCH", "gfx950")
 
 

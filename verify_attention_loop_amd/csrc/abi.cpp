@@ -35,6 +35,7 @@ hipError_t launch_append(const CopyParams& p, int dtype, int head_dim, hipStream
 hipError_t launch_fill(void* dst, uint64_t n_bytes, uint32_t value, hipStream_t s);
 hipError_t launch_table_write(int32_t* dst, const int32_t* src, int64_t n, hipStream_t s);
 hipError_t launch_cell(const CellParams& p, int head_dim, int waves, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_probe_read(const void* buf, uint64_t bytes, uint32_t* sink, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_pack_codes(const PackParams& p, int head_dim, hipStream_t s);
 hipError_t launch_encode_pages(const EncodeParams& p, int head_dim, hipStream_t s);
 hipError_t launch_read_codes(const PackParams& p, int head_dim, void* k_codes, void* k_meta, void* v_codes,
@@ -1059,6 +1060,17 @@ lkv_status lkv_seq_info(const lkv_cache* c, int32_t seq, int32_t* len, int32_t* 
   *len = c->seqs[(size_t)seq].len;
   *committed = c->seqs[(size_t)seq].committed;
   return LKV_OK;
+}
+
+lkv_status lkv_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* ev_begin, void* ev_end,
+                          void* stream) {
+  if (!buf || !sink) return LKV_EINVAL;
+  if (bytes < LKV_PROBE_CHUNK || bytes % LKV_PROBE_CHUNK != 0 || bytes / LKV_PROBE_CHUNK > 0x7FFFFFFFull)
+    return LKV_EINVAL;
+  LaunchEvents ev;
+  ev.start = (hipEvent_t)ev_begin;
+  ev.stop = (hipEvent_t)ev_end;
+  return launch_probe_read(buf, bytes, sink, (hipStream_t)stream, ev) == hipSuccess ? LKV_OK : LKV_EDEVICE;
 }
 
 }  // extern "C"

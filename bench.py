@@ -166,33 +166,46 @@ def cpu_baseline(w, seconds: float):
                       f"{rows_per_token} rows = 1 loop-query token"}
 
 
-def read_probe(nbytes: int, reps: int = 10):
-    """Achievable HBM read rate for a launch of nbytes: the library's streaming-read probe (lkv_probe_read:
+class ReadProbe:
+    """Achievable HBM read rate of a launch of n bytes: the library's streaming-read probe (lkv_probe_read:
     16-byte nontemporal loads, as the page streams use), timed with the same launch-stamped events as the
-    sampled attention launches.  Launch i reads region i mod m of m regions of one buffer, with m regions
-    spanning at least 768 MB, so no launch finds its bytes in the 256 MB Infinity Cache.  Returns
-    (bytes per launch, GB/s)."""
-    import numpy as np
-    import torch
+    sampled attention launches.  The probe buffer (8 GiB) is allocated before the workload, as a fresh
+    allocation, so its placement does not depend on what the workload allocated and freed.  Launch i reads
+    region i mod m of the buffer, with m regions spanning at least 768 MB where n allows, so no launch finds
+    its bytes in the 256 MB Infinity Cache."""
 
-    import verify_attention_loop_amd as vla
+    TOTAL = 8 << 30
 
-    n = max(vla.PROBE_CHUNK, nbytes // vla.PROBE_CHUNK * vla.PROBE_CHUNK)
-    m = max(2, -(-(768 << 20) // n))
-    buf = torch.empty(m * n, dtype=torch.uint8, device="cuda")
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in evs:
-        a.record()  # torch creates the underlying HIP event on its first record
-        b.record()
-    for i in range(2):
-        vla.lkv_probe_read(buf[i % m * n:], n, sink)
-    for i, (a, b) in enumerate(evs):
-        vla.lkv_probe_read(buf[(i + 2) % m * n:], n, sink, a.cuda_event, b.cuda_event)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-    del buf
-    return n, n / (ms / 1e3) / 1e9
+    def __init__(self):
+        import torch
+
+        self.buf = torch.empty(self.TOTAL, dtype=torch.uint8, device="cuda")
+        self.sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def rate(self, nbytes: int, reps: int = 15):
+        """(bytes per launch, GB/s) for launches of about nbytes (rounded down to the probe's chunk), from the
+        median launch."""
+        import numpy as np
+        import torch
+
+        import verify_attention_loop_amd as vla
+
+        n = min(self.TOTAL // 2, max(vla.PROBE_CHUNK, nbytes // vla.PROBE_CHUNK * vla.PROBE_CHUNK))
+        m = min(self.TOTAL // n, max(2, -(-(768 << 20) // n)), 64)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record()  # torch creates the underlying HIP event on its first record
+            b.record()
+        for i in range(m + 1):  # every region once before timing
+            vla.lkv_probe_read(self.buf[i % m * n:], n, self.sink)
+        for i, (a, b) in enumerate(evs):
+            vla.lkv_probe_read(self.buf[(i + m + 1) % m * n:], n, self.sink, a.cuda_event, b.cuda_event)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        return n, n / (ms / 1e3) / 1e9
+
+    def close(self):
+        del self.buf
 
 
 def read_traffic(workload: str, khash: str):
@@ -259,6 +272,7 @@ def main():
 
     vla.load()
     torch.cuda.set_device(0)
+    prober = None if args.no_probe else ReadProbe()
     w = synth.WORKLOADS[args.workload]
     if args.batch > 0:
         import dataclasses
@@ -385,11 +399,17 @@ def main():
         torch.cuda.synchronize()
 
     probe = None
-    if not args.no_probe:
-        pb, pr = read_probe(int(alg_bytes))
-        probe = {"bytes": pb, "GBps": round(pr, 1), "frac": round(achieved / pr, 4)}
-        pb4, pr4 = read_probe(4 << 30)
-        probe.update(GBps_4GiB=round(pr4, 1))
+    if prober is not None:
+        # the same byte count as the attention launch (none for latency-bound launches under 16 MB, whose
+        # time is the launch itself), and the large-read asymptote
+        # (the 4 GiB reads first: they also bring the clocks back up after the host-side work above)
+        r4 = prober.rate(4 << 30)[1]
+        probe = {"bytes": None, "GBps": None, "frac": None}
+        if alg_bytes >= 16e6:
+            pb, pr = prober.rate(int(alg_bytes))
+            probe = {"bytes": pb, "GBps": round(pr, 1), "frac": round(achieved / pr, 4)}
+        probe.update(GBps_4GiB=round(r4, 1))
+        prober.close()
 
     cpu = None
     if not args.no_cpu_baseline:

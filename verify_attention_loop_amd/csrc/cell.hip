@@ -407,6 +407,12 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
     }
     m0 = fmaxf(m0, __shfl_xor(m0, 16));
     m0 = fmaxf(m0, __shfl_xor(m0, 32));
+    // the key codes of odd channels are converted as 16 times their value (one mask per
+    // nibble parity), so those channels' query entries carry 1/16: exact, and each product
+    // (q / 16) (16 c) equals q c bit for bit
+    float qk[E];
+#pragma unroll
+    for (int c = 0; c < E; ++c) qk[c] = (c & 1) ? qf[c] * 0.0625f : qf[c];  // (the bias sums odd channels apart, times 16)
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
     const int n_cp = (n_far + kCodePage - 1) / kCodePage;
@@ -435,12 +441,14 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
       load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
       // q' = q sigma and bias = q . z; fma with a zero addend so the fp16 operand folds into
       // v_fma_mix_f32 (q sigma is exact in fp32: bf16 x fp16)
-      float qs[E], bias = 0.f;
+      float qs[E], bias_e = 0.f, bias_o = 0.f;
 #pragma unroll
       for (int c = 0; c < E; ++c) {
-        qs[c] = fmaf(qf[c], f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
-        bias = fmaf(qf[c], f16_to_f32(km.w[c] >> 16), bias);
+        qs[c] = fmaf(qk[c], f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
+        if (c & 1) bias_o = fmaf(qk[c], f16_to_f32(km.w[c] >> 16), bias_o);
+        else bias_e = fmaf(qk[c], f16_to_f32(km.w[c] >> 16), bias_e);
       }
+      const float bias = fmaf(bias_o, 16.f, bias_e);
       float sc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -448,7 +456,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
         if constexpr (BITS == 4) code = i < 4 ? k0.w[i] : k1.w[i - 4];
         else code = lo_nibbles((k0.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
         float f[E];
-        nibbles_f32(code, f);
+        nibbles16_f32(code, f);  // odd channels 16 times their code, against q / 16
         sc[i] = bias;
 #pragma unroll
         for (int c = 0; c < E; ++c) sc[i] = fmaf(qs[c], f[c], sc[i]);
@@ -458,7 +466,10 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
       xs = row_sum16_t8(sc, li) * p.scale_log2;
       // Past the sequence (last page only): score -inf and V meta cleared, so that those
       // tokens get zero weight against finite scales whatever the page holds there.
-      if (cp * kCodePage + kCodePage > n_far) {
+      // (tested as "the last code page": the past-the-end tests below imply "the page ends
+      // past the history", so with that test the compiler dropped the branch and ran them on
+      // every page)
+      if (cp == n_cp - 1) {
         if (cp * kCodePage + g + 4 * (li >> 1) >= n_far) xs = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i)

@@ -4,7 +4,8 @@
 // head_dim 128).  Per head, INT4 (40 * D bytes = 160 B per token-head: 4-bit K and
 // V codes plus fp16 scale/zero per 32 elements, LoopKV page App. C):
 //   [0,    4D)  K meta   [channel][scale, zero] fp16, per channel over the page
-//   [4D,  20D)  K codes  4-bit, lane-major: [half][g][li][4 tokens][8 nibbles]
+//   [4D,  20D)  K codes  4-bit, lane-major: [half][g][li][4 slots][8 nibbles]; slot
+//                        i ^ (li >> 1) holds token 4 i + g (kslot)
 //   [20D, 28D)  V hi     2-bit hi = c >> 2, lane-major: [g][li][8 tokens][16 bits]
 //   [28D, 36D)  V lo     2-bit lo = c & 3, token-major: [token][li][16 bits]
 //   [36D, 40D)  V meta   [g][group][8 tokens][scale, zero] fp16, per token and 32 channels
@@ -39,6 +40,10 @@ uint64_t code_page_bytes(int hkv, int head_dim, int bits) {
 __host__ __device__ __forceinline__ int hi_crumb(int c) { return c < 4 ? 2 * c + 1 : 2 * (c - 4); }
 __host__ __device__ __forceinline__ int lo_crumb(int c) { return c < 4 ? 2 * c : 2 * (c - 4) + 1; }
 
+// Key slot of token 4 i + g in lane li's K code words: i ^ (li >> 1), the order in which
+// the transposed 16-lane score sums take a lane's eight tokens without selects.
+__host__ __device__ __forceinline__ int kslot(int i, int li) { return i ^ (li >> 1); }
+
 // Byte offsets inside one head's slice of a code page (d = 128).
 __host__ __device__ constexpr uint64_t code_head_bytes(int bits) { return (uint64_t)(bits == 4 ? 40 : 24) * 128; }
 __host__ __device__ constexpr uint64_t vcode_offset(int bits) { return (bits == 4 ? 20 : 12) * 128; }
@@ -58,7 +63,7 @@ __device__ __forceinline__ void pack_item(uint8_t* hb, int bits, int tok, int li
       vhi |= (uint32_t)((vin[c] >> 2) & 3u) << (2 * hi_crumb(c));
       vlo |= (uint32_t)(vin[c] & 3u) << (2 * lo_crumb(c));
     }
-    const int hh = i >> 2, ii = i & 3;
+    const int ks = kslot(i, li), hh = ks >> 2, ii = ks & 3;
     *reinterpret_cast<uint32_t*>(hb + 4 * D + hh * 1024 + (g * 16 + li) * 16 + ii * 4) = kw;
     *reinterpret_cast<uint16_t*>(hb + 20 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)vhi;
     *reinterpret_cast<uint16_t*>(hb + 28 * D + tok * 32 + li * 2) = (uint16_t)vlo;
@@ -68,7 +73,7 @@ __device__ __forceinline__ void pack_item(uint8_t* hb, int bits, int tok, int li
       kw |= (uint32_t)(kin[c] & 3u) << (2 * lo_crumb(c));
       vw |= (uint32_t)(vin[c] & 3u) << (2 * lo_crumb(c));
     }
-    *reinterpret_cast<uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)kw;
+    *reinterpret_cast<uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + kslot(i, li) * 2) = (uint16_t)kw;
     *reinterpret_cast<uint16_t*>(hb + 12 * D + (g * 16 + li) * 16 + i * 2) = (uint16_t)vw;
   }
   if (li < 4) {
@@ -89,7 +94,7 @@ __device__ __forceinline__ void unpack_item(const uint8_t* hb, int bits, int tok
   constexpr int D = 128;
   const int g = tok & 3, i = tok >> 2;
   if (bits == 4) {
-    const int hh = i >> 2, ii = i & 3;
+    const int ks = kslot(i, li), hh = ks >> 2, ii = ks & 3;
     const uint32_t kw = *reinterpret_cast<const uint32_t*>(hb + 4 * D + hh * 1024 + (g * 16 + li) * 16 + ii * 4);
     const uint32_t vhi = *reinterpret_cast<const uint16_t*>(hb + 20 * D + (g * 16 + li) * 16 + i * 2);
     const uint32_t vlo = *reinterpret_cast<const uint16_t*>(hb + 28 * D + tok * 32 + li * 2);
@@ -98,7 +103,7 @@ __device__ __forceinline__ void unpack_item(const uint8_t* hb, int bits, int tok
       vout[c] = (uint8_t)((((vhi >> (2 * hi_crumb(c))) & 3u) << 2) | ((vlo >> (2 * lo_crumb(c))) & 3u));
     }
   } else {
-    const uint32_t kw = *reinterpret_cast<const uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + i * 2);
+    const uint32_t kw = *reinterpret_cast<const uint16_t*>(hb + 4 * D + (g * 16 + li) * 16 + kslot(i, li) * 2);
     const uint32_t vw = *reinterpret_cast<const uint16_t*>(hb + 12 * D + (g * 16 + li) * 16 + i * 2);
     for (int c = 0; c < 8; ++c) {
       kout[c] = (uint8_t)((kw >> (2 * lo_crumb(c))) & 3u);
@@ -449,7 +454,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
         else bias_e = fmaf(qk[c], f16_to_f32(km.w[c] >> 16), bias_e);
       }
       const float bias = fmaf(bias_o, 16.f, bias_e);
-      float sc[8];
+      float sc[8];  // slot s: the lane's K code word s, token g + 4 (s ^ (li >> 1)) (kslot)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         uint32_t code;
@@ -462,8 +467,8 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
         for (int c = 0; c < E; ++c) sc[i] = fmaf(qs[c], f[c], sc[i]);
       }
       // the row sums of the eight tokens, transposed: this lane keeps the score of its own
-      // token li / 2 (base-2 units)
-      xs = row_sum16_t8(sc, li) * p.scale_log2;
+      // token g + 4 (li / 2) (base-2 units)
+      xs = row_sum16_t8(sc) * p.scale_log2;
       // Past the sequence (last page only): score -inf and V meta cleared, so that those
       // tokens get zero weight against finite scales whatever the page holds there.
       // (tested as "the last code page": the past-the-end tests below imply "the page ends

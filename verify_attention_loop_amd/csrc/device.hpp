@@ -48,18 +48,21 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x;
 }
 
-// Eight 16-lane row sums at once, transposed: lane l of a DPP row ends with the row sum of
-// v[l >> 1] (each sum held by two neighbouring lanes).  Each step pairs a lane with one whose
-// index differs in one bit (mirror: bit 3, half mirror: bit 2, xor 2, xor 1), keeps half of
-// its values and adds the partner's other half: 22 VALU ops for the eight sums instead of 32.
-__device__ __forceinline__ float row_sum16_t8(const float* v, int li) {
-  const bool b3 = li & 8, b2 = li & 4, b1 = li & 2;
+// Eight 16-lane row sums at once, transposed.  Lane l of a DPP row holds in v[s] its
+// partial value of item s ^ (l >> 1) (each lane keeps the eight items in its own order);
+// lane l ends with the row sum of item l >> 1 (each sum held by two neighbouring lanes).
+// Each step pairs a lane with one whose index differs in the next bits (mirror: l and
+// 15 - l; half mirror: l and l ^ 7; quad permute: l ^ 2, then l ^ 1) and adds the
+// partner's partial of the items it keeps; with that order of items the partner's
+// partial sits in the same register in every lane, so the eight sums take 8 DPP adds and
+// no selects.  Every item's partials are paired as in a plain butterfly.
+__device__ __forceinline__ float row_sum16_t8(const float* v) {
   float a[4], c[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) a[k] = (b3 ? v[k + 4] : v[k]) + dpp<0x140>(b3 ? v[k] : v[k + 4]);
+  for (int k = 0; k < 4; ++k) a[k] = v[k] + dpp<0x140>(v[7 - k]);
 #pragma unroll
-  for (int k = 0; k < 2; ++k) c[k] = (b2 ? a[k + 2] : a[k]) + dpp<0x141>(b2 ? a[k] : a[k + 2]);
-  const float e = (b1 ? c[1] : c[0]) + dpp<0x4E>(b1 ? c[0] : c[1]);
+  for (int k = 0; k < 2; ++k) c[k] = a[k] + dpp<0x141>(a[3 - k]);
+  const float e = c[0] + dpp<0x4E>(c[1]);
   return e + dpp<0xB1>(e);
 }
 

@@ -32,16 +32,22 @@
 
 namespace lkv {
 
+// Max and sum over the lanes n, n + 16, n + 32, n + 48 of a query column, on the VALU:
+// the gfx950 permlane swaps hand each lane its own value and its partner row's (lanes l
+// and l ^ 16, then l and l ^ 32), where a shuffle would go through the LDS crossbar.  Each
+// lane adds the same two values as a butterfly would, so sums are unchanged bit for bit.
 __device__ __forceinline__ float xmax4(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ float xsum4(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <typename T, int D, int WAVES, bool TRACE, int G, int NCT>

@@ -265,19 +265,6 @@ __device__ __forceinline__ float ubyte_f32(uint32_t x) {
   return r;
 }
 
-// The eight nibbles of a code word as floats, f[c] = nibble c.
-__device__ __forceinline__ void nibbles_f32(uint32_t code, float* f) {
-  const uint32_t ev = code & 0x0F0F0F0Fu, od = (code >> 4) & 0x0F0F0F0Fu;
-  f[0] = ubyte_f32<0>(ev);
-  f[1] = ubyte_f32<0>(od);
-  f[2] = ubyte_f32<1>(ev);
-  f[3] = ubyte_f32<1>(od);
-  f[4] = ubyte_f32<2>(ev);
-  f[5] = ubyte_f32<2>(od);
-  f[6] = ubyte_f32<3>(ev);
-  f[7] = ubyte_f32<3>(od);
-}
-
 // The eight nibbles of a code word as floats with the odd ones scaled by 16:
 // f[c] = nibble c (c even) or 16 nibble c (c odd), one mask per parity instead of a
 // shift and a mask.  The scale is a power of two, so a product or sum that carries it

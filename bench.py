@@ -166,6 +166,14 @@ def cpu_baseline(w, seconds: float):
                       f"{rows_per_token} rows = 1 loop-query token"}
 
 
+def probe_regions(nbytes: int, total: int, chunk: int):
+    """(n, m): launches of n bytes (nbytes rounded down to the chunk, at least one chunk, at most half the
+    buffer) over m regions of the buffer (m n <= total), with m n >= 768 MB where 64 regions allow it."""
+    n = min(total // 2, max(chunk, nbytes // chunk * chunk))
+    m = min(total // n, max(2, -(-(768 << 20) // n)), 64)
+    return n, m
+
+
 class ReadProbe:
     """Achievable HBM read rate of a launch of n bytes: the library's streaming-read probe (lkv_probe_read:
     16-byte nontemporal loads, as the page streams use), timed with the same launch-stamped events as the
@@ -190,8 +198,7 @@ class ReadProbe:
 
         import verify_attention_loop_amd as vla
 
-        n = min(self.TOTAL // 2, max(vla.PROBE_CHUNK, nbytes // vla.PROBE_CHUNK * vla.PROBE_CHUNK))
-        m = min(self.TOTAL // n, max(2, -(-(768 << 20) // n)), 64)
+        n, m = probe_regions(nbytes, self.TOTAL, vla.PROBE_CHUNK)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in evs:
             a.record()  # torch creates the underlying HIP event on its first record

@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--v-rule", choices=["fixed", "running"], default="fixed",
                     help="quantised cells: the workload's fixed hot rule (s >= m0 - 4) or the running-maximum rule")
     ap.add_argument("--v-tau", type=float, default=14.0, help="tau of the running-maximum rule")
+    ap.add_argument("--v-offset", type=float, default=4.0,
+                    help="fixed rule's offset: a far token is hot iff its score >= m0 - offset (the workload: 4.0)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -323,7 +325,7 @@ def main():
     ws = torch.empty(max(4, ws_bytes), dtype=torch.uint8, device="cuda")
     extra = {}
     if w.quant:
-        extra = {"v_thresh_offset": 4.0}
+        extra = {"v_thresh_offset": args.v_offset}
         if args.v_rule == "running":
             extra = {"v_rule": vla.VRULE_RUNNING, "v_tau": args.v_tau}
 
@@ -337,6 +339,7 @@ def main():
         for b, nf in enumerate(n_far):
             valid[b, 0, :nf] = True
         call_bytes = []
+        cold_total, masked_total = 0, 0  # cold far token-heads of the cells that test hotness
         for c in calls:
             layer, loop, _ = c
             src_layer = layers[layer % len(layers)]
@@ -346,6 +349,9 @@ def main():
                 len(built.seqs), w.n_heads, words * 32).astype(bool)
             n_cold = int((~bits & valid.numpy()).sum())
             call_bytes.append(harness.cell_bytes_per_call(built, src_layer, loop, n_cold))
+            if built.plan[src_layer, loop] != synth.CELL_INT2:
+                cold_total += n_cold
+                masked_total += int(valid.numpy().sum()) * w.n_heads
     elif draft:  # the cached positions and the g draft tokens, once per (seq, KV head)
         call_bytes = [harness.algorithmic_bytes_per_call(w, [L + g for L in built.lengths], 1) for (_, _, g) in calls]
     else:
@@ -393,7 +399,9 @@ def main():
     # achieved = algorithmic bytes of the sampled launches / their summed duration
     achieved = float(sum(call_bytes[n] for (_, n) in sampled)) / (kern.sum() / 1e3) / 1e9
     khash = kernel_hash(args.workload)
-    traffic = read_traffic(args.workload, khash) if args.batch <= 0 else None  # counters: the workload's batch
+    # the counters were taken on the workload as defined: its batch and, for cells, the fixed rule at m0 - 4.0
+    as_profiled = args.batch <= 0 and (not w.quant or (args.v_rule == "fixed" and args.v_offset == 4.0))
+    traffic = read_traffic(args.workload, khash) if as_profiled else None
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -439,8 +447,8 @@ def main():
         cfg.update(draft_passes=passes, draft_loops=d_loops, draft_window=w.extra["draft_window"],
                    draft_block="1..%d tokens from scratch" % passes)
     if w.quant:
-        cfg.update(sink=w.sink, tail=w.tail,
-                   v_thresh="m0 - 4.0" if args.v_rule == "fixed" else f"max(m, m0) - {args.v_tau} ln 2 (running)",
+        cfg.update(sink=w.sink, tail=w.tail, cold_fraction=round(cold_total / max(1, masked_total), 4),
+                   v_thresh=f"m0 - {args.v_offset}" if args.v_rule == "fixed" else f"max(m, m0) - {args.v_tau} ln 2 (running)",
                    plan={k: int((built.plan == v).sum()) for k, v in (("int4", synth.CELL_INT4),
                                                                       ("int2", synth.CELL_INT2),
                                                                       ("shared", synth.CELL_SHARED))})

@@ -399,8 +399,10 @@ def main():
     # achieved = algorithmic bytes of the sampled launches / their summed duration
     achieved = float(sum(call_bytes[n] for (_, n) in sampled)) / (kern.sum() / 1e3) / 1e9
     khash = kernel_hash(args.workload)
-    # the counters were taken on the workload as defined: its batch and, for cells, the fixed rule at m0 - 4.0
-    as_profiled = args.batch <= 0 and (not w.quant or (args.v_rule == "fixed" and args.v_offset == 4.0))
+    # the counters were taken on the workload as defined: its batch, splits and resident layers and, for
+    # cells, the fixed rule at m0 - 4.0
+    as_profiled = (args.batch <= 0 and args.split_k < 0 and args.layers <= 0 and
+                   (not w.quant or (args.v_rule == "fixed" and args.v_offset == 4.0)))
     traffic = read_traffic(args.workload, khash) if as_profiled else None
 
     if args.calibrate_copy:

@@ -160,9 +160,23 @@ def cpu_baseline(w, seconds: float):
         elapsed += time.perf_counter() - t1
         done += n_rows
     rows_per_s = done / elapsed
+    cores = oracle.threads()
+    # the same rows on one core, for about a fifth of the time
+    prev = oracle.set_threads(1)
+    done1, elapsed1 = 0, 0.0
+    try:
+        while elapsed1 < seconds / 5:
+            t1 = time.perf_counter()
+            oracle.attend_rows(q, ko, vo, kd, vd, t, t0, loops, pol, R, window)
+            elapsed1 += time.perf_counter() - t1
+            done1 += n_rows
+    finally:
+        oracle.set_threads(prev)
     rows_per_token = w.n_layers * w.n_heads  # one loop-query token = every layer and head of one (seq, loop)
-    return {"value": rows_per_s / rows_per_token, "unit": "loop-query tokens/s", "cores": oracle.threads(),
+    return {"value": rows_per_s / rows_per_token, "unit": "loop-query tokens/s", "cores": cores,
             "kind": "oracle", "host": host_info(),
+            "one_core": {"value": done1 / elapsed1 / rows_per_token, "seconds": round(elapsed1, 1),
+                         "row_ms": round(1e3 * elapsed1 / done1, 3)},
             "sample": f"{done} rows ({n_rows} distinct (seq, layer 0, loop, head) rows of the {w.name} workload, "
                       f"L={L}, d={w.head_dim}, repeated) in {elapsed:.1f} s of fp64 oracle time; "
                       f"{rows_per_token} rows = 1 loop-query token"}

@@ -91,6 +91,8 @@ def _lib():
         L.oracle_f32_from_f16.restype = ctypes.c_float
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = i32
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_set_threads.restype = i32
         _LIB = L
     return _LIB
 
@@ -113,6 +115,11 @@ def _u8(a):
 def threads() -> int:
     """OpenMP threads the row-parallel oracle routines run on."""
     return int(_lib().oracle_threads())
+
+
+def set_threads(n: int) -> int:
+    """Run the row-parallel routines on n threads from here on; returns the previous setting."""
+    return int(_lib().oracle_set_threads(n))
 
 
 def oracle_plane(policy: int, loop: int, n_loops: int, t: int, t0: int, j: int, window: int) -> int:

@@ -419,3 +419,11 @@ int oracle_threads(void) {
   }
   return n;
 }
+
+/* Sets the threads the row-parallel routines use from here on (for timing them on one
+   core); returns the previous setting.  No arithmetic depends on it. */
+int oracle_set_threads(int n) {
+  const int prev = omp_get_max_threads();
+  omp_set_num_threads(n > 0 ? n : 1);
+  return prev;
+}

@@ -370,3 +370,31 @@ def test_binding_rejects_host_noncontiguous_and_undersized_tensors():
     with pytest.raises(ValueError, match="needs 11"):
         need(FakeDev(10, 2, torch.bfloat16), "q", 11, 2, (torch.bfloat16,))
     need(FakeDev(3, 8, torch.float64), "workspace", 0, None)
+
+
+def test_commit_is_monotone(lib):
+    """RIPE page, Algorithm 1: the window only slides forward.  A commit below the committed length is refused,
+    since the ring pages of positions that left the window were already returned to the pool; after the refusal
+    the cache still holds what it held, and a later forward commit works."""
+    W = 16
+    c = make(n_pages=100, window=W, max_block=8)
+    s = c.lkv_add_seq()
+    c.lkv_reserve(s, 0, 3, 0, 100)
+    c.lkv_commit(s, 100)
+    for p in range(3):
+        c.lkv_reserve(s, 0, p, 100 - W, W)
+    used = c.lkv_mem_stats()["pages_in_use"]
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_commit(s, 50)
+    assert e.value.status == vla.LKV_EINVAL
+    assert c.lkv_seq_info(s) == (100, 100)
+    assert c.lkv_mem_stats()["pages_in_use"] == used
+    # the truncate that could have followed a backwards commit is refused as well (below committed)
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_truncate(s, 60)
+    assert e.value.status == vla.LKV_EINVAL
+    # appending the next position and committing forward still works
+    for p in range(4):
+        c.lkv_reserve(s, 0, p, 100, 1)
+    c.lkv_commit(s, 101)
+    assert c.lkv_seq_info(s) == (101, 101)

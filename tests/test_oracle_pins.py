@@ -510,3 +510,138 @@ def test_running_rule_with_dominant_seed_is_the_fixed_rule():
     kh, vh = _dequant(kc, ks, kz, vc, vs, vz, vc.astype(np.float64))
     kk, vv = _view(k_near, v_near, kh, vh, sink, tail)
     np.testing.assert_allclose(out, _sdpa(q, kk, vv), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- the row-parallel routine
+
+@pytest.mark.parametrize("policy", [oracle.FULL, oracle.RIPE])
+def test_attend_rows_equals_attend_row_bitwise(policy):
+    """The OpenMP row routine (the one the CPU baseline times) is the single-row definition (RIPE page,
+    Sec. 2 policy pi and Eq. (9)) applied row by row: identical bits for rows of mixed query position,
+    block start, loop and window, including W = 0 (the deepest-plane cache) and W >= L (the full cache)."""
+    rng = np.random.default_rng(41)
+    R, L, d = 4, 70, 32
+    n = 12
+    q = rng.standard_normal((n, d))
+    ko, vo, kd, vd = (rng.standard_normal((n, L, d)) for _ in range(4))
+    t = rng.integers(L // 2, L, n).astype(np.int32)
+    t0 = np.array([rng.integers(max(0, ti - 7), ti + 1) for ti in t], dtype=np.int32)
+    loops = rng.integers(0, R, n).astype(np.int32)
+    for W in (0, 7, L + 3):
+        out, lse = oracle.attend_rows(q, ko, vo, kd, vd, t, t0, loops, policy, R, W)
+        for i in range(n):
+            o1, l1 = oracle.attend_row(q[i], ko[i], vo[i], kd[i], vd[i], int(t[i]), int(t0[i]), policy,
+                                       int(loops[i]), R, W)
+            assert np.array_equal(out[i], o1), (W, i)
+            assert lse[i] == l1, (W, i)
+    # and on one thread (the one-core figure) the same bits again
+    prev = oracle.set_threads(1)
+    try:
+        out1, lse1 = oracle.attend_rows(q, ko, vo, kd, vd, t, t0, loops, policy, R, 7)
+    finally:
+        oracle.set_threads(prev)
+    out7, lse7 = oracle.attend_rows(q, ko, vo, kd, vd, t, t0, loops, policy, R, 7)
+    assert np.array_equal(out1, out7) and np.array_equal(lse1, lse7)
+
+
+# ----------------------------------------------------------------------------- cell groups against exact values
+
+def _bf16_round(x):
+    """Round fp64 values to the nearest bf16 (ties to even), returned as float32."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_cell_over_codec_codes_stays_within_the_codec_error_of_exact_attention(bits):
+    """LoopKV page, Sec. 3.1 (KIVI groups of 32: keys per channel over a page's 32 tokens, values per token
+    over 32 channels) and Sec. 3.4 (a page holds 32 tokens of one cell; far pages start after the sink).
+    Exact keys and values are encoded page by page from the far start with the codec, and the cell routine
+    reads the codes with every far token hot.  Position j's value is the unit vector e_j, so output channel j
+    is the softmax weight the routine gave position j, and each weight must lie within the codec's error of
+    the exact attention weight: e^(+-2 delta) (1 +- eps_v) times it, with delta the largest score error the
+    codec's key error allows.  Each far page's keys carry their own offset along q, so a grouping counted
+    from another origin (e.g. position 0 instead of the far start) would dequantise the tokens at a page edge
+    with a neighbour page's zero, move their scores by several units and break the bound."""
+    rng = np.random.default_rng(77)
+    d, sink, tail = 128, 4, 4
+    n_far = 3 * 32 + 11  # three whole pages and a partial last one
+    L = sink + n_far + tail
+    assert L <= d
+    k = rng.standard_normal((L, d)) * 0.5
+    for p in range((n_far + 31) // 32):
+        k[sink + 32 * p: sink + 32 * p + 32] += 1.5 * (p + 1) * (-1) ** p  # per-page offsets
+    v = np.zeros((L, d))
+    v[np.arange(L), np.arange(L)] = 1.0
+    k = _bf16_round(k).astype(np.float64)
+    q = np.full(d, 0.1)
+    n_pg = (n_far + 31) // 32
+    kc = np.zeros((n_far, d), np.uint8)
+    vc = np.zeros((n_far, d), np.uint8)
+    ks, kz = np.zeros((n_pg, d)), np.zeros((n_pg, d))
+    vs, vz = np.zeros((n_far, d // 32)), np.zeros((n_far, d // 32))
+    f16 = np.vectorize(oracle.f32_from_f16)
+    for p in range(n_pg):
+        f0, f1 = 32 * p, min(n_far, 32 * p + 32)
+        a, b = sink + f0, sink + f1
+        c_k, m_k, c_v, m_v = oracle.kivi_encode(k[a:b].astype(np.float32), v[a:b].astype(np.float32), bits)
+        kc[f0:f1], vc[f0:f1] = c_k, c_v
+        ks[p], kz[p] = f16(m_k[:, 0]), f16(m_k[:, 1])
+        vs[f0:f1], vz[f0:f1] = f16(m_v[..., 0]), f16(m_v[..., 1])
+    kind = oracle.CELL_INT2 if bits == 2 else oracle.CELL_INT4
+    out, lse, hot, n_cold = oracle.cell_row(q, k, v, kc, ks, kz, vc, vs, vz, sink, tail, kind, thr_offset=math.inf)
+    assert hot.all() and n_cold == 0
+    s = k @ q / math.sqrt(d)
+    w_exact = np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+    # codec error per element: half a step, plus the fp16 rounding of the group's zero and of its step
+    # (x_hat = z16 + s16 c, c clamped to [0, 2^b - 1])
+    levels = (1 << bits) - 1
+    eps_k = 0.0
+    for p in range(n_pg):
+        grp = k[sink + 32 * p: sink + min(n_far, 32 * p + 32)]
+        mn, mx = grp.min(0), grp.max(0)
+        eps_k = max(eps_k, (ks[p] / 2 + np.abs(kz[p] - mn) + levels * np.abs(ks[p] - (mx - mn) / levels)).max())
+    vg = v[sink:sink + n_far].reshape(n_far, d // 32, 32)
+    mnv, mxv = vg.min(2), vg.max(2)
+    eps_v = (vs / 2 + np.abs(vz - mnv) + levels * np.abs(vs - (mxv - mnv) / levels)).max()
+    delta = np.abs(q).sum() * eps_k / math.sqrt(d)
+    ratio = out[:L] / w_exact
+    lo, hi = (1 - eps_v) * math.exp(-2 * delta), (1 + eps_v) * math.exp(2 * delta)
+    assert ((ratio >= lo) & (ratio <= hi)).all(), (ratio.min(), ratio.max(), lo, hi)
+    assert np.abs(out[L:]).max() == 0.0
+    # a misplaced group moves a page-edge token's score by at least 4.5 * 12.8 / sqrt(128) = 5.1 (the offsets
+    # of neighbouring pages differ by >= 4.5 along q), a weight ratio of e^(+-5.1): outside the bound
+    assert math.log(hi) < 3.0 and math.log(lo) > -3.0
+
+
+def test_cell_groups_start_at_the_far_start_worked_case():
+    """A hand-computed cell whose two far groups have different zeros (LoopKV page, Sec. 3.1 groups of 32
+    counted from the far start, Sec. 3.3 fixed hot rule and bucket midpoint).  sink 4, far 40, tail 1, d 32;
+    q = sqrt(d) e_0.  Every far key code is 1 on channel 0 with scale 1: group 0 (far tokens 0..31) has zero -10
+    and decodes to k_0 = -9, score -9 (cold: below m0 - 4 = -4, with m0 = 0 from zero sink keys); group 1 (far
+    tokens 32..39) has zero 0, decodes to k_0 = 1, score 1 (hot).  A grouping shifted by the sink would give far
+    tokens 28..31 group 1's metadata and make them hot.  Every V code is 5 (hi 1, lo 1) with scale 1 and zero
+    0: hot tokens decode to 5, cold ones to 4 + 1.5 = 5.5; sink and tail values are 0 and the tail key is 0.
+    So out_c = (32 e^-9 5.5 + 8 e^1 5) / (4 + 1 + 32 e^-9 + 8 e) in every channel."""
+    d, sink, tail, n_far = 32, 4, 1, 40
+    L = sink + n_far + tail
+    q = np.zeros(d)
+    q[0] = math.sqrt(d)
+    k_near = np.zeros((L, d))
+    v_near = np.zeros((L, d))
+    kc = np.zeros((n_far, d), np.uint8)
+    kc[:, 0] = 1
+    ks = np.ones((2, d))
+    kz = np.zeros((2, d))
+    kz[0, 0] = -10.0
+    vc = np.full((n_far, d), 5, np.uint8)
+    vs = np.ones((n_far, 1))
+    vz = np.zeros((n_far, 1))
+    out, lse, hot, n_cold = oracle.cell_row(q, k_near, v_near, kc, ks, kz, vc, vs, vz, sink, tail,
+                                            oracle.CELL_INT4, thr_offset=4.0)
+    assert hot.tolist() == [0] * 32 + [1] * 8 and n_cold == 32
+    den = 4 + 1 + 32 * math.exp(-9) + 8 * math.e
+    want = (32 * math.exp(-9) * 5.5 + 8 * math.e * 5) / den
+    np.testing.assert_allclose(out, np.full(d, want), rtol=0, atol=1e-13)
+    assert abs(lse - (1.0 + math.log(den / math.e))) < 1e-13

@@ -453,8 +453,10 @@ lkv_status lkv_commit(lkv_cache* c, int32_t seq, int32_t new_len) {
   if (!c) return LKV_EINVAL;
   if (!c->live(seq)) return c->fail(LKV_EINVAL, "sequence %d is not live", seq);
   auto& S = c->seqs[(size_t)seq];
-  if (new_len < 0 || new_len > S.len)
-    return c->fail(LKV_EINVAL, "commit length %d outside [0, %d]", new_len, S.len);
+  // Commit is monotone: the window slides forward only.  Moving it back would re-open
+  // positions whose ring pages were already returned to the pool.
+  if (new_len < S.committed || new_len > S.len)
+    return c->fail(LKV_EINVAL, "commit length %d outside [committed %d, len %d]", new_len, S.committed, S.len);
   S.committed = new_len;
   const int32_t lo_win = std::max(0, new_len - c->cfg.window);
   for (auto& T : c->tabs) {

@@ -65,6 +65,11 @@ enum { LKV_CELL_BF16 = 0, LKV_CELL_INT4 = 1, LKV_CELL_INT2 = 2, LKV_CELL_SHARED 
    score of the split's pages up to and including p.  Scores are logits in natural
    units (q.k / sqrt(d)); ties are hot. */
 enum { LKV_VRULE_FIXED = 0, LKV_VRULE_RUNNING = 1 };
+/* Kernel choice of an attend call (lkv_attend_args.kernel).  AUTO: q = 1 decode of a
+   grouped-query cache runs on the MFMA tile kernel, everything else on its own kernel.
+   VALU: grouped-query decode on the VALU decode kernel instead (the draft step always
+   runs there). */
+enum { LKV_KERNEL_AUTO = 0, LKV_KERNEL_VALU = 1 };
 
 /* Tokens per plain page and per code page. */
 #define LKV_PAGE_TOKENS 16
@@ -143,6 +148,13 @@ typedef struct {
   /* Quantised cells: hot-test rule (LKV_VRULE_*) and, for RUNNING, tau (the page uses 14). */
   int32_t v_rule;
   float v_tau;
+  /* Launch shape; 0 = the library's default, measured best on MI355X at the workloads'
+     shapes.  Wavefronts per workgroup of the attention kernel: multi-head decode and
+     draft 2, 4 or 8 (default 8, or 4 for grouped-query heads), grouped-query decode tile
+     1, 2 or 4 (default 4), verify 1, 2 or 4 (default 2), quantised cells 2 or 4 (default
+     4).  Any other value is EINVAL.  The results do not depend on it. */
+  int32_t waves;
+  int32_t kernel;            /* LKV_KERNEL_* */
 } lkv_attend_args;
 
 typedef struct {
@@ -176,19 +188,32 @@ lkv_status lkv_free_seq(lkv_cache* c, int32_t seq);
 lkv_status lkv_reserve(lkv_cache* c, int32_t seq, int32_t layer, int32_t plane, int32_t pos0,
                        int32_t n_tok);
 
-/* Write positions [pos0, pos0 + n_tok) of (seq, layer, plane): k and v are device
-   [n_tok][n_heads_kv][head_dim] in kv dtype, caller-owned, read on `stream`.
-   Errors as lkv_reserve, plus EDEVICE. */
+/* Write positions [pos0, pos0 + n_tok) of (seq, layer, plane): the keys and values
+   that loop `plane` of core layer `layer` computed for those positions (RIPE page,
+   Sec. 2: loop r of a core layer writes plane r; Algorithm 1, step 7: the emitted
+   tokens' planes are appended to the cache, and step 5: the block's plane r exists by
+   the time loop r attends).  k and v are device [n_tok][n_heads_kv][head_dim] in kv
+   dtype, caller-owned, read on `stream`; the library copies them into its pages, so
+   the caller may reuse them once the stream passes the call.  Quantised caches take
+   the exact sink and tail positions here (LoopKV page, Sec. 3.2: sink and window stay
+   exact bf16).  Errors as lkv_reserve, plus EDEVICE. */
 lkv_status lkv_append_plane(lkv_cache* c, int32_t seq, int32_t layer, int32_t plane, int32_t pos0,
                             int32_t n_tok, const void* k, const void* v, void* stream);
 
-/* The window slide of the RIPE page (Sec. 4, Algorithm 1): positions < new_len are committed, and
-   the non-deepest planes of positions older than new_len - W are dropped
-   (their window-ring pages return to the pool).  new_len <= length. */
+/* The window slide of the RIPE page (Sec. 4 and Algorithm 1, step 7: drop planes
+   1..R-1 of positions older than W): positions < new_len are committed, and the
+   non-deepest planes of positions older than new_len - W are dropped (their
+   window-ring pages return to the pool).  Commit is monotone: committed <= new_len
+   <= length, else EINVAL (a window moved back would re-open positions whose ring
+   pages are gone).  Quantised caches: host bookkeeping only; the tail's exit is
+   lkv_window_exit. */
 lkv_status lkv_commit(lkv_cache* c, int32_t seq, int32_t new_len);
 
-/* Roll the sequence back to new_len positions (a rejected draft block): pages
-   holding only positions >= new_len return to the pool.  new_len >= committed. */
+/* Roll the sequence back to new_len positions: the rejected tail of a verified block
+   (RIPE page, Algorithm 1, step 6: tokens past the accepted prefix and the verifier's
+   token are not emitted, so step 7 appends nothing for them).  Pages holding only
+   positions >= new_len return to the pool.  committed <= new_len <= length, else
+   EINVAL. */
 lkv_status lkv_truncate(lkv_cache* c, int32_t seq, int32_t new_len);
 
 /* Quantised caches: the kind of every (layer, loop) cell, host int8
@@ -197,7 +222,13 @@ lkv_status lkv_truncate(lkv_cache* c, int32_t seq, int32_t new_len);
 lkv_status lkv_set_plan(lkv_cache* c, const int8_t* kinds);
 
 /* Quantised caches: write far-history code pages [page0, page0 + n_pages) of
-   (seq, layer, loop).  Far page p holds positions sink + 32p .. sink + 32p + 31.
+   (seq, layer, loop), already encoded by the caller ("LoopKV: Loop-Aware KV Cache
+   Compression for Serving Looped Transformers", Sec. 3.1: KIVI-style codes with one
+   fp16 scale and zero per group of 32, keys per channel and values per token;
+   Sec. 3.3: INT4 value codes stored as a hi and a lo bit plane; Sec. 3.4: a page holds
+   32 tokens of one (loop, layer) cell).  Far page p holds positions sink + 32p ..
+   sink + 32p + 31.  The library packs the codes into its page layout.  The cell's
+   encoded far history then extends to the end of page page0 + n_pages - 1.
    Inputs are device arrays in a plain logical layout (the library packs them):
      k_codes [n_pages*32][n_heads_kv][head_dim] uint8, values 0..2^bits-1;
      k_meta  [n_pages][n_heads_kv][head_dim][2] fp16 (scale, zero) per channel
@@ -229,7 +260,9 @@ lkv_status lkv_encode_pages(lkv_cache* c, int32_t seq, int32_t layer, int32_t lo
 
 /* Quantised caches: read code pages back into the logical layout lkv_append_coded
    takes (the inverse of its packing), into caller-owned device buffers of the
-   same shapes.  Errors: EINVAL (arguments, shared cell), ESTATE (page not
+   same shapes: the page contents of LoopKV page Sec. 3.1 and 3.3-3.4 (codes, fp16
+   scale and zero, hi and lo planes merged back into one code), for byte checks of
+   the codec.  Errors: EINVAL (arguments, shared cell), ESTATE (page not
    resident), EDEVICE. */
 lkv_status lkv_read_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0,
                           int32_t n_pages, void* k_codes, void* k_meta, void* v_codes, void* v_meta,
@@ -238,11 +271,21 @@ lkv_status lkv_read_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop
 /* Workspace an attend call needs (0 when it runs unsplit). */
 lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, size_t* bytes);
 
-/* Attention of n_seqs rows at (layer, loop), on `stream`.
-   DECODE (q_len = 1) and VERIFY (q_len = k, causal inside [t0, L)) read the
-   cache; DRAFT reads cached positions < len through the policy with the given
-   window (0 = the deepest plane, the RIPE page's Alg. 1 draft) and the block's
-   positions from draft_k / draft_v.  Quantised caches serve DECODE.
+/* Attention of n_seqs rows at (layer, loop), on `stream`: for query position t,
+   out = softmax(q k_j / sqrt(d)) v over keys j <= t, each key read from the plane
+   the policy names (RIPE page, Sec. 2 policy pi and Eq. (9); positions of the
+   query's own block read plane r, proof of Prop. 1), lse = natural log of the
+   softmax denominator.
+   DECODE (q_len = 1) and VERIFY (q_len = k, causal inside [t0, L); RIPE page,
+   Algorithm 1, step 5: one R-loop pass over the block) read the cache; with
+   W >= k - 1 a verify equals k sequential decodes (Prop. 1).  DRAFT (Algorithm 1,
+   steps 2-4) reads cached positions < len through the policy with the given
+   window (0 = the deepest plane, as the page's drafts read) and the block's
+   positions from draft_k / draft_v.  Quantised caches serve DECODE over their
+   cells (LoopKV page, Sec. 3.1-3.4 and App. E Algorithm 1: exact sink and tail,
+   INT4 / INT2 / shared far history, V lo plane read only for hot tokens).
+   Splits of a row's pages are merged exactly by log-sum-exp (LoopKV page,
+   Sec. 3.4).  Workspace, outputs and traces are caller-owned device memory.
    Errors: EINVAL (arguments), ESTATE (a needed page is missing), ENOMEM
    (workspace too small), EUNSUPPORTED, EDEVICE. */
 lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream);
@@ -251,7 +294,8 @@ lkv_status lkv_mem_stats(const lkv_cache* c, lkv_mem_info* out);
 
 /* Host index function: the plane, physical page and slot that the row at
    position t of a block starting at t0 reads for key j (window -1 = cache
-   default).  -1 for a page that is not resident. */
+   default), by RIPE page Sec. 2 policy pi and Eq. (9) with the block rule of the
+   proof of Prop. 1.  -1 for a page that is not resident. */
 lkv_status lkv_debug_resolve(const lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t t,
                              int32_t t0, int32_t j, int32_t window, int32_t* plane,
                              int32_t* phys_page, int32_t* slot);

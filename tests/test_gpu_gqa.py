@@ -1,6 +1,6 @@
 """Grouped-query attention through the C-ABI against the fp64 oracle: a workgroup serves the G query heads of a
 KV head from one stream of its pages (G = 2, 4, 8); query head h reads KV head h // G.  Decode runs on the MFMA
-tile kernel (G columns) and, with LKV_GQA_VALU=1, on the VALU decode kernel; verify blocks whose k G fits the
+tile kernel (G columns) and, with the kernel choice LKV_KERNEL_VALU, on the VALU decode kernel; verify blocks whose k G fits the
 tile's 16 columns share the tile too.  Draft runs on the same caches.  Tolerances as for multi-head caches:
 1e-5 (fp32), 2e-2 (bf16)."""
 import numpy as np
@@ -45,8 +45,8 @@ def _attend(built, layer, loop, q, split_k, mode=vla.MODE_DECODE, trace_len=0, *
 @pytest.mark.parametrize("D,dt,tol", [(64, synth.DT_F32, 1e-5), (128, synth.DT_BF16, 2e-2), (96, synth.DT_BF16, 2e-2),
                                       (256, synth.DT_BF16, 2e-2)])
 @pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 20)])
-def test_gqa_decode_every_row(G, D, dt, tol, policy, W, kernel, monkeypatch):
-    monkeypatch.setenv("LKV_GQA_VALU", "1" if kernel == "valu" else "0")
+def test_gqa_decode_every_row(G, D, dt, tol, policy, W, kernel):
+    kern = vla.KERNEL_VALU if kernel == "valu" else vla.KERNEL_AUTO
     w = _wl(D, G, dt, scale=0.25 if dt == synth.DT_F32 else 1.0)
     lengths = [1, 17, 100, 300]
     built = harness.build_plain(w, lengths=lengths, policy=policy, window=W, shuffle=True, poison=True)
@@ -55,7 +55,7 @@ def test_gqa_decode_every_row(G, D, dt, tol, policy, W, kernel, monkeypatch):
         want, want_lse = harness.oracle_rows(w, rows, 0, loop, lengths, 1, policy, W)
         q = harness.gpu_queries(built, 0, loop, 1)
         for split_k in (1, 3):
-            o, lse, tr = _attend(built, 0, loop, q, split_k, trace_len=300)
+            o, lse, tr = _attend(built, 0, loop, q, split_k, trace_len=300, kernel=kern)
             got = o[:, 0].reshape(-1, D)
             assert np.isfinite(got).all()
             assert np.abs(got - want).max() <= tol, (loop, split_k)

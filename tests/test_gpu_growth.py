@@ -89,7 +89,7 @@ def _build(lengths, hq, hkv, d, q_len, policy, W, ks, vs):
     return cache, seqs
 
 
-def _check(lengths, hq, hkv, d, q_len, policy, W, mode, split_ks, seed):
+def _check(lengths, hq, hkv, d, q_len, policy, W, mode, split_ks, seed, kernel=vla.KERNEL_AUTO):
     ks, vs, qs = _inputs(seed, lengths, hq, hkv, d, q_len)
     cache, seqs = _build(lengths, hq, hkv, d, q_len, policy, W, ks, vs)
     G = hq // hkv
@@ -110,7 +110,8 @@ def _check(lengths, hq, hkv, d, q_len, policy, W, mode, split_ks, seed):
         lse = torch.empty((len(lengths), q_len, hq), dtype=torch.float32, device="cuda")
         wsb = cache.lkv_workspace_bytes(0, 0, seqs, q_len=q_len, mode=mode, split_k=split_k)
         ws = torch.empty(max(4, wsb), dtype=torch.uint8, device="cuda")
-        cache.lkv_attend(0, 0, seqs, q, out, q_len=q_len, mode=mode, split_k=split_k, lse=lse, workspace=ws)
+        cache.lkv_attend(0, 0, seqs, q, out, q_len=q_len, mode=mode, split_k=split_k, lse=lse, workspace=ws,
+                         kernel=kernel)
         torch.cuda.synchronize()
         got = harness.out_f64(out)
         assert np.isfinite(got).all()
@@ -129,11 +130,11 @@ def test_verify_with_growing_scores(policy, W, hq, hkv, d):
 @pytest.mark.parametrize("kernel", ["tile", "valu"])
 @pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 20)])
 @pytest.mark.parametrize("G,d", [(4, 64), (8, 128), (4, 256)])
-def test_grouped_decode_with_growing_scores(policy, W, G, d, kernel, monkeypatch):
+def test_grouped_decode_with_growing_scores(policy, W, G, d, kernel):
     """q = 1 on a grouped-query cache: the MFMA tile kernel (G columns; two page buffers up to d = 128, one at
     d = 256) and the VALU decode kernel."""
-    monkeypatch.setenv("LKV_GQA_VALU", "1" if kernel == "valu" else "0")
-    _check([1, 97, 300], 2 * G, 2, d, 1, policy, W, vla.MODE_DECODE, (1, 3), seed=12)
+    _check([1, 97, 300], 2 * G, 2, d, 1, policy, W, vla.MODE_DECODE, (1, 3), seed=12,
+           kernel=vla.KERNEL_VALU if kernel == "valu" else vla.KERNEL_AUTO)
 
 
 @pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 20)])

@@ -65,8 +65,9 @@ def test_normal_moments_and_range():
     assert np.abs(n).max() <= 6.0
 
 
-def test_ripening_noise_shrinks_toward_the_deepest_plane():
-    """Huginn-shaped planes: plane r - plane R has standard deviation 0.88^(R-1-r)."""
+def test_ripening_noise_grows_with_the_loop_index():
+    """Huginn-shaped planes, the workload's literal formula: plane r - plane R has standard deviation
+    0.88^(R-1-r), which grows with r (0.019 at r = 0, 0.88 at r = R - 2)."""
     R = 32
     deep = synth.f32_from_bf16(synth.kv(synth.DT_BF16, 0, synth.T_K, 0, 0, R - 1, 2, 96, 0, 512, synth.MODE_RIPEN,
                                         R)).astype(np.float64)

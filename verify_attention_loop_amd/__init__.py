@@ -21,6 +21,7 @@ POLICY_FULL, POLICY_RIPE = 0, 1
 MODE_DECODE, MODE_VERIFY, MODE_DRAFT = 0, 1, 2
 CELL_BF16, CELL_INT4, CELL_INT2, CELL_SHARED = 0, 1, 2, 3
 VRULE_FIXED, VRULE_RUNNING = 0, 1
+KERNEL_AUTO, KERNEL_VALU = 0, 1
 PAGE_TOKENS, CODE_PAGE_TOKENS = 16, 32
 
 EXPORTS = [
@@ -58,7 +59,8 @@ class lkv_attend_args(ctypes.Structure):
                 ("draft_k", ctypes.c_void_p), ("draft_v", ctypes.c_void_p), ("draft_len", ctypes.c_int32),
                 ("index_trace", ctypes.c_void_p), ("trace_len", ctypes.c_int32), ("mask_trace", ctypes.c_void_p),
                 ("ev_begin", ctypes.c_void_p), ("ev_end", ctypes.c_void_p),
-                ("v_rule", ctypes.c_int32), ("v_tau", ctypes.c_float)]
+                ("v_rule", ctypes.c_int32), ("v_tau", ctypes.c_float),
+                ("waves", ctypes.c_int32), ("kernel", ctypes.c_int32)]
 
 
 class lkv_mem_info(ctypes.Structure):
@@ -299,7 +301,7 @@ class LoopCache:
     def _args(self, layer, loop, seq_ids, q, out, q_len=1, mode=MODE_DECODE, window=-1, split_k=0,
               v_thresh_offset=4.0, lse=None, workspace=None, draft_k=None, draft_v=None, draft_len=0,
               index_trace=None, trace_len=0, mask_trace=None, ev_begin=None, ev_end=None, v_rule=VRULE_FIXED,
-              v_tau=14.0):
+              v_tau=14.0, waves=0, kernel=KERNEL_AUTO):
         ids = (ctypes.c_int32 * len(seq_ids))(*seq_ids)
         a = lkv_attend_args()
         a.layer, a.loop, a.n_seqs, a.seq_ids = layer, loop, len(seq_ids), ids
@@ -312,6 +314,7 @@ class LoopCache:
         a.ev_begin = ev_begin or 0
         a.ev_end = ev_end or 0
         a.v_rule, a.v_tau = v_rule, v_tau
+        a.waves, a.kernel = waves, kernel
         return a, ids
 
     def lkv_workspace_bytes(self, layer, loop, seq_ids, q_len=1, mode=MODE_DECODE, split_k=0) -> int:

@@ -196,11 +196,6 @@ lkv_status hip_fail(lkv_cache* c, hipError_t e, const char* what) {
   return c->fail(LKV_EDEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v ? atoi(v) : dflt;
-}
-
 }  // namespace
 
 extern "C" {
@@ -733,6 +728,11 @@ LaunchEvents launch_events(const lkv_attend_args* a, bool first, bool last) {
   return ev;
 }
 
+// Workgroups an automatic split count aims at: eight per CU of the 256-CU MI355X, and two
+// per CU for grouped-query decode.
+constexpr int kTargetWgs = 2048;
+constexpr int kGqaTargetWgs = 512;
+
 // Splits of a plain-cache call: enough workgroups to fill the chip.  Decode and draft
 // workgroups serve all query heads of one KV head; verify workgroups the query heads of
 // one KV head when the block's rows fit one or two 16-column tiles, else one query head.
@@ -744,7 +744,7 @@ int auto_splits(const lkv_cache* c, int n_seqs, int mode, int q_len, int max_pag
   const int rows =
       n_seqs * (mode == LKV_MODE_VERIFY ? hq / verify_heads_per_wg(hq, hkv, std::max(1, q_len), c->cfg.head_dim) : hkv);
   const bool gqa = mode == LKV_MODE_DECODE && hq > hkv;
-  const int target = gqa ? env_int("LKV_GQA_TARGET_WGS", 512) : env_int("LKV_TARGET_WGS", 2048);
+  const int target = gqa ? kGqaTargetWgs : kTargetWgs;
   int s = (target + rows - 1) / rows;
   s = std::min(s, std::max(1, max_pages / 8));
   return std::max(1, std::min(s, 64));
@@ -754,7 +754,7 @@ int auto_splits(const lkv_cache* c, int n_seqs, int mode, int q_len, int max_pag
 // chip, at most one per code page and at most 64.
 int cell_splits(const lkv_cache* c, int n_seqs, int split_k, int max_code_pages) {
   const int rows = n_seqs * c->cfg.n_heads_q;
-  int S = split_k > 0 ? split_k : std::max(1, std::min(64, (env_int("LKV_TARGET_WGS", 2048) + rows - 1) / rows));
+  int S = split_k > 0 ? split_k : std::max(1, std::min(64, (kTargetWgs + rows - 1) / rows));
   return std::min(S, std::max(1, max_code_pages));
 }
 
@@ -809,9 +809,27 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
   if (a->v_rule != LKV_VRULE_FIXED && a->v_rule != LKV_VRULE_RUNNING)
     return c->fail(LKV_EINVAL, "v_rule %d", a->v_rule);
   if (a->v_rule == LKV_VRULE_RUNNING && !(a->v_tau >= 0.f)) return c->fail(LKV_EINVAL, "v_tau must be >= 0");
+  if (a->kernel != LKV_KERNEL_AUTO && a->kernel != LKV_KERNEL_VALU) return c->fail(LKV_EINVAL, "kernel %d", a->kernel);
+  if (a->waves < 0) return c->fail(LKV_EINVAL, "waves %d", a->waves);
   hipStream_t s = (hipStream_t)stream;
   if (cfg.quant) return attend_cell(c, a, s);
 
+  // q = 1 decode of a grouped-query cache runs on the MFMA kernel (its G query heads are
+  // G columns of one tile); multi-head decode and the draft on the VALU decode kernel.
+  const int group = cfg.n_heads_q / cfg.n_heads_kv;
+  const bool gqa = a->mode == LKV_MODE_DECODE && (group == 2 || group == 4 || group == 8) &&
+                   a->kernel == LKV_KERNEL_AUTO;
+  // Waves per workgroup (defaults measured best on MI355X at the workloads' shapes): 8 for
+  // multi-head q = 1 rows, 4 for grouped-query rows (and the grouped VALU kernel, whose
+  // registers grow with G), 2 for verify tiles.
+  const int waves = a->waves > 0 ? a->waves
+                    : a->mode == LKV_MODE_VERIFY ? 2
+                    : gqa                        ? 4
+                                                 : (group == 1 ? 8 : 4);
+  const bool waves_ok = a->mode == LKV_MODE_VERIFY ? (waves == 1 || waves == 2 || waves == 4)
+                        : gqa                      ? (waves == 1 || waves == 2 || waves == 4)
+                                                   : (waves == 2 || waves == 4 || waves == 8);
+  if (!waves_ok) return c->fail(LKV_EINVAL, "waves %d is not built for this kernel", waves);
   const int window = a->window < 0 ? cfg.window : a->window;
   const int R = cfg.n_loops;
   const bool ripe = cfg.policy == LKV_POLICY_RIPE && a->loop != R - 1;
@@ -837,17 +855,6 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
     hipError_t e = launch_fill(a->index_trace, (uint64_t)a->n_seqs * a->q_len * a->trace_len * 8, 0xFFFFFFFFu, s);
     if (e != hipSuccess) return hip_fail(c, e, "trace clear");
   }
-  // q = 1 decode of a grouped-query cache runs on the MFMA kernel (its G query heads are
-  // G columns of one tile); multi-head decode and the draft on the VALU decode kernel.
-  const int group = hq / cfg.n_heads_kv;
-  const bool gqa = a->mode == LKV_MODE_DECODE && (group == 2 || group == 4 || group == 8) &&
-                   env_int("LKV_GQA_VALU", 0) == 0;
-  // Waves per workgroup (measured best on MI355X at the workloads' shapes; the environment
-  // can override for experiments): 8 for multi-head q = 1 rows, 4 for grouped-query rows
-  // (and the grouped VALU kernel, whose registers grow with G), 2 for verify tiles.
-  const int waves = a->mode == LKV_MODE_VERIFY ? env_int("LKV_VERIFY_WAVES", 2)
-                    : gqa                     ? env_int("LKV_GQA_WAVES", 4)
-                                              : env_int("LKV_WAVES", group == 1 ? 8 : 4);
   const int64_t qrow = (int64_t)a->q_len * hq * D;
   for (int b0 = 0; b0 < a->n_seqs; b0 += kMaxRows) {
     const int nb = std::min(kMaxRows, a->n_seqs - b0);
@@ -907,6 +914,8 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
 static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_t s) {
   const auto& cfg = c->cfg;
   if (a->mode != LKV_MODE_DECODE) return c->fail(LKV_EUNSUPPORTED, "quantised cells serve decode only");
+  const int waves = a->waves > 0 ? a->waves : 4;
+  if (waves != 2 && waves != 4) return c->fail(LKV_EINVAL, "waves %d is not built for the cell kernel", waves);
   if (!c->plan_set) return c->fail(LKV_ESTATE, "lkv_set_plan first");
   const int R = cfg.n_loops;
   const int8_t kind = c->plan[(size_t)a->layer * R + a->loop];
@@ -954,7 +963,6 @@ static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_
     hipError_t e = launch_fill(a->mask_trace, (uint64_t)a->n_seqs * hq * mask_words * 4, 0u, s);
     if (e != hipSuccess) return hip_fail(c, e, "mask clear");
   }
-  const int waves = env_int("LKV_CELL_WAVES", 4);
   for (int b0 = 0; b0 < a->n_seqs; b0 += kMaxRows) {
     const int nb = std::min(kMaxRows, a->n_seqs - b0);
     CellParams P{};

@@ -145,9 +145,18 @@ __global__ __launch_bounds__(WAVES * 64) void verify_kernel(const PlainParams p)
       for (int s = 0; s < NB; ++s) load_stream<16>(kst[s], base + kslice + (s * 64 + lane) * 16);
 #pragma unroll
       for (int s = 0; s < NB; ++s) load_stream<16>(vr[s], base + voff + s * VSTEP);
+      // The slice is shared by the lanes of one wave: other lanes' reads of the previous
+      // page must be done before it is overwritten, and its stores visible before it is
+      // read (wavefront-scope fences around a wave barrier; no workgroup barrier needed).
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int s = 0; s < NB; ++s)
         *reinterpret_cast<u32x4_t*>(&sm_k[w][(s * 64 + lane) * 16]) = u32x4_t{kst[s].w[0], kst[s].w[1], kst[s].w[2], kst[s].w[3]};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int s = 0; s < NB; ++s) {
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&sm_k[w][kl + s * KSTEP]);

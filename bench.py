@@ -1,17 +1,19 @@
 """Benchmark: loop-query tokens/s of loop-aware attention on one MI355X.
 
-Default workload: Huginn-shaped RIPE decode (32 sequences, 4 core layers x 32
-loops, 55 heads x 96, bf16, context 1024, window 64, 16-token pages).  One step
-runs every core layer at every loop as its own attention call, loop-major, as a
-looped model's sequential loops require; it yields batch * q * loops
-loop-query tokens.  Inputs are resident in HBM before timing starts.
+Default workload: the largest single-GPU configuration, Ouro-shaped paged decode with
+split-K (32 sequences, 24 core layers x 4 loops, 16 heads x 128, bf16, context 8192,
+16-token pages behind shuffled block tables, 8 splits merged by log-sum-exp; all 96
+(layer, loop) planes resident, 206 GB).  One step runs every core layer at every loop
+as its own attention call, loop-major, as a looped model's sequential loops require;
+it yields batch * q * loops loop-query tokens.  Inputs are resident in HBM before
+timing starts.
 
 Prints one JSON line with the throughput, the roofline of the attention kernel
 (algorithmic bytes per launch / mean launch time from HIP events recorded
 around each launch on the launch stream) and the fp64 oracle's throughput on a
 bounded sample of the same workload on the host cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload huginn_ripe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ouro_splitk] [--policy full|ripe]
 """
 from __future__ import annotations
 
@@ -65,10 +67,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="huginn_ripe",
+    ap.add_argument("--workload", default="ouro_splitk",
                     choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "huginn_draft", "loopkv_cells",
                              "raven_ripe", "dory_lastloop", "tiny"])
     ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
+    ap.add_argument("--policy", choices=["default", "full", "ripe"], default="default",
+                    help="cache policy of a plain workload (default: the workload's own; the verify configuration "
+                         "names both the full-depth cache and the RIPE window)")
     ap.add_argument("--layers", type=int, default=0, help="distinct layers held in HBM (0: all)")
     ap.add_argument("--batch", type=int, default=0,
                     help="sequences per call (0: the workload's); other batches report no traffic figure")
@@ -297,9 +302,11 @@ def main():
     torch.cuda.set_device(0)
     prober = None if args.no_probe else ReadProbe()
     w = synth.WORKLOADS[args.workload]
+    import dataclasses
     if args.batch > 0:
-        import dataclasses
         w = dataclasses.replace(w, batch=args.batch)
+    if args.policy != "default" and not w.quant and args.policy != w.policy:
+        w = dataclasses.replace(w, policy=args.policy, window=w.window if args.policy == "ripe" else 0)
     t_setup = time.perf_counter()
     R, B, q_len = w.n_loops, w.batch, w.q_len
     split = w.split_k if args.split_k < 0 else args.split_k
@@ -417,7 +424,8 @@ def main():
     # cells, the fixed rule at m0 - 4.0
     as_profiled = (args.batch <= 0 and args.split_k < 0 and args.layers <= 0 and
                    (not w.quant or (args.v_rule == "fixed" and args.v_offset == 4.0)))
-    traffic = read_traffic(args.workload, khash) if as_profiled else None
+    policy_tag = "" if w.policy == synth.WORKLOADS[args.workload].policy else "_" + w.policy
+    traffic = read_traffic(args.workload + policy_tag, khash) if as_profiled else None
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -457,8 +465,7 @@ def main():
            "kv_heads": w.hkv,
            "head_dim": w.head_dim, "context": w.length, "q_len": q_len, "policy": w.policy, "window": w.window,
            "page_tokens": 32 if w.quant else 16, "split_k": split, "calls_per_step": len(calls),
-           "layers_resident": len(layers), "kernel_ms_per_step": round(mean_launch_ms * len(calls), 4),
-           "setup_s": round(setup_s, 1)}
+           "layers_resident": len(layers), "setup_s": round(setup_s, 1)}
     if draft:
         cfg.update(draft_passes=passes, draft_loops=d_loops, draft_window=w.extra["draft_window"],
                    draft_block="1..%d tokens from scratch" % passes)
@@ -489,6 +496,12 @@ def main():
             "kernel": kernel,
             "algorithmic_bytes_per_launch": int(alg_bytes), "mean_launch_us": round(mean_launch_ms * 1e3, 2),
             "launches_timed": len(sampled),
+            # whole-step rate: every call's algorithmic bytes over the wall time of the step (launch gaps, merge
+            # launches and host issue included), a lower bound of the kernels' own rate
+            "step_GBps": round(float(sum(call_bytes)) / (ms_per_step / 1e3) / 1e9, 1),
+            # the sampled launches' event durations scaled to a step; the launch-stamped events run ~1 us per launch
+            # longer than the kernel trace (rocprofv3), so for back-to-back launches this can exceed ms_per_step
+            "event_ms_per_step": round(mean_launch_ms * len(calls), 4),
             "kernel_hash": khash,
             "read_probe": probe,
         },

@@ -378,27 +378,29 @@ class SpecLoop:
     """A synthetic run of the RIPE page's self-speculative step (Sec. 4, Algorithm 1) through the C-ABI.
 
     The cache holds positions [0, len) of each sequence; the next block starts with the last emitted token x at
-    position len.  One step: gamma draft passes (q = 1 at loops 0..d-1, cached positions read plane R, the block
-    from caller scratch), one verify pass over the block of gamma + 1 tokens at every loop (the block's plane r is
-    appended before loop r attends), then a seeded acceptance of a in [0, gamma] drafts: the planes of x and the
-    accepted drafts stay (commit to len + 1 + a, which also drops non-deepest planes that left the window) and
-    the rest is truncated.  Keys and values of position j are generated with a per-position version that grows
-    every time the position is written again, so a truncated and rewritten position holds new values.  There are
-    no logits: acceptance is drawn, and the attention outputs are what the caller checks."""
+    position len.  One step of block length gamma (drawn per step by the caller, 1 <= gamma <= max_gamma): gamma
+    draft passes (q = 1 at loops 0..d-1, cached positions read plane R, the block from caller scratch), one verify
+    pass over the block of gamma + 1 tokens at every loop (the block's plane r is appended before loop r
+    attends), then a seeded acceptance of a in [0, gamma] drafts: the planes of x and the accepted drafts stay
+    (commit to len + 1 + a, which also drops non-deepest planes that left the window) and the rest is truncated.
+    Keys and values of position j are generated with a per-position version that grows every time the position
+    is written again, so a truncated and rewritten position holds new values.  There are no logits: acceptance
+    is drawn, and the attention outputs are what the caller checks."""
 
-    def __init__(self, w: synth.Workload, prefix_lengths, gamma: int, d: int, window: int, seed: int = 0):
+    def __init__(self, w: synth.Workload, prefix_lengths, max_gamma: int, d: int, window: int, seed: int = 0):
         import torch
-        self.w, self.gamma, self.d, self.W = w, gamma, d, window
-        self.k = gamma + 1
+        self.w, self.max_gamma, self.d, self.W = w, max_gamma, d, window
+        self.max_block = max_gamma + 1
         self.rng = np.random.default_rng(seed)
         R, H, D = w.n_loops, w.hkv, w.head_dim
-        max_len = max(prefix_lengths) + 64 * self.k
+        max_len = max(prefix_lengths) + 64 * self.max_block
         self.max_len = max_len
         cfg = vla.LoopCache.config(n_layers=w.n_layers, n_loops=R, n_heads_q=w.n_heads, n_heads_kv=H, head_dim=D,
                                    kv_dtype=w.dtype, policy=vla.POLICY_RIPE, window=window,
-                                   max_seqs=len(prefix_lengths), max_len=max_len, max_block=self.k, poison=1,
+                                   max_seqs=len(prefix_lengths), max_len=max_len, max_block=self.max_block, poison=1,
                                    shuffle_seed=0x5EED + seed)
-        n_pages = len(prefix_lengths) * w.n_layers * ((max_len + 15) // 16 + (R - 1) * ((window + self.k) // 16 + 2))
+        n_pages = len(prefix_lengths) * w.n_layers * ((max_len + 15) // 16 +
+                                                      (R - 1) * ((window + self.max_block) // 16 + 2))
         self.cache = vla.LoopCache.on_device(cfg, n_pages)
         self.version = [np.zeros(max_len, dtype=np.int64) for _ in prefix_lengths]
         self.seqs = [self.cache.lkv_add_seq() for _ in prefix_lengths]
@@ -412,6 +414,10 @@ class SpecLoop:
                     a = max(0, L - window)
                     self._append(b, layer, plane, a, L - a)
         torch.cuda.synchronize()
+
+    def draw_gamma(self, lo: int = 1, hi: int = 0) -> int:
+        """A block length for the next step, uniform in [lo, hi] (hi = max_gamma by default), seeded."""
+        return int(self.rng.integers(lo, (hi or self.max_gamma) + 1))
 
     # generator coordinates of (seq b, position j): one row per (b, version)
     def _row(self, b, j):
@@ -481,10 +487,12 @@ class SpecLoop:
                 res[(layer, loop)] = (out, dk, dv)
         return res
 
-    def verify_pass(self):
-        """Append the block's planes and verify at every (layer, loop); returns {(layer, loop): out}."""
+    def verify_pass(self, gamma: int):
+        """Append the planes of a block of gamma + 1 tokens and verify at every (layer, loop); returns
+        {(layer, loop): out}."""
         import torch
-        w, k = self.w, self.k
+        assert 1 <= gamma <= self.max_gamma
+        w, k = self.w, gamma + 1
         outs = {}
         for loop in range(w.n_loops):
             for layer in range(w.n_layers):
@@ -501,12 +509,13 @@ class SpecLoop:
         self.lengths = [L + k for L in self.lengths]
         return outs
 
-    def accept(self):
-        """Seeded acceptance: keep x and a in [0, gamma] drafts of each sequence, drop the rest."""
+    def accept(self, gamma: int):
+        """Seeded acceptance after a verified block of gamma + 1 tokens: keep x and a in [0, gamma] drafts of each
+        sequence, drop the rest."""
         accepted = []
         for b, L in enumerate(self.lengths):
-            a = int(self.rng.integers(0, self.gamma + 1))
-            new_len = L - self.k + 1 + a
+            a = int(self.rng.integers(0, gamma + 1))
+            new_len = L - (gamma + 1) + 1 + a
             self.cache.lkv_commit(self.seqs[b], new_len)
             self.cache.lkv_truncate(self.seqs[b], new_len)
             self.version[b][new_len:] += 1  # positions past the accepted prefix get new values when rewritten

@@ -156,20 +156,32 @@ def test_split_k_merge_matches_unsplit_fp32():
 @pytest.mark.slow
 def test_huginn_ripe_full_size_sampled():
     """Huginn-shaped RIPE decode at full size (32 sequences, 55 heads x 96, L = 1024, W = 64, page 16),
-    layer 0, loops 0 / 17 / 31, the launch configuration the benchmark times; sampled rows vs the oracle,
-    the whole index trace of head 0 vs the oracle's plane map."""
+    layer 0, loops 0 / 17 / 31, in two launch configurations:
+      * the one the benchmark times: one split, the untraced 8-wave decode kernel, no merge;
+      * the library's own split choice with the index trace on (the traced kernel instance and the merge).
+    Sampled rows of both against the oracle element by element, and the whole index trace of head 0 against the
+    oracle's plane map."""
     w = synth.WORKLOADS["huginn_ripe"]
+    assert w.split_k == 1  # the benchmark's launch configuration
     built = harness.build_plain(w, layers=(0,))
     L = w.length
-    rows = harness.sample_rows(w.batch, 1, w.n_heads, 20, seed=1)
+    rows = harness.sample_rows(w.batch, 1, w.n_heads, 40, seed=1)
     for loop in (0, 17, 31):
         q = harness.gpu_queries(built, 0, loop, 1)
-        out, lse, tr = _attend(built, 0, loop, q, 0, trace_len=L)
+        want, want_lse = harness.oracle_rows(w, rows, 0, loop, built.lengths, 1, vla.POLICY_RIPE, w.window)
+        # the timed configuration
+        out, lse, _ = _attend(built, 0, loop, q, 1)
         o = harness.out_f64(out)
         assert np.isfinite(o).all()
-        want, want_lse = harness.oracle_rows(w, rows, 0, loop, built.lengths, 1, vla.POLICY_RIPE, w.window)
         got = np.array([o[b, i, h] for (b, i, h) in rows])
-        assert np.abs(got - want).max() <= TOL_BF16
+        assert np.abs(got - want).max() <= TOL_BF16, loop
+        got_lse = lse.cpu().numpy()
+        assert np.abs(np.array([got_lse[b, i, h] for (b, i, h) in rows]) - want_lse).max() <= 1e-3
+        # library-chosen splits with the trace
+        out_t, _, tr = _attend(built, 0, loop, q, 0, trace_len=L)
+        o_t = harness.out_f64(out_t)
+        assert np.isfinite(o_t).all()
+        assert np.abs(np.array([o_t[b, i, h] for (b, i, h) in rows]) - want).max() <= TOL_BF16, loop
         pm = oracle.plane_map(vla.POLICY_RIPE, loop, w.n_loops, L - 1, L - 1, L, w.window)
         t = tr.cpu().numpy()
         for b in range(w.batch):

@@ -184,18 +184,24 @@ def test_draft_step(policy, W, D):
 @pytest.mark.parametrize("policy", [vla.POLICY_FULL, vla.POLICY_RIPE])
 def test_huginn_verify_full_size_sampled(policy):
     """Self-speculative verify at the Huginn shape: 16 sequences, L = 808 (800 cached + block of 8),
-    55 heads x 96, full cache vs RIPE W = 64; layer 0, loops 0 and 31; sampled rows."""
+    55 heads x 96, full cache vs RIPE W = 64; layer 0, loops 0 and 31; sampled rows against the oracle in the
+    launch configuration the benchmark times (one split, the untraced two-wave verify kernel, no merge) and with
+    the library's own split choice (splits and the merge)."""
     w = synth.WORKLOADS["huginn_verify"]
+    assert w.split_k == 1  # the benchmark's launch configuration
     built = harness.build_plain(w, layers=(0,), policy=policy, planes=[0, 31])
-    rows = harness.sample_rows(w.batch, w.q_len, w.n_heads, 24, seed=3)
+    rows = harness.sample_rows(w.batch, w.q_len, w.n_heads, 40, seed=3)
     for loop in (0, 31):
         q = harness.gpu_queries(built, 0, loop, w.q_len)
-        out, _, _ = _verify(built, 0, loop, q)
-        o = harness.out_f64(out)
-        assert np.isfinite(o).all()
-        want, _ = harness.oracle_rows(w, rows, 0, loop, built.lengths, w.q_len, policy, w.window)
-        got = np.array([o[b, i, h] for (b, i, h) in rows])
-        assert np.abs(got - want).max() <= TOL_BF16
+        want, want_lse = harness.oracle_rows(w, rows, 0, loop, built.lengths, w.q_len, policy, w.window)
+        for split_k in (1, 0):
+            out, lse, _ = _verify(built, 0, loop, q, split_k=split_k)
+            o = harness.out_f64(out)
+            assert np.isfinite(o).all()
+            got = np.array([o[b, i, h] for (b, i, h) in rows])
+            assert np.abs(got - want).max() <= TOL_BF16, (loop, split_k)
+            got_lse = lse.cpu().numpy()
+            assert np.abs(np.array([got_lse[b, i, h] for (b, i, h) in rows]) - want_lse).max() <= 1e-3
     built.cache.close()
 
 

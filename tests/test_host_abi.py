@@ -287,10 +287,11 @@ def test_quant_workspace_matches_the_cell_split_rule(lib):
     assert c.lkv_workspace_bytes(0, 0, seqs[2:], split_k=5) == 4 * (1 + 1) * 129 * 4  # 1 code page caps the splits
 
 
-@pytest.mark.parametrize("gamma,W", [(4, 8), (7, 7), (2, 40)])
+@pytest.mark.parametrize("gamma,W", [(4, 8), (7, 7), (2, 40), (9, 4)])
 def test_speculative_steps_keep_exactly_the_ripe_pages(lib, gamma, W):
-    """Host bookkeeping of many self-speculative steps (RIPE page, Sec. 4 and Algorithm 1): reserve the block's
-    planes at every loop, accept a seeded prefix, commit and truncate.  After every step the pages in use are the
+    """Host bookkeeping of many self-speculative steps (RIPE page, Sec. 4 and Algorithm 1) with a block length
+    drawn per step in [1, gamma] (also above W in the last case): reserve the block's planes at every loop, accept
+    a seeded prefix, commit and truncate.  After every step the pages in use are the
     deepest plane of every position plus the window ring of every other plane, the logical bytes follow Eq. (10),
     and every cached position that the next token (at position len) reads resolves to a resident page of the
     plane the policy names."""
@@ -307,14 +308,16 @@ def test_speculative_steps_keep_exactly_the_ripe_pages(lib, gamma, W):
                 lo = max(0, L - W)
                 c.lkv_reserve(s, layer, plane, lo, L - lo)
     rng = np.random.default_rng(gamma * 100 + W)
-    k = gamma + 1
     b_tok = 2 * 2 * 64 * 2
+    drawn = set()
     for step in range(60):
+        g = int(rng.integers(1, gamma + 1))  # this step's block length g + 1
+        drawn.add(g)
         for b, s in enumerate(seqs):
             for loop in range(R):
                 for layer in range(n_layers):
-                    c.lkv_reserve(s, layer, loop, lens[b], k)
-            a = int(rng.integers(0, gamma + 1))
+                    c.lkv_reserve(s, layer, loop, lens[b], g + 1)
+            a = int(rng.integers(0, g + 1))
             new_len = lens[b] + 1 + a
             c.lkv_commit(s, new_len)
             c.lkv_truncate(s, new_len)
@@ -333,6 +336,7 @@ def test_speculative_steps_keep_exactly_the_ripe_pages(lib, gamma, W):
                     plane, phys, slot = c.lkv_debug_resolve(s, 1, loop, t, t, j)
                     assert plane == oracle.oracle_plane(oracle.RIPE, loop, R, t, t, j, W)
                     assert phys >= 0 and slot == j % 16
+    assert len(drawn) > 1  # the block length varied
 
 
 def test_binding_rejects_host_noncontiguous_and_undersized_tensors():
@@ -398,3 +402,4 @@ def test_commit_is_monotone(lib):
         c.lkv_reserve(s, 0, p, 100, 1)
     c.lkv_commit(s, 101)
     assert c.lkv_seq_info(s) == (101, 101)
+

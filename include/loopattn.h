@@ -290,6 +290,20 @@ lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, siz
    (workspace too small), EUNSUPPORTED, EDEVICE. */
 lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream);
 
+/* lkv_attend for callers that cannot allocate device memory or pass a workspace: code
+   under HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same
+   arguments, checks, kernels and results as lkv_attend, except that workspace must be
+   NULL and workspace_bytes 0: the split partials go to a fixed device array of
+   LKV_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the
+   process ends.  A call whose partials would not fit is refused (EINVAL) before any
+   device work.  Nothing is allocated (no hipMalloc, hipFree or allocating library
+   routine).  Every call on one GPU uses that GPU's one array, so calls that overlap on
+   the same GPU (other streams, other threads, other handles) race and must be
+   serialised by the caller.  The handle's device must be current.  Errors as
+   lkv_attend, plus EDEVICE if the array's address cannot be resolved. */
+#define LKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+lkv_status lkv_attend_noalloc(lkv_cache* c, const lkv_attend_args* a, void* stream);
+
 lkv_status lkv_mem_stats(const lkv_cache* c, lkv_mem_info* out);
 
 /* Host index function: the plane, physical page and slot that the row at

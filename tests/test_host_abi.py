@@ -403,3 +403,21 @@ def test_commit_is_monotone(lib):
     c.lkv_commit(s, 101)
     assert c.lkv_seq_info(s) == (101, 101)
 
+
+def test_noalloc_refuses_workspace_and_oversized_calls_before_device_work(lib):
+    """lkv_attend_noalloc takes no workspace, and a call whose split partials exceed its fixed scratch is refused
+    on the host with EINVAL (no device is touched: this runs without a GPU)."""
+    c = make(n_pages=400, n_heads_q=55, n_heads_kv=55, head_dim=96, max_seqs=16, max_len=256)
+    seqs = [c.lkv_add_seq() for _ in range(16)]
+    for s in seqs:
+        c.lkv_reserve(s, 0, 3, 0, 64)
+    per_split = 16 * 8 * 55 * 97 * 4  # verify blocks of 8 rows
+    assert vla.NOALLOC_SCRATCH_BYTES == 32 << 20
+    a, _ids = c._args(0, 3, seqs, 1 << 40, 1 << 41, q_len=8, mode=vla.MODE_VERIFY, split_k=64)
+    assert 64 * per_split > vla.NOALLOC_SCRATCH_BYTES
+    assert lib.lkv_attend_noalloc(c.h, ctypes.byref(a), 0) == vla.LKV_EINVAL
+    assert b"scratch" in lib.lkv_last_error(c.h)
+    a, _ids = c._args(0, 3, seqs, 1 << 40, 1 << 41, split_k=2)
+    a.workspace, a.workspace_bytes = 1 << 42, 1 << 20
+    assert lib.lkv_attend_noalloc(c.h, ctypes.byref(a), 0) == vla.LKV_EINVAL
+    assert b"no workspace" in lib.lkv_last_error(c.h)

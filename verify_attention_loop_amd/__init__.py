@@ -23,11 +23,12 @@ CELL_BF16, CELL_INT4, CELL_INT2, CELL_SHARED = 0, 1, 2, 3
 VRULE_FIXED, VRULE_RUNNING = 0, 1
 KERNEL_AUTO, KERNEL_VALU = 0, 1
 PAGE_TOKENS, CODE_PAGE_TOKENS = 16, 32
+NOALLOC_SCRATCH_BYTES = 32 << 20  # LKV_NOALLOC_SCRATCH_BYTES
 
 EXPORTS = [
     "lkv_sizes", "lkv_create", "lkv_destroy", "lkv_add_seq", "lkv_free_seq", "lkv_reserve", "lkv_append_plane",
     "lkv_commit", "lkv_truncate", "lkv_set_plan", "lkv_append_coded", "lkv_encode_pages", "lkv_read_coded",
-    "lkv_workspace_bytes", "lkv_attend",
+    "lkv_workspace_bytes", "lkv_attend", "lkv_attend_noalloc",
     "lkv_mem_stats", "lkv_debug_resolve", "lkv_seq_info", "lkv_last_error", "lkv_status_str", "lkv_probe_read",
 ]
 
@@ -103,6 +104,7 @@ def load():
         "lkv_read_coded": [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "lkv_workspace_bytes": [vp, P(lkv_attend_args), P(ctypes.c_size_t)],
         "lkv_attend": [vp, P(lkv_attend_args), vp],
+        "lkv_attend_noalloc": [vp, P(lkv_attend_args), vp],
         "lkv_mem_stats": [vp, P(lkv_mem_info)],
         "lkv_debug_resolve": [vp, i32, i32, i32, i32, i32, i32, i32, P(i32), P(i32), P(i32)],
         "lkv_seq_info": [vp, i32, P(i32), P(i32)],
@@ -348,6 +350,17 @@ class LoopCache:
             raise ValueError(f"n_seqs {a.n_seqs} outside [1, {self.cfg.max_seqs}]")
         self._attend_buffers(a, q, out, kw)
         self._check(self.lib.lkv_attend(self.h, ctypes.byref(a), _stream(stream)), "lkv_attend")
+
+    def lkv_attend_noalloc(self, layer, loop, seq_ids, q, out, stream=None, **kw):
+        """lkv_attend without a workspace: the split partials live in the library's fixed device scratch
+        (nothing is allocated).  Calls that overlap on one GPU race."""
+        if kw.get("workspace") is not None:
+            raise ValueError("lkv_attend_noalloc takes no workspace")
+        a, _ids = self._args(layer, loop, seq_ids, q, out, **kw)
+        if not 1 <= a.n_seqs <= self.cfg.max_seqs:
+            raise ValueError(f"n_seqs {a.n_seqs} outside [1, {self.cfg.max_seqs}]")
+        self._attend_buffers(a, q, out, kw)
+        self._check(self.lib.lkv_attend_noalloc(self.h, ctypes.byref(a), _stream(stream)), "lkv_attend_noalloc")
 
     def lkv_mem_stats(self) -> dict:
         m = lkv_mem_info()

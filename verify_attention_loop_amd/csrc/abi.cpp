@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1081,6 +1082,72 @@ lkv_status lkv_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* e
   ev.start = (hipEvent_t)ev_begin;
   ev.stop = (hipEvent_t)ev_end;
   return launch_probe_read(buf, bytes, sink, (hipStream_t)stream, ev) == hipSuccess ? LKV_OK : LKV_EDEVICE;
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------------------------- attend without allocation
+//
+// lkv_attend_noalloc runs lkv_attend with the split partials in a fixed device array
+// instead of a caller workspace, for callers that cannot allocate.  The array is one
+// file-scope __device__ object: every GPU the library runs on holds its own copy until
+// the process ends, at its own address, which is looked up once per device with
+// hipGetSymbolAddress (the array's name in host code is only a host-side stand-in).
+// The partials are written in full before they are read, so nothing in it has to start
+// at zero; calls that overlap on one device share it and race.
+static __device__ __align__(256) uint8_t scratch[LKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of the scratch array (resolved on first use, with
+// the device current).
+hipError_t scratch_ptr(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int prev = -1;
+    hipError_t e = hipGetDevice(&prev);
+    if (e != hipSuccess) return e;
+    if (prev != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (prev != device) {
+      const hipError_t e2 = hipSetDevice(prev);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+lkv_status lkv_attend_noalloc(lkv_cache* c, const lkv_attend_args* a, void* stream) {
+  if (!c) return LKV_EINVAL;
+  if (!a) return c->fail(LKV_EINVAL, "args is NULL");
+  if (a->workspace || a->workspace_bytes)
+    return c->fail(LKV_EINVAL, "lkv_attend_noalloc takes no workspace (its partials live in the library's scratch)");
+  if (c->device < 0 || c->device >= kMaxDevices) return c->fail(LKV_EINVAL, "device %d", c->device);
+  size_t need = 0;
+  lkv_status st = lkv_workspace_bytes(c, a, &need);
+  if (st != LKV_OK) return c->fail(st, "workspace size of the call");
+  if (need > LKV_NOALLOC_SCRATCH_BYTES)
+    return c->fail(LKV_EINVAL, "the call needs %zu bytes of partials, more than the %zu-byte scratch of "
+                   "lkv_attend_noalloc (fewer splits or sequences per call, or lkv_attend with a workspace)",
+                   need, (size_t)LKV_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  hipError_t e = scratch_ptr(c->device, &ptr);
+  if (e != hipSuccess) return hip_fail(c, e, "scratch address (hipGetSymbolAddress)");
+  lkv_attend_args b = *a;
+  b.workspace = ptr;
+  b.workspace_bytes = LKV_NOALLOC_SCRATCH_BYTES;
+  return lkv_attend(c, &b, stream);
 }
 
 }  // extern "C"

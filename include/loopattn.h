@@ -181,10 +181,12 @@ lkv_status lkv_free_seq(lkv_cache* c, int32_t seq);
 
 /* Allocate the pages that positions [pos0, pos0 + n_tok) of plane `plane` need,
    without writing them (host bookkeeping; lkv_append_plane = reserve + copy).
-   Extends the sequence length to pos0 + n_tok.  Plain caches: positions must
-   not leave a gap after the plane's last position (ESTATE); RIPE non-deepest
-   planes accept only positions >= committed - W that fit the window ring
-   (EWINDOW); ENOMEM if the pool is empty. */
+   Extends the sequence length to pos0 + n_tok.  Positions must not leave a gap
+   after the plane's last position (ESTATE); RIPE non-deepest planes accept only
+   positions >= committed - W that fit the window ring (EWINDOW).  Quantised caches
+   hold the sink and the tail here: after the sink the far history may be skipped
+   (supplied as code pages), and positions that already left the tail (encoded by
+   lkv_window_exit) cannot be written again (ESTATE).  ENOMEM if the pool is empty. */
 lkv_status lkv_reserve(lkv_cache* c, int32_t seq, int32_t layer, int32_t plane, int32_t pos0,
                        int32_t n_tok);
 
@@ -257,6 +259,24 @@ lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t lo
 lkv_status lkv_encode_pages(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop, int32_t page0,
                             int32_t n_pages, int32_t n_valid_last, const void* k, const void* v,
                             void* stream);
+
+/* Quantised caches: the window exit ("LoopKV: Loop-Aware KV Cache Compression for
+   Serving Looped Transformers", Sec. 3.4 and Sec. 4: when a page leaves the exact
+   window, a KIVI codec quantises it into its cell's pool and the bf16 block is
+   released; the quantisation runs before the step that reads it).  For sequence seq
+   of length L, the far history is [sink, L - tail): every far position that left the
+   tail since the last exit is encoded, in every INT4 and INT2 cell, from the cell's
+   own exact plane (appended with lkv_append_plane) into its code pages with the codec
+   of lkv_encode_pages; a partially filled last code page is encoded again from all its
+   valid tokens, so the codes always equal the codec applied to the page's exact
+   values.  Exact pages that no cell reads any more return to the pool: pages wholly
+   past the sink whose positions lie in complete code pages (or, for a shared cell,
+   that all left the tail).  Call it after appending a step's tokens and before the
+   step's attend calls; positions that left the tail can no longer be appended or
+   truncated.  Device work on `stream`.  Errors: ESTATE (not a quantised cache, no
+   plan, an exact page missing), ENOMEM (code pools exhausted; nothing changed),
+   EDEVICE. */
+lkv_status lkv_window_exit(lkv_cache* c, int32_t seq, void* stream);
 
 /* Quantised caches: read code pages back into the logical layout lkv_append_coded
    takes (the inverse of its packing), into caller-owned device buffers of the

@@ -28,6 +28,7 @@ NOALLOC_SCRATCH_BYTES = 32 << 20  # LKV_NOALLOC_SCRATCH_BYTES
 EXPORTS = [
     "lkv_sizes", "lkv_create", "lkv_destroy", "lkv_add_seq", "lkv_free_seq", "lkv_reserve", "lkv_append_plane",
     "lkv_commit", "lkv_truncate", "lkv_set_plan", "lkv_append_coded", "lkv_encode_pages", "lkv_read_coded",
+    "lkv_window_exit",
     "lkv_workspace_bytes", "lkv_attend", "lkv_attend_noalloc",
     "lkv_mem_stats", "lkv_debug_resolve", "lkv_seq_info", "lkv_last_error", "lkv_status_str", "lkv_probe_read",
 ]
@@ -102,6 +103,7 @@ def load():
         "lkv_append_coded": [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp],
         "lkv_encode_pages": [vp, i32, i32, i32, i32, i32, i32, vp, vp, vp],
         "lkv_read_coded": [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp],
+        "lkv_window_exit": [vp, i32, vp],
         "lkv_workspace_bytes": [vp, P(lkv_attend_args), P(ctypes.c_size_t)],
         "lkv_attend": [vp, P(lkv_attend_args), vp],
         "lkv_attend_noalloc": [vp, P(lkv_attend_args), vp],
@@ -299,6 +301,9 @@ class LoopCache:
         self._coded_args(n_pages, k_codes, k_meta, v_codes, v_meta)
         self._check(self.lib.lkv_read_coded(self.h, seq, layer, loop, page0, n_pages, _ptr(k_codes), _ptr(k_meta),
                                             _ptr(v_codes), _ptr(v_meta), _stream(stream)), "lkv_read_coded")
+
+    def lkv_window_exit(self, seq: int, stream=None):
+        self._check(self.lib.lkv_window_exit(self.h, seq, _stream(stream)), "lkv_window_exit")
 
     def _args(self, layer, loop, seq_ids, q, out, q_len=1, mode=MODE_DECODE, window=-1, split_k=0,
               v_thresh_offset=4.0, lse=None, workspace=None, draft_k=None, draft_v=None, draft_len=0,

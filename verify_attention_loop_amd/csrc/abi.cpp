@@ -338,6 +338,15 @@ struct Touched {
   bool fresh;
 };
 
+// Far positions of (seq, layer, loop) already held as codes: those of the cell's source
+// (its own codes, or the final loop's for a shared cell); 0 before a plan is set.
+static int32_t encoded_far(const lkv_cache* c, int32_t seq, int32_t layer, int32_t loop) {
+  if (!c->cfg.quant || !c->plan_set) return 0;
+  const int R = c->cfg.n_loops;
+  const int src = c->plan[(size_t)layer * R + loop] == LKV_CELL_SHARED ? R - 1 : loop;
+  return c->ctabs[(size_t)layer * R + src].hi[(size_t)seq];
+}
+
 static lkv_status reserve_impl(lkv_cache* c, int32_t seq, int32_t layer, int32_t plane, int32_t pos0,
                                int32_t n_tok, std::vector<Touched>* touched) {
   if (!c->live(seq)) return c->fail(LKV_EINVAL, "sequence %d is not live", seq);
@@ -349,7 +358,18 @@ static lkv_status reserve_impl(lkv_cache* c, int32_t seq, int32_t layer, int32_t
   const auto& S = c->seqs[(size_t)seq];
   const int32_t hi = T.hi[(size_t)seq];
   const int32_t lo_win = std::max(0, S.committed - c->cfg.window);
-  if (!c->cfg.quant) {
+  if (c->cfg.quant) {
+    // The exact bf16 plane holds the sink and the tail; positions that left the tail
+    // live as codes.  No gap, except that a far history supplied as code pages may be
+    // skipped after the sink; positions already encoded cannot be written again.
+    if (pos0 > hi && !(hi <= c->cfg.sink && pos0 >= c->cfg.sink))
+      return c->fail(LKV_ESTATE, "gap: plane %d of seq %d holds positions up to %d, append starts at %d", plane, seq,
+                     hi, pos0);
+    const int32_t enc = encoded_far(c, seq, layer, plane);
+    if (enc > 0 && pos0 < c->cfg.sink + enc && pos0 + n_tok > c->cfg.sink)
+      return c->fail(LKV_ESTATE, "positions [%d, %d) of plane %d already left the tail (encoded up to %d)", pos0,
+                     pos0 + n_tok, plane, c->cfg.sink + enc);
+  } else {
     if (T.window_ring) {
       if (pos0 < lo_win)
         return c->fail(LKV_EWINDOW, "plane %d keeps positions >= %d only (committed %d, window %d); got %d", plane,
@@ -476,6 +496,11 @@ lkv_status lkv_truncate(lkv_cache* c, int32_t seq, int32_t new_len) {
   auto& S = c->seqs[(size_t)seq];
   if (new_len < S.committed || new_len > S.len)
     return c->fail(LKV_EINVAL, "truncate length %d outside [committed %d, len %d]", new_len, S.committed, S.len);
+  if (c->cfg.quant)
+    for (int l = 0; l < c->cfg.n_layers; ++l)
+      for (int r = 0; r < c->cfg.n_loops; ++r)
+        if (new_len - c->cfg.tail < c->cfg.sink + encoded_far(c, seq, l, r))
+          return c->fail(LKV_ESTATE, "truncate to %d would re-open positions that already left the tail", new_len);
   const int32_t first_dead_page = (new_len + kPage - 1) / kPage;
   for (auto& T : c->tabs) {
     release_row(c, T, c->pages, seq, first_dead_page);
@@ -543,7 +568,6 @@ static lkv_status claim_code_pages(lkv_cache* c, Table& T, FreeList& fl, int32_t
       T.dirty[(size_t)seq] = 1;
     }
   }
-  T.hi[(size_t)seq] = std::max(T.hi[(size_t)seq], page0 + n_pages);
   return LKV_OK;
 }
 
@@ -560,6 +584,7 @@ lkv_status lkv_append_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t lo
   if (st != LKV_OK) return st;
   if (!k_codes || !k_meta || !v_codes || !v_meta) return c->fail(LKV_EINVAL, "NULL code buffer");
   if ((st = claim_code_pages(c, *T, *fl, seq, page0, n_pages)) != LKV_OK) return st;
+  T->hi[(size_t)seq] = std::max(T->hi[(size_t)seq], (page0 + n_pages) * kCodePage);
   const int hkv = c->cfg.n_heads_kv, d = c->cfg.head_dim;
   hipStream_t s = (hipStream_t)stream;
   for (int q0 = page0; q0 < page0 + n_pages; q0 += 64) {
@@ -595,6 +620,7 @@ lkv_status lkv_encode_pages(lkv_cache* c, int32_t seq, int32_t layer, int32_t lo
   if (n_valid_last < 1 || n_valid_last > kCodePage)
     return c->fail(LKV_EINVAL, "n_valid_last %d outside [1, %d]", n_valid_last, kCodePage);
   if ((st = claim_code_pages(c, *T, *fl, seq, page0, n_pages)) != LKV_OK) return st;
+  T->hi[(size_t)seq] = std::max(T->hi[(size_t)seq], (page0 + n_pages - 1) * kCodePage + n_valid_last);
   const int hkv = c->cfg.n_heads_kv, d = c->cfg.head_dim;
   hipStream_t s = (hipStream_t)stream;
   for (int q0 = page0; q0 < page0 + n_pages; q0 += 64) {
@@ -937,6 +963,10 @@ static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_
     max_far = std::max(max_far, n_far);
     const int n_cp = (n_far + kCodePage - 1) / kCodePage;
     if (n_cp > c->max_code_pages) return c->fail(LKV_ESTATE, "seq %d: far history longer than max_len", sq);
+    if (Tc.hi[(size_t)sq] < n_far)
+      return c->fail(LKV_ESTATE, "seq %d: cell (%d, %d) holds %d far positions as codes, the call needs %d "
+                     "(lkv_window_exit encodes the positions that left the tail)", sq, a->layer, src_loop,
+                     Tc.hi[(size_t)sq], n_far);
     for (int p = 0; p < n_cp; ++p)
       if (Tc.owner[(size_t)sq * Tc.ring + p] != p)
         return c->fail(LKV_ESTATE, "seq %d: code page %d of cell (%d, %d) is not resident", sq, p, a->layer, src_loop);
@@ -1085,6 +1115,104 @@ lkv_status lkv_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* e
 }
 
 }  // extern "C"
+
+// ----------------------------------------------------------------------------- window exit of quantised caches
+
+extern "C" lkv_status lkv_window_exit(lkv_cache* c, int32_t seq, void* stream) {
+  if (!c) return LKV_EINVAL;
+  const auto& cfg = c->cfg;
+  if (!cfg.quant) return c->fail(LKV_ESTATE, "the cache has no quantised cells");
+  if (!c->plan_set) return c->fail(LKV_ESTATE, "lkv_set_plan first");
+  if (!c->live(seq)) return c->fail(LKV_EINVAL, "sequence %d is not live", seq);
+  const int R = cfg.n_loops, nl = cfg.n_layers;
+  const int32_t L = c->seqs[(size_t)seq].len;
+  const int32_t fe = std::max(0, L - cfg.tail - cfg.sink);  // far positions that left the tail
+  if ((fe + kCodePage - 1) / kCodePage > c->max_code_pages)
+    return c->fail(LKV_ESTATE, "far history of seq %d longer than max_len allows", seq);
+  // Phase 1 (host checks, nothing changes): the positions to encode are resident in each
+  // cell's exact plane, and the pools hold the code pages that are needed.
+  int64_t need4 = 0, need2 = 0;
+  for (int l = 0; l < nl; ++l)
+    for (int r = 0; r < R; ++r) {
+      const int8_t kind = c->plan[(size_t)l * R + r];
+      if (kind == LKV_CELL_SHARED) continue;
+      const Table& Tc = c->ctab(l, r);
+      const int32_t done = Tc.hi[(size_t)seq];
+      if (fe <= done) continue;
+      const int32_t p0 = done / kCodePage, p1 = (fe - 1) / kCodePage;
+      for (int p = p0; p <= p1; ++p)
+        if (Tc.owner[(size_t)seq * Tc.ring + p] != p) ++(kind == LKV_CELL_INT2 ? need2 : need4);
+      const Table& Tn = c->tab(l, r);
+      const int32_t a = cfg.sink + p0 * kCodePage, b = cfg.sink + fe;
+      if (Tn.hi[(size_t)seq] < b)
+        return c->fail(LKV_ESTATE, "seq %d: plane %d of layer %d holds positions below %d, the exit needs %d", seq, r,
+                       l, Tn.hi[(size_t)seq], b);
+      for (int pg = a / kPage; pg <= (b - 1) / kPage; ++pg)
+        if (Tn.owner[(size_t)seq * Tn.ring + pg] != pg)
+          return c->fail(LKV_ESTATE, "seq %d: page %d of plane %d (layer %d) is not resident", seq, pg, r, l);
+    }
+  if (need4 > c->codes4.available() || need2 > c->codes2.available())
+    return c->fail(LKV_ENOMEM, "need %lld INT4 and %lld INT2 code pages, %lld and %lld free", (long long)need4,
+                   (long long)need2, (long long)c->codes4.available(), (long long)c->codes2.available());
+  // Phase 2: encode every non-shared cell's new far positions from its exact plane (the
+  // partial last page is encoded again from all its valid tokens), on the stream.
+  hipStream_t s = (hipStream_t)stream;
+  const int hkv = cfg.n_heads_kv, d = cfg.head_dim;
+  const std::vector<int32_t> one{seq};
+  for (int l = 0; l < nl; ++l)
+    for (int r = 0; r < R; ++r) {
+      const int8_t kind = c->plan[(size_t)l * R + r];
+      if (kind == LKV_CELL_SHARED) continue;
+      Table& Tc = c->ctab(l, r);
+      const int32_t done = Tc.hi[(size_t)seq];
+      if (fe <= done) continue;
+      FreeList& fl = kind == LKV_CELL_INT2 ? c->codes2 : c->codes4;
+      const int32_t p0 = done / kCodePage, p1 = (fe - 1) / kCodePage;
+      lkv_status st = claim_code_pages(c, Tc, fl, seq, p0, p1 - p0 + 1);
+      if (st != LKV_OK) return st;  // cannot happen after phase 1
+      Table& Tn = c->tab(l, r);
+      if ((st = upload(c, Tn, one, s)) != LKV_OK) return st;
+      for (int q0 = p0; q0 <= p1; q0 += 64) {
+        EncodeParams P{};
+        P.arena = (uint8_t*)(kind == LKV_CELL_INT2 ? c->ar.codes2 : c->ar.codes4);
+        P.page_bytes = kind == LKV_CELL_INT2 ? c->code2_bytes : c->code4_bytes;
+        P.pool = (const uint8_t*)c->ar.pages;
+        P.plain_page_bytes = c->page_bytes;
+        P.tab_plain = (const int32_t*)((const uint8_t*)c->ar.meta + Tn.dev_off) + (size_t)seq * Tn.ring;
+        P.pos0 = cfg.sink + q0 * kCodePage;
+        P.hkv = hkv;
+        P.bits = kind == LKV_CELL_INT2 ? 2 : 4;
+        P.n_pages = std::min(64, p1 + 1 - q0);
+        P.n_valid_last = q0 + P.n_pages - 1 == p1 ? fe - p1 * kCodePage : kCodePage;
+        for (int x = 0; x < P.n_pages; ++x) P.phys[x] = Tc.phys[(size_t)seq * Tc.ring + q0 + x];
+        hipError_t e = launch_encode_pages(P, d, s);
+        if (e != hipSuccess) return hip_fail(c, e, "encode kernel");
+      }
+      Tc.hi[(size_t)seq] = fe;
+    }
+  // Phase 3: release the exact pages no cell reads any more: pages wholly past the sink
+  // whose positions all lie in complete code pages (a cell with codes), or that all left
+  // the tail (a shared cell, which reads the final loop's codes).  Released pages go back
+  // to the pool; device work that writes them again must follow this call's kernels on
+  // the stream.
+  const int32_t whole = cfg.sink + fe / kCodePage * kCodePage;
+  for (int l = 0; l < nl; ++l)
+    for (int r = 0; r < R; ++r) {
+      const int32_t limit = c->plan[(size_t)l * R + r] == LKV_CELL_SHARED ? cfg.sink + fe : whole;
+      Table& Tn = c->tab(l, r);
+      for (int e = 0; e < Tn.ring; ++e) {
+        const size_t i = (size_t)seq * Tn.ring + e;
+        const int32_t o = Tn.owner[i];
+        if (o >= 0 && o * kPage >= cfg.sink && (o + 1) * kPage <= limit) {
+          c->pages.push(Tn.phys[i]);
+          Tn.phys[i] = -1;
+          Tn.owner[i] = -1;
+          Tn.dirty[(size_t)seq] = 1;
+        }
+      }
+    }
+  return LKV_OK;
+}
 
 // ----------------------------------------------------------------------------- attend without allocation
 //

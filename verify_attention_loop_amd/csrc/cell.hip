@@ -194,17 +194,33 @@ __global__ __launch_bounds__(128) void encode_pages_kernel(const EncodeParams p)
   const int levels = (1 << p.bits) - 1;
   __shared__ uint8_t kc[kCodePage][D], vc[kCodePage][D];
   __shared__ uint16_t km[D][2], vm[kCodePage][4][2];
-  const int64_t tok_stride = (int64_t)p.hkv * D;
-  const uint16_t* kin = p.k + ((int64_t)pi * kCodePage * p.hkv + h) * D;
-  const uint16_t* vin = p.v + ((int64_t)pi * kCodePage * p.hkv + h) * D;
+  // the page's exact keys and values of head h, token-major, staged in LDS (thread = channel)
+  __shared__ uint16_t kx[kCodePage][D], vx[kCodePage][D];
+  for (int t = 0; t < n; ++t) {
+    if (p.tab_plain) {
+      // plain page layout: K block [head][token][channel]; V block [head][quad][channel][i],
+      // entry i of quad g = token 4 i + g
+      const int j = p.pos0 + pi * kCodePage + t, s = j % kPage;
+      const uint8_t* base = p.pool + (uint64_t)p.tab_plain[j / kPage] * p.plain_page_bytes;
+      const uint64_t head = (uint64_t)kPage * D * 2;
+      kx[t][tid] = *reinterpret_cast<const uint16_t*>(base + h * head + ((uint64_t)s * D + tid) * 2);
+      vx[t][tid] = *reinterpret_cast<const uint16_t*>(base + (p.hkv + h) * head +
+                                                      (((uint64_t)(s & 3) * D + tid) * kQuad + (s >> 2)) * 2);
+    } else {
+      const int64_t row = ((int64_t)pi * kCodePage + t) * p.hkv + h;
+      kx[t][tid] = p.k[row * D + tid];
+      vx[t][tid] = p.v[row * D + tid];
+    }
+  }
+  __syncthreads();
   // keys: thread = channel
-  encode_group(kin + tid, n, (int)tok_stride, levels, &kc[0][tid], D, km[tid]);
+  encode_group(&kx[0][tid], n, D, levels, &kc[0][tid], D, km[tid]);
   for (int t = n; t < kCodePage; ++t) kc[t][tid] = 0;
   // values: thread = (token, 32-channel group)
   {
     const int t = tid >> 2, grp = tid & 3;
     if (t < n) {
-      encode_group(vin + t * tok_stride + 32 * grp, 32, 1, levels, &vc[t][32 * grp], 1, vm[t][grp]);
+      encode_group(&vx[t][32 * grp], 32, 1, levels, &vc[t][32 * grp], 1, vm[t][grp]);
     } else {
       for (int c = 0; c < 32; ++c) vc[t][32 * grp + c] = 0;
       vm[t][grp][0] = 0;

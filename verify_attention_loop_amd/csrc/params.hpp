@@ -106,12 +106,17 @@ struct PackParams {
 };
 
 // Encode exact bf16 keys and values of up to 64 far pages into code pages (the
-// window-exit codec).
+// window-exit codec).  The values come either from caller arrays (k, v) or, when
+// tab_plain is set, from the cell's own plain pages (the tail the positions leave).
 struct EncodeParams {
   uint8_t* arena;
   uint64_t page_bytes;
   const uint16_t* k;          // bf16 [n_pages * 32][hkv][D]
   const uint16_t* v;
+  const uint8_t* pool;        // plain page arena, when reading from pages
+  uint64_t plain_page_bytes;
+  const int32_t* tab_plain;   // the sequence's row of the plain table, or null
+  int32_t pos0;               // position of token 0 of batch page 0 (sink + 32 page0)
   int32_t hkv, bits;
   int32_t n_pages;
   int32_t n_valid_last;       // valid tokens of the last page (1..32)

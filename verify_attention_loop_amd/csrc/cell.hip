@@ -19,10 +19,10 @@
 // hi crumbs sit at crumb 2c + 1 (c < 4) or 2(c - 4) (c >= 4), lo and INT2 crumbs
 // at crumb 2c (c < 4) or 2(c - 4) + 1 (c >= 4).  Then x | x << 18 puts hi_c at
 // bits 2-3 of nibble c and y | y << 14 puts lo_c at bits 0-1 of nibble c, so one
-// bitfield insert yields the eight 4-bit codes 4 hi + lo of a hot token, and
-// byte conversions turn nibbles into floats: about 3 VALU instructions per code
-// instead of 6 for separate hi and lo planes.  K codes are plain nibbles (nibble c
-// = channel c).
+// bitfield insert yields the eight 4-bit codes 4 hi + lo of a hot token.  K codes are
+// plain nibbles (nibble c = channel c).  Nibble words and INT2 words reach the
+// arithmetic as exact fp16 pairs (offset + code) with one mask-and-exponent
+// instruction per pair (int4_pairs_f16, int2_pairs_f16).
 #include <hip/hip_runtime.h>
 
 #include "attn_common.hpp"
@@ -268,43 +268,71 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
 __device__ __forceinline__ uint32_t hi_nibbles(uint32_t x) { return (x | (x << 18)) & 0xCCCCCCCCu; }
 __device__ __forceinline__ uint32_t lo_nibbles(uint32_t y) { return (y | (y << 14)) & 0x33333333u; }
 
-// Byte k of a word as a float (v_cvt_f32_ubyte{0..3}: one VALU op).  Written as an
-// instruction because the compiler, knowing the bytes hold nibbles, otherwise
-// extracts each one with a separate bitfield op first.
-template <int K>
-__device__ __forceinline__ float ubyte_f32(uint32_t x) {
-  float r;
-  if constexpr (K == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x));
-  else if constexpr (K == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x));
-  else if constexpr (K == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x));
-  else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x));
-  return r;
-}
-
-// The eight nibbles of a code word as floats with the odd ones scaled by 16:
-// f[c] = nibble c (c even) or 16 nibble c (c odd), one mask per parity instead of a
-// shift and a mask.  The scale is a power of two, so a product or sum that carries it
-// rounds exactly as the unscaled one and dividing by 16 at the end restores it bit for bit.
-__device__ __forceinline__ void nibbles16_f32(uint32_t code, float* f) {
-  const uint32_t ev = code & 0x0F0F0F0Fu, od = code & 0xF0F0F0F0u;
-  f[0] = ubyte_f32<0>(ev);
-  f[1] = ubyte_f32<0>(od);
-  f[2] = ubyte_f32<1>(ev);
-  f[3] = ubyte_f32<1>(od);
-  f[4] = ubyte_f32<2>(ev);
-  f[5] = ubyte_f32<2>(od);
-  f[6] = ubyte_f32<3>(ev);
-  f[7] = ubyte_f32<3>(od);
-}
-
-// Inline asm is opaque to the compiler's hazard checks: ubyte_f32 only takes operands
-// made by bitwise ops, never by a transcendental op (v_exp and the like), whose result
-// a dependent VALU op on gfx950 may read only after a wait state.
 __device__ __forceinline__ uint32_t or4(uint32_t v) {
   v |= (uint32_t)__shfl_xor((int)v, 16);
   v |= (uint32_t)__shfl_xor((int)v, 32);
   return v;
 }
+
+// INT2 codes as fp16 pairs.  A lane's 32-bit word of INT2 codes holds two tokens, one
+// per 16-bit half, with channel c's crumb at bit crumb_bit(c) of each half.  A crumb at
+// bits 4-5, 6-7 or 8-9 of a half lies in an fp16 mantissa whose unit is 1 for the
+// exponents of 64, 16 and 4: masking the word to that crumb in both halves and ORing
+// in the exponent gives the exact pair (off + code of the low token, off + code of the
+// high token), one v_and_or_b32.  Three channels already sit there; w >> 6 and w << 4
+// bring the other five there, so a word takes 2 shifts and 8 v_and_or_b32 for its 16
+// codes.  The offsets come off once (the sum of q' off for keys, the sum of the weights
+// for values).
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__host__ __device__ constexpr int crumb_bit(int c) { return 2 * (c < 4 ? 2 * c : 2 * (c - 4) + 1); }
+
+// fp16 offset of channel c's pair (64, 16 or 4 by the bit its crumb is brought to)
+__host__ __device__ constexpr float int2_off(int c) {
+  return (c == 0 || c == 1 || c == 6) ? 64.f : (c == 2 || c == 7) ? 4.f : 16.f;
+}
+
+// v_and_or_b32 (x & mask) | base, written as an instruction because the compiler splits
+// it into an and and an or.  Inline asm is opaque to the compiler's hazard checks: it only
+// takes code words (loaded, shifted or combined by bitwise ops) and constants, never the
+// result of a transcendental op (v_exp and the like), which a dependent VALU op on gfx950
+// may read only after a wait state.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t base) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(base));
+  return r;
+}
+
+// The eight fp16 pairs of a word (pair c: channel c of the low and the high token).
+__device__ __forceinline__ void int2_pairs_f16(uint32_t w, uint32_t b64, uint32_t b16, uint32_t b4, uint32_t* pr) {
+  const uint32_t x1 = w >> 6, x2 = w << 4;
+  pr[0] = and_or(x2, 0x00300030u, b64);  // bits 0-1 -> 4-5
+  pr[1] = and_or(w, 0x00300030u, b64);   // bits 4-5
+  pr[2] = and_or(w, 0x03000300u, b4);    // bits 8-9
+  pr[3] = and_or(x1, 0x00C000C0u, b16);  // bits 12-13 -> 6-7
+  pr[4] = and_or(x2, 0x00C000C0u, b16);  // bits 2-3 -> 6-7
+  pr[5] = and_or(w, 0x00C000C0u, b16);   // bits 6-7
+  pr[6] = and_or(x1, 0x00300030u, b64);  // bits 10-11 -> 4-5
+  pr[7] = and_or(x1, 0x03000300u, b4);   // bits 14-15 -> 8-9
+}
+
+// INT4 codes as fp16 pairs.  A word of 8 nibbles (nibble c = channel c: K codes, or the
+// combined 4 hi + lo of V) holds channels c and c + 4 exactly 16 bits apart, so the same
+// mask-and-exponent step gives the pair (off + code of channel c, off + code of channel
+// c + 4): nibbles at bits 4-7 are units of fp16 64, at bits 6-9 units of fp16 16.
+// Channel pairs (0, 4) and (1, 5) take offset 64, (2, 6) and (3, 7) offset 16; three
+// shifts and four v_and_or_b32 per word of eight codes.
+__host__ __device__ constexpr float int4_off(int c) { return (c & 3) < 2 ? 64.f : 16.f; }
+
+__device__ __forceinline__ void int4_pairs_f16(uint32_t w, uint32_t b64, uint32_t b16, uint32_t* pr) {
+  pr[0] = and_or(w << 4, 0x00F000F0u, b64);  // nibbles 0, 4 -> bits 4-7 of each half
+  pr[1] = and_or(w, 0x00F000F0u, b64);       // nibbles 1, 5 at bits 4-7
+  pr[2] = and_or(w >> 2, 0x03C003C0u, b16);  // nibbles 2, 6 -> bits 6-9
+  pr[3] = and_or(w >> 6, 0x03C003C0u, b16);  // nibbles 3, 7 -> bits 6-9
+}
+
+__device__ __forceinline__ float f16_lo_f32(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16_hi_f32(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // One launch per cell: grid.x = n_splits far blocks + 1 near block.
 //   near block: exact bf16 attention over the sink [0, sink) and the tail
@@ -326,10 +354,10 @@ __device__ __forceinline__ uint32_t or4(uint32_t v) {
 // each lane takes one exponential, and the weights and hot bits reach the whole row
 // by lane broadcasts.
 template <int WAVES, bool TRACE, int BITS, bool RUNNING>
-// The kernel is VALU-bound; six waves per SIMD fit the fixed rule in 80 VGPRs and INT2
-// cells (no hot test) seven in 72 (the running rule keeps a page's scores across a barrier
-// and takes five; the traced variants, for tests, are left unconstrained).
-__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ? 7 : 6))) void cell_kernel(const CellParams p) {
+// The kernel is bound by VALU issue; six waves per SIMD fit the fixed rule and INT2 cells in
+// 80 VGPRs (the running rule keeps a page's scores across a barrier and takes five; the
+// traced variants, for tests, are left unconstrained).
+__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cell_kernel(const CellParams p) {
   constexpr int D = 128, E = 8;
   constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -363,6 +391,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   float zacc = 0.f;
+  float wacc = 0.f;  // far blocks: the running sum of the V weights (INT2: fp16-rounded), rescaled like o
 
   if (part == p.n_splits) {
     // ---------------- near block: sink and tail, bf16, own loop
@@ -418,9 +447,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
     // the key codes of odd channels are converted as 16 times their value (one mask per
     // nibble parity), so those channels' query entries carry 1/16: exact, and each product
     // (q / 16) (16 c) equals q c bit for bit
-    float qk[E];
-#pragma unroll
-    for (int c = 0; c < E; ++c) qk[c] = (c & 1) ? qf[c] * 0.0625f : qf[c];  // (the bias sums odd channels apart, times 16)
+    const uint32_t b64 = 0x54005400u, b16 = 0x4C004C00u, b4 = 0x44004400u;  // fp16 64, 16, 4 in both halves
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
     const int n_cp = (n_far + kCodePage - 1) / kCodePage;
@@ -449,25 +476,45 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
       load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
       // q' = q sigma and bias = q . z; fma with a zero addend so the fp16 operand folds into
       // v_fma_mix_f32 (q sigma is exact in fp32: bf16 x fp16)
-      float qs[E], bias_e = 0.f, bias_o = 0.f;
+      float qs[E], bias = 0.f;
 #pragma unroll
       for (int c = 0; c < E; ++c) {
-        qs[c] = fmaf(qk[c], f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
-        if (c & 1) bias_o = fmaf(qk[c], f16_to_f32(km.w[c] >> 16), bias_o);
-        else bias_e = fmaf(qk[c], f16_to_f32(km.w[c] >> 16), bias_e);
+        qs[c] = fmaf(qf[c], f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
+        bias = fmaf(qf[c], f16_to_f32(km.w[c] >> 16), bias);
       }
-      const float bias = fmaf(bias_o, 16.f, bias_e);
+      // the codes reach the scores as fp16 pairs (off + c) through v_fma_mix_f32 (the fp16
+      // operand converts exactly), and sum off q' comes off the bias
+#pragma unroll
+      for (int c = 0; c < E; ++c) bias = fmaf(BITS == 4 ? -int4_off(c) : -int2_off(c), qs[c], bias);
       float sc[8];  // slot s: the lane's K code word s, token g + 4 (s ^ (li >> 1)) (kslot)
+      if constexpr (BITS == 4) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t code;
-        if constexpr (BITS == 4) code = i < 4 ? k0.w[i] : k1.w[i - 4];
-        else code = lo_nibbles((k0.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-        float f[E];
-        nibbles16_f32(code, f);  // odd channels 16 times their code, against q / 16
-        sc[i] = bias;
+        for (int i = 0; i < 8; ++i) {
+          uint32_t pr[4];
+          int4_pairs_f16(i < 4 ? k0.w[i] : k1.w[i - 4], b64, b16, pr);
+          float sv = bias;
 #pragma unroll
-        for (int c = 0; c < E; ++c) sc[i] = fmaf(qs[c], f[c], sc[i]);
+          for (int c = 0; c < 4; ++c) {
+            sv = fmaf(qs[c], f16_lo_f32(pr[c]), sv);
+            sv = fmaf(qs[c + 4], f16_hi_f32(pr[c]), sv);
+          }
+          sc[i] = sv;
+        }
+      } else {
+        // word j holds slots 2 j and 2 j + 1; each channel's pair feeds both scores
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float sa = bias, sb = bias;
+          uint32_t pr[E];
+          int2_pairs_f16(k0.w[j], b64, b16, b4, pr);
+#pragma unroll
+          for (int c = 0; c < E; ++c) {
+            sa = fmaf(qs[c], f16_lo_f32(pr[c]), sa);
+            sb = fmaf(qs[c], f16_hi_f32(pr[c]), sb);
+          }
+          sc[2 * j] = sa;
+          sc[2 * j + 1] = sb;
+        }
       }
       // the row sums of the eight tokens, transposed: this lane keeps the score of its own
       // token g + 4 (li / 2) (base-2 units)
@@ -549,17 +596,37 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
         zacc = fmaf(x[i], f16_to_f32(vm.w[i] >> 16), zacc);        // + p z
         if (masked) zacc = fmaf(1.5f, hot[i] ? 0.f : wgt[i], zacc);  // cold: bucket midpoint
       }
-      // V codes: INT4 hot 4 hi + lo, cold 4 hi (the bucket midpoint's 1.5 is in zacc); INT2 the code
+      // V codes: INT4 hot 4 hi + lo, cold 4 hi (the bucket midpoint's 1.5 is in zacc)
+      if constexpr (BITS == 4) {
+        // the code word 4 hi + lo as fp16 pairs (off + c) through v_fma_mix_f32; wacc sums the
+        // weights, and off times it comes off each channel at the end
+        wacc *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t hw = (vh.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-        uint32_t code;
-        if constexpr (BITS == 4) code = hi_nibbles(hw) | lo_nibbles(lo16[i]);
-        else code = lo_nibbles(hw);
-        float f[E];
-        nibbles16_f32(code, f);  // odd channels accumulate 16 times their value
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t hw = (vh.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+          uint32_t pr[4];
+          int4_pairs_f16(hi_nibbles(hw) | lo_nibbles(lo16[i]), b64, b16, pr);
 #pragma unroll
-        for (int c = 0; c < E; ++c) o[c] = fmaf(wgt[i], f[c], o[c]);
+          for (int c = 0; c < 4; ++c) {
+            o[c] = fmaf(wgt[i], f16_lo_f32(pr[c]), o[c]);
+            o[c + 4] = fmaf(wgt[i], f16_hi_f32(pr[c]), o[c + 4]);
+          }
+          wacc += wgt[i];
+        }
+      } else {
+        // INT2: the weights of tokens 2 j and 2 j + 1 as an fp16 pair (nearest even) against
+        // each channel's pair (off + c), v_dot2c_f32_f16; wacc sums the same rounded weights,
+        // and off times it comes off each channel at the end
+        wacc *= alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f16x2_t wp = f16x2_t{(_Float16)wgt[2 * j], (_Float16)wgt[2 * j + 1]};
+          wacc = __builtin_amdgcn_fdot2(wp, f16x2_t{(_Float16)1.f, (_Float16)1.f}, wacc, false);
+          uint32_t pr[E];
+          int2_pairs_f16(vh.w[j], b64, b16, b4, pr);
+#pragma unroll
+          for (int c = 0; c < E; ++c) o[c] = __builtin_amdgcn_fdot2(wp, __builtin_bit_cast(f16x2_t, pr[c]), o[c], false);
+        }
       }
       if constexpr (TRACE) {
         const uint32_t word = or4(hotbits);
@@ -620,7 +687,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : (BITS == 2 ?
 
   if (part != p.n_splits) {
 #pragma unroll
-    for (int e = 1; e < E; e += 2) o[e] *= 0.0625f;  // undo the odd channels' scale of 16 (exact)
+    for (int e = 0; e < E; ++e) o[e] = fmaf(BITS == 4 ? -int4_off(e) : -int2_off(e), wacc, o[e]);  // the pairs' offsets
     st.l = 0.5f * row_sum16(st.l);  // lanes 2t and 2t + 1 hold equal sums, so this is exact
   }
 

@@ -6,14 +6,16 @@ split-K (32 sequences, 24 core layers x 4 loops, 16 heads x 128, bf16, context 8
 (layer, loop) planes resident, 206 GB).  One step runs every core layer at every loop
 as its own attention call, loop-major, as a looped model's sequential loops require;
 it yields batch * q * loops loop-query tokens.  Inputs are resident in HBM before
-timing starts.
+timing starts.  Without --workload the same run then times the Huginn-shaped RIPE
+decode (the other configuration with a bandwidth target) and reports it under
+"secondary".
 
 Prints one JSON line with the throughput, the roofline of the attention kernel
 (algorithmic bytes per launch / mean launch time from HIP events recorded
 around each launch on the launch stream) and the fp64 oracle's throughput on a
 bounded sample of the same workload on the host cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ouro_splitk] [--policy full|ripe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload W] [--policy full|ripe] [--also W,...]
 """
 from __future__ import annotations
 
@@ -67,7 +69,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="ouro_splitk",
+    ap.add_argument("--workload", default=None,
                     choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "huginn_draft", "loopkv_cells",
                              "raven_ripe", "dory_lastloop", "tiny"])
     ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
@@ -88,6 +90,9 @@ def parse():
     ap.add_argument("--v-tau", type=float, default=14.0, help="tau of the running-maximum rule")
     ap.add_argument("--v-offset", type=float, default=4.0,
                     help="fixed rule's offset: a far token is hot iff its score >= m0 - offset (the workload: 4.0)")
+    ap.add_argument("--also", default="auto",
+                    help="workloads timed after the first one in the same run, reported under 'secondary' "
+                         "(comma-separated; 'auto': huginn_ripe when no --workload is given, else none; 'none')")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     return ap.parse_args()
@@ -285,11 +290,9 @@ def cpu_baseline_cells(bc, seconds: float):
                       f"{rows_per_token} rows = 1 loop-query token"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
-        sys.exit(2)
+def run_workload(args, workload: str, prober, with_cpu: bool) -> dict:
+    """Build one workload in HBM, time it, and return its bench line (a dict)."""
+    import dataclasses
 
     import numpy as np
     import torch
@@ -298,10 +301,7 @@ def main():
     import synth
     import verify_attention_loop_amd as vla
 
-    vla.load()
-    torch.cuda.set_device(0)
-    prober = None if args.no_probe else ReadProbe()
-    w = synth.WORKLOADS[args.workload]
+    w = synth.WORKLOADS[workload]
     import dataclasses
     if args.batch > 0:
         w = dataclasses.replace(w, batch=args.batch)
@@ -419,13 +419,13 @@ def main():
     alg_bytes = float(np.mean(call_bytes))
     # achieved = algorithmic bytes of the sampled launches / their summed duration
     achieved = float(sum(call_bytes[n] for (_, n) in sampled)) / (kern.sum() / 1e3) / 1e9
-    khash = kernel_hash(args.workload)
+    khash = kernel_hash(workload)
     # the counters were taken on the workload as defined: its batch, splits and resident layers and, for
     # cells, the fixed rule at m0 - 4.0
     as_profiled = (args.batch <= 0 and args.split_k < 0 and args.layers <= 0 and
                    (not w.quant or (args.v_rule == "fixed" and args.v_offset == 4.0)))
-    policy_tag = "" if w.policy == synth.WORKLOADS[args.workload].policy else "_" + w.policy
-    traffic = read_traffic(args.workload + policy_tag, khash) if as_profiled else None
+    policy_tag = "" if w.policy == synth.WORKLOADS[workload].policy else "_" + w.policy
+    traffic = read_traffic(workload + policy_tag, khash) if as_profiled else None
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -448,10 +448,9 @@ def main():
             pb, pr = prober.rate(int(alg_bytes))
             probe = {"bytes": pb, "GBps": round(pr, 1), "frac": round(achieved / pr, 4)}
         probe.update(GBps_4GiB=round(r4, 1))
-        prober.close()
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if with_cpu and not args.no_cpu_baseline:
         cpu = cpu_baseline_cells(built, args.cpu_seconds) if w.quant else cpu_baseline(w, args.cpu_seconds)
 
     if w.quant:
@@ -507,6 +506,48 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (--gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import verify_attention_loop_amd as vla
+
+    vla.load()
+    torch.cuda.set_device(0)
+    prober = None if args.no_probe else ReadProbe()
+    # Without --workload: the largest single-GPU configuration (Ouro-shaped split-K, all layers resident), then
+    # the other configuration with a bandwidth target (Huginn-shaped RIPE decode), timed in the same run after
+    # the first workload's memory is released and reported in a compact block.
+    also = args.also
+    if also == "auto":
+        also = "huginn_ripe" if args.workload is None else "none"
+    workload = args.workload or "ouro_splitk"
+    line = run_workload(args, workload, prober, with_cpu=True)
+    if also != "none":
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        line["secondary"] = []
+        for wl in also.split(","):
+            sub = run_workload(args, wl, prober, with_cpu=False)
+            r = sub["roofline"]
+            line["secondary"].append({
+                "workload": wl, "value": sub["value"], "unit": sub["unit"], "ms_per_step": sub["ms_per_step"],
+                "steps": sub["steps"], "config": sub["config"],
+                "roofline": {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel",
+                                               "algorithmic_bytes_per_launch", "mean_launch_us", "launches_timed",
+                                               "step_GBps", "kernel_hash", "read_probe")}})
+            gc.collect()
+            torch.cuda.empty_cache()
+    if prober is not None:
+        prober.close()
     print(json.dumps(line))
 
 

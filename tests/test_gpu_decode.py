@@ -277,3 +277,34 @@ def test_split_merge_is_deterministic():
     got = np.array([o[b, 0, h] for b in range(8) for h in (0, 7)])
     assert np.abs(got - want).max() <= TOL_BF16
     built.cache.close()
+
+
+@pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 20), (vla.POLICY_RIPE, 0)])
+def test_traced_physical_slots_hold_the_oracle_planes_keys(policy, W):
+    """The physical half of the index trace, checked by content: for every key position j a row reads, the pool
+    bytes at the traced physical page and slot (head 0's K row) equal, bit for bit, the generator's key of
+    position j in the plane the oracle names (RIPE page, Sec. 2 policy pi and Eq. (9) with the block rule).  This
+    pins the page resolution to the oracle and the seeded generator, not to the library's own tables."""
+    w = _ragged(96)
+    lengths = [1, 15, 16, 17, 100, 257]
+    built = harness.build_plain(w, lengths=lengths, layers=(1,), policy=policy, window=W, shuffle=True,
+                                poison=True)
+    pool = built.cache._keep[0].cpu().numpy()
+    page_bytes = vla.LoopCache.sizes(built.cache.cfg).page_bytes
+    D, R = w.head_dim, w.n_loops
+    for loop in (0, 2, R - 1):
+        q = harness.gpu_queries(built, 1, loop, 1)
+        _, _, tr = _attend(built, 1, loop, q, 2, trace_len=max(lengths))
+        t = tr.cpu().numpy()
+        for b, L in enumerate(lengths):
+            pm = oracle.plane_map(policy, loop, R, L - 1, L - 1, L, W)
+            np.testing.assert_array_equal(t[b, 0, :L, 0], pm)
+            for plane in set(pm.tolist()):
+                want = synth.kv(w.dtype, w.seed, synth.T_K, built.rows[b], 1, plane, w.hkv, D, 0, L, w.mode, R,
+                                w.scale, heads=[0])[:, 0, :]  # bf16 bits [L][D]
+                for j in np.flatnonzero(pm == plane):
+                    phys, slot = divmod(int(t[b, 0, j, 1]), 16)
+                    off = phys * page_bytes + slot * D * 2  # head 0's K block: [token][channel]
+                    got = pool[off:off + D * 2].view(np.uint16)
+                    assert np.array_equal(got, want[j]), (loop, b, j, plane)
+    built.cache.close()

@@ -236,3 +236,32 @@ def test_huginn_draft_full_size_sampled():
                 want, _ = oracle.attend_row(qq, ko, vo, kd, vd, L - 1, n, vla.POLICY_RIPE, loop, R, 0)
                 assert np.abs(o[b, 0, h] - want).max() <= TOL_BF16, (loop, g, b, h)
     built.cache.close()
+
+
+@pytest.mark.parametrize("policy,W", [(vla.POLICY_FULL, 0), (vla.POLICY_RIPE, 7)])
+def test_verify_traced_physical_slots_hold_the_oracle_planes_keys(policy, W):
+    """The physical half of the verify trace, checked by content: for every (block row, key) the pool bytes at the
+    traced physical page and slot (head 0's K row) equal the generator's key of that position in the plane the
+    oracle names (RIPE page, Eq. (9); block positions read the own plane, proof of Prop. 1)."""
+    w = _wl(96)
+    lengths = [8, 21, 100, 300]
+    k = 8
+    built = harness.build_plain(w, lengths=lengths, policy=policy, window=W, q_len=k, shuffle=True, poison=True)
+    pool = built.cache._keep[0].cpu().numpy()
+    page_bytes = vla.LoopCache.sizes(built.cache.cfg).page_bytes
+    D, R = w.head_dim, w.n_loops
+    for loop in (0, R - 1):
+        q = harness.gpu_queries(built, 0, loop, k)
+        _, _, tr = _verify(built, 0, loop, q, 2, trace_len=300)
+        t = tr.cpu().numpy()
+        for b, L in enumerate(lengths):
+            keys = {p: synth.kv(w.dtype, w.seed, synth.T_K, built.rows[b], 0, p, w.hkv, D, 0, L, w.mode, R, w.scale,
+                                heads=[0])[:, 0, :] for p in (loop, R - 1)}
+            for i in range(k):
+                pm = oracle.plane_map(policy, loop, R, L - k + i, L - k, 300, W)
+                np.testing.assert_array_equal(t[b, i, :, 0], pm)
+                for j in range(L - k + i + 1):
+                    phys, slot = divmod(int(t[b, i, j, 1]), 16)
+                    off = phys * page_bytes + slot * D * 2
+                    assert np.array_equal(pool[off:off + D * 2].view(np.uint16), keys[int(pm[j])][j]), (loop, b, i, j)
+    built.cache.close()

@@ -99,21 +99,33 @@ def test_all_hot_cell_reads_full_int4_codes_bitwise_equal_to_negative_infinite_t
 
 
 @pytest.mark.slow
-def test_loopkv_full_shape_sampled():
+@pytest.mark.parametrize("layer", [0, 14])
+def test_loopkv_full_shape_sampled(layer):
     """The LoopKV-shaped workload at full length: 16 sequences, L = 16384 (sink 4, far 16252, tail 128),
-    16 heads x 128, seeded plan over layer 0's four loops; sampled rows and their masks."""
+    16 heads x 128, the seeded plan's cells of one layer's four loops (layer 0: four INT4 cells; layer 14: INT2,
+    shared, shared, INT4); sampled rows and their masks with the hot-mask trace on (the traced kernel
+    instance), and sampled rows in the launch configuration the benchmark times (untraced kernel, the
+    library's split choice)."""
     w = synth.WORKLOADS["loopkv_cells"]
     plan = synth.cell_plan(w.seed, w.n_layers, w.n_loops)
-    bc = harness.build_cells(w, layers=(0,), plan=plan)
-    rng = np.random.default_rng(4)
+    bc = harness.build_cells(w, layers=(layer,), plan=plan)
+    rng = np.random.default_rng(4 + layer)
     n_far = w.length - w.sink - w.tail
     for loop in range(w.n_loops):
-        out, lse, mask = _attend_cells(bc, 0, loop, 4.0)
+        out, lse, mask = _attend_cells(bc, layer, loop, 4.0)
         assert np.isfinite(out).all()
+        q = harness.gpu_queries(bc, layer, loop, 1)
+        plain = torch.empty_like(q)
+        ws = torch.empty(bc.cache.lkv_workspace_bytes(layer, loop, bc.seqs) + 4, dtype=torch.uint8, device="cuda")
+        bc.cache.lkv_attend(layer, loop, bc.seqs, q, plain, workspace=ws, v_thresh_offset=4.0)
+        torch.cuda.synchronize()
+        plain = harness.out_f64(plain)
+        assert np.isfinite(plain).all()
         for _ in range(4):
             b, h = int(rng.integers(w.batch)), int(rng.integers(w.n_heads))
-            want, want_lse, hot, s_far, thr = harness.cell_oracle_row(bc, b, 0, loop, h, 4.0)
+            want, want_lse, hot, s_far, thr = harness.cell_oracle_row(bc, b, layer, loop, h, 4.0)
             assert np.abs(out[b, 0, h] - want).max() <= TOL
+            assert np.abs(plain[b, 0, h] - want).max() <= TOL
             got = _bits(mask[b, h], n_far)
             near = np.abs(s_far - thr) <= BAND
             assert np.array_equal(got[~near], hot[~near])

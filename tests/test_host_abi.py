@@ -421,3 +421,29 @@ def test_noalloc_refuses_workspace_and_oversized_calls_before_device_work(lib):
     a.workspace, a.workspace_bytes = 1 << 42, 1 << 20
     assert lib.lkv_attend_noalloc(c.h, ctypes.byref(a), 0) == vla.LKV_EINVAL
     assert b"no workspace" in lib.lkv_last_error(c.h)
+
+
+def test_quantised_plane_appends_keep_sink_then_tail_without_gaps(lib):
+    """Quantised caches hold the exact sink and tail in their bf16 planes (LoopKV page, Sec. 3.2): after the sink the
+    far history may be skipped (it comes as code pages), but any other gap is refused, and the tail grows one
+    position after another."""
+    cfg = vla.LoopCache.config(n_layers=1, n_loops=4, n_heads_q=2, n_heads_kv=2, head_dim=128,
+                               kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=2, max_len=512,
+                               max_block=1, quant=1, sink=4, tail=32)
+    ha = HostArenas(cfg, 64, 16, 16)
+    c = vla.LoopCache(cfg, ha.ar, 0)
+    c._host_arenas = ha
+    c.lkv_set_plan(np.array([[vla.CELL_INT4, vla.CELL_INT2, vla.CELL_SHARED, vla.CELL_INT4]], dtype=np.int8))
+    s = c.lkv_add_seq()
+    c.lkv_reserve(s, 0, 0, 0, 4)          # sink
+    c.lkv_reserve(s, 0, 0, 200 - 32, 32)  # tail of a 200-token sequence; the far history comes as codes
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_reserve(s, 0, 0, 205, 1)    # a gap after the tail
+    assert e.value.status == vla.LKV_ESTATE
+    c.lkv_reserve(s, 0, 0, 200, 3)        # the tail grows
+    assert c.lkv_seq_info(s) == (203, 0)
+    s2 = c.lkv_add_seq()
+    c.lkv_reserve(s2, 0, 1, 0, 2)
+    with pytest.raises(vla.LkvError) as e:
+        c.lkv_reserve(s2, 0, 1, 3, 1)     # a gap inside the sink
+    assert e.value.status == vla.LKV_ESTATE

@@ -19,7 +19,7 @@ def test_f16_conversion_matches_numpy_ieee_half():
     for x in vals:
         want = int(np.array([x], dtype=np.float32).astype(np.float16).view(np.uint16)[0])
         assert oracle.f16_from_f32(float(x)) == want, x
-    for h in range(0, 0x10000, 7):
+    for h in range(0, 0x10000):
         if (h & 0x7C00) == 0x7C00 and (h & 0x3FF):
             continue  # NaN payloads
         want = float(np.array([h], dtype=np.uint16).view(np.float16).astype(np.float32)[0])

@@ -777,11 +777,21 @@ int auto_splits(const lkv_cache* c, int n_seqs, int mode, int q_len, int max_pag
   return std::max(1, std::min(s, 64));
 }
 
-// Far splits of a quantised-cell call: enough (split, head, seq) workgroups to fill the
-// chip, at most one per code page and at most 64.
-int cell_splits(const lkv_cache* c, int n_seqs, int split_k, int max_code_pages) {
+// Far splits of a quantised-cell call, at most one per code page and at most 64.  INT4 and
+// shared cells under the fixed rule run a software-pipelined far loop (a wave computes the
+// next page's scores while the current page's lo rows are in flight) at five waves per SIMD,
+// which pays off over long runs of pages: they take as many splits as keep the whole grid,
+// near blocks included, resident at once (five 4-wave workgroups per CU on the 256 CUs;
+// one split more and the last far blocks start a whole block late; measured on MI355X).
+// Other cells take enough (split, head, seq) workgroups to fill the chip several times.
+constexpr int kCellPipelinedWgs = 5 * 256;
+
+int cell_splits(const lkv_cache* c, int n_seqs, int split_k, int max_code_pages, int bits, int rule) {
   const int rows = n_seqs * c->cfg.n_heads_q;
-  int S = split_k > 0 ? split_k : std::max(1, std::min(64, (kTargetWgs + rows - 1) / rows));
+  int S;
+  if (split_k > 0) S = split_k;
+  else if (bits == 4 && rule == LKV_VRULE_FIXED) S = std::max(1, std::min(64, kCellPipelinedWgs / rows - 1));
+  else S = std::max(1, std::min(64, (kTargetWgs + rows - 1) / rows));
   return std::min(S, std::max(1, max_code_pages));
 }
 
@@ -799,7 +809,9 @@ lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, siz
     max_pages = std::max(max_pages, (L + kPage - 1) / kPage);
     max_cp = std::max(max_cp, (std::max(0, L - c->cfg.sink - c->cfg.tail) + kCodePage - 1) / kCodePage);
   }
-  const int S = c->cfg.quant ? cell_splits(c, a->n_seqs, a->split_k, max_cp)
+  // (quantised caches: the larger of the two cell rules, whatever the (layer, loop) cell is)
+  const int S = c->cfg.quant ? std::max(cell_splits(c, a->n_seqs, a->split_k, max_cp, 2, a->v_rule),
+                                        cell_splits(c, a->n_seqs, a->split_k, max_cp, 4, a->v_rule))
                              : (a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, a->q_len, max_pages));
   const int parts = c->cfg.quant ? S + 1 : S;
   if (parts <= 1) {
@@ -982,7 +994,7 @@ static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_
   }
   const int D = cfg.head_dim, hq = cfg.n_heads_q;
   const int max_cp = (max_far + kCodePage - 1) / kCodePage;
-  const int S = cell_splits(c, a->n_seqs, a->split_k, max_cp);
+  const int S = cell_splits(c, a->n_seqs, a->split_k, max_cp, bits, a->v_rule);
   const size_t ws_need = (size_t)a->n_seqs * hq * (S + 1) * (D + 1) * 4;
   if (!a->workspace || a->workspace_bytes < ws_need)
     return c->fail(LKV_ENOMEM, "workspace of %zu bytes needed", ws_need);

@@ -264,9 +264,18 @@ __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-// Nibble c of the result = 4 hi_c (bits 2-3) / lo_c (bits 0-1) from a lane's crumb word.
-__device__ __forceinline__ uint32_t hi_nibbles(uint32_t x) { return (x | (x << 18)) & 0xCCCCCCCCu; }
-__device__ __forceinline__ uint32_t lo_nibbles(uint32_t y) { return (y | (y << 14)) & 0x33333333u; }
+// V codes 4 hi + lo of two tokens a, b from their crumb words: hi = H (a in the low half,
+// b in the high half), lo = L (same).  Channels c < 4 have hi at odd and lo at even crumbs
+// (crumbs 2c + 1 and 2c), so one bit-field select of the odd crumbs of H and the even
+// crumbs of L gives nibble c = 4 hi_c + lo_c in each half; channels c >= 4 have them the
+// other way round (hi at crumb 2(c - 4), lo at 2(c - 4) + 1), and H << 2, L >> 2 move
+// them to the same places (a crumb that crosses into the other half lands in the part the
+// select drops).  Each half of the two results holds the nibbles of channels 0-3 resp.
+// 4-7 of its token.
+__device__ __forceinline__ uint32_t vcodes_lo4(uint32_t H, uint32_t L) { return (H & 0xCCCCCCCCu) | (L & 0x33333333u); }
+__device__ __forceinline__ uint32_t vcodes_hi4(uint32_t H, uint32_t L) {
+  return ((H << 2) & 0xCCCCCCCCu) | ((L >> 2) & 0x33333333u);
+}
 
 __device__ __forceinline__ uint32_t or4(uint32_t v) {
   v |= (uint32_t)__shfl_xor((int)v, 16);
@@ -316,12 +325,12 @@ __device__ __forceinline__ void int2_pairs_f16(uint32_t w, uint32_t b64, uint32_
   pr[7] = and_or(x1, 0x03000300u, b4);   // bits 14-15 -> 8-9
 }
 
-// INT4 codes as fp16 pairs.  A word of 8 nibbles (nibble c = channel c: K codes, or the
-// combined 4 hi + lo of V) holds channels c and c + 4 exactly 16 bits apart, so the same
-// mask-and-exponent step gives the pair (off + code of channel c, off + code of channel
-// c + 4): nibbles at bits 4-7 are units of fp16 64, at bits 6-9 units of fp16 16.
-// Channel pairs (0, 4) and (1, 5) take offset 64, (2, 6) and (3, 7) offset 16; three
-// shifts and four v_and_or_b32 per word of eight codes.
+// INT4 codes as fp16 pairs.  A word of 8 nibbles holds nibbles k and k + 4 exactly 16 bits
+// apart, so the same mask-and-exponent step gives the pair (off + nibble k, off + nibble
+// k + 4): nibbles at bits 4-7 are units of fp16 64, at bits 6-9 units of fp16 16.  In a K
+// code word nibble c is channel c of one token, so pair k is channels (k, k + 4); in the V
+// words of vcodes_lo4 / vcodes_hi4 pair k is one channel of two tokens.  Pairs 0 and 1 take
+// offset 64, 2 and 3 offset 16; three shifts and four v_and_or_b32 per word of eight codes.
 __host__ __device__ constexpr float int4_off(int c) { return (c & 3) < 2 ? 64.f : 16.f; }
 
 __device__ __forceinline__ void int4_pairs_f16(uint32_t w, uint32_t b64, uint32_t b16, uint32_t* pr) {
@@ -329,6 +338,28 @@ __device__ __forceinline__ void int4_pairs_f16(uint32_t w, uint32_t b64, uint32_
   pr[1] = and_or(w, 0x00F000F0u, b64);       // nibbles 1, 5 at bits 4-7
   pr[2] = and_or(w >> 2, 0x03C003C0u, b16);  // nibbles 2, 6 -> bits 6-9
   pr[3] = and_or(w >> 6, 0x03C003C0u, b16);  // nibbles 3, 7 -> bits 6-9
+}
+
+// A code page's head slice as a buffer resource (base and size in scalar registers): each
+// load then takes the page in the resource and a 32-bit lane offset, loop-invariant per
+// load site, instead of a 64-bit address pair per lane; loads past the slice return 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t slice_rsrc(const uint8_t* hb, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(hb), 0, (int)bytes, 0x00020000);
+}
+
+// NB bytes (16 or 32) at byte offset off of the resource; NT: nontemporal (whole lines only)
+// (SOFF, a constant, goes in the instruction's scalar offset)
+template <int NB, bool NT, int SOFF = 0>
+__device__ __forceinline__ void buf_load(Raw<NB>& r, rsrc_t rs, uint32_t off) {
+#pragma unroll
+  for (int o = 0; o < NB; o += 16) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, SOFF + o, NT ? 2 : 0);
+    r.w[o / 4 + 0] = v.x;
+    r.w[o / 4 + 1] = v.y;
+    r.w[o / 4 + 2] = v.z;
+    r.w[o / 4 + 3] = v.w;
+  }
 }
 
 __device__ __forceinline__ float f16_lo_f32(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
@@ -354,10 +385,11 @@ __device__ __forceinline__ float f16_hi_f32(uint32_t w) { return (float)__builti
 // each lane takes one exponential, and the weights and hot bits reach the whole row
 // by lane broadcasts.
 template <int WAVES, bool TRACE, int BITS, bool RUNNING>
-// The kernel is bound by VALU issue; six waves per SIMD fit the fixed rule and INT2 cells in
-// 80 VGPRs (the running rule keeps a page's scores across a barrier and takes five; the
-// traced variants, for tests, are left unconstrained).
-__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cell_kernel(const CellParams p) {
+// Five waves per SIMD (96 VGPRs) for INT4 and shared cells, whose fixed-rule loop holds one
+// page's value-phase state while it computes the next page's scores, and for the running rule
+// (a page's scores across a barrier); six (80 VGPRs) for INT2 cells.  The traced variants, for
+// tests, are left unconstrained.
+__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING || BITS == 4 ? 5 : 6)) void cell_kernel(const CellParams p) {
   constexpr int D = 128, E = 8;
   constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -369,18 +401,14 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
   const int n_far = L - p.sink - p.tail;
   const int tail_lo = L - p.tail;
 
-  // q: this lane's channels 8 li .. 8 li + 7, as bf16 pairs (dot2) and as floats
-  float qf[E];
+  // q: this lane's channels 8 li .. 8 li + 7, as bf16 pairs (dot2; converted per page in the
+  // far blocks)
   uint32_t qw[E / 2];
   {
     Raw<16> r;
     load_raw<16>(r, reinterpret_cast<const uint8_t*>(p.q) + (((int64_t)b * p.hq + h) * D + li * E) * 2);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      qw[x] = r.w[x];
-      qf[2 * x] = bf_lo(r.w[x]);
-      qf[2 * x + 1] = bf_hi(r.w[x]);
-    }
+    for (int x = 0; x < 4; ++x) qw[x] = r.w[x];
   }
   const int32_t* tab_near = p.tab_near + (int64_t)slot * p.ring_near;
   const uint64_t koff = (uint64_t)hk * HEADB + (uint64_t)li * 16;
@@ -457,30 +485,41 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
     constexpr uint64_t head_bytes = (uint64_t)(BITS == 4 ? 40 : 24) * D;
     constexpr uint64_t vcode_off = BITS == 4 ? 20 * D : 12 * D;
     constexpr uint64_t vmeta_off = BITS == 4 ? 36 * D : 20 * D;
+    // the lane's byte offsets inside a page's head slice, 32-bit so that each load takes the
+    // page's address in scalar registers plus one lane offset (lane = 16 g + li)
+    const uint32_t off_km = (uint32_t)li * 32u, off_k = 4u * D + (uint32_t)lane * 16u;
+    const uint32_t off_vm = (uint32_t)vmeta_off + (uint32_t)(g * 4 + (li >> 2)) * 32u;
+    const uint32_t off_lo = 28u * D + (uint32_t)g * 32u + (uint32_t)li * 2u;  // V lo of token g
 
     // Key phase of code page cp: loads, K dequant folded into q (LoopKV page, App. E: the
     // per-channel scale multiplies the query, the zero becomes a bias), and the score of
     // the lane's token g + 4 (li / 2) in base-2 units (xs; -inf past the sequence); the V
     // codes and V meta are loaded here too.  A score is bias + sum_c q'_c c_jc over the
     // lane's 8 channels for each of its 8 tokens, then the transposed 16-lane sum.
-    auto far_keys = [&](int cp, const uint8_t*& hb, float& xs, Raw<16>& vh, Raw<32>& vm) {
-      hb = p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes;
-      // Issue the page's loads together: K meta of the lane's 8 channels, K codes, V hi
-      // (or INT2 V codes), V meta.
+    auto far_keys = [&](int cp, rsrc_t& rs, float& xs, Raw<16>& vh, Raw<32>& vm) {
+      rs = slice_rsrc(p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes, head_bytes);
+      // Issue the page's loads together: K meta of the lane's 8 channels, K codes, INT2 V
+      // codes, V meta (INT4 V hi goes out with the lo rows in the value phase).
       Raw<32> km;
-      load_raw<32>(km, hb + li * 32);
+      buf_load<32, false>(km, rs, off_km);
       Raw<16> k0, k1;
-      load_stream<16>(k0, hb + 4 * D + (g * 16 + li) * 16);
-      if constexpr (BITS == 4) load_stream<16>(k1, hb + 4 * D + 1024 + (g * 16 + li) * 16);
-      load_stream<16>(vh, hb + vcode_off + (g * 16 + li) * 16);
-      load_raw<32>(vm, hb + vmeta_off + ((g * 4 + (li >> 2)) * 8) * 4);
+      buf_load<16, true>(k0, rs, off_k);
+      if constexpr (BITS == 4) buf_load<16, true, 1024>(k1, rs, off_k);
+      if constexpr (BITS == 2) buf_load<16, true, (int)(vcode_off - 4 * D)>(vh, rs, off_k);  // INT2 V codes
+      buf_load<32, false>(vm, rs, off_vm);
+      // In the pipelined loop the previous page's accumulation follows this key phase; keep
+      // the scheduler from moving any of it above these loads, where it would wait for the
+      // previous page's lo rows before the loads go out.
+      if constexpr (masked && !RUNNING) __builtin_amdgcn_sched_barrier(0);
       // q' = q sigma and bias = q . z; fma with a zero addend so the fp16 operand folds into
       // v_fma_mix_f32 (q sigma is exact in fp32: bf16 x fp16)
       float qs[E], bias = 0.f;
 #pragma unroll
       for (int c = 0; c < E; ++c) {
-        qs[c] = fmaf(qf[c], f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
-        bias = fmaf(qf[c], f16_to_f32(km.w[c] >> 16), bias);
+        // q_c from the bf16 pairs per page (4 registers across the loop instead of 8)
+        const float qc = (c & 1) ? bf_hi(qw[c >> 1]) : bf_lo(qw[c >> 1]);
+        qs[c] = fmaf(qc, f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
+        bias = fmaf(qc, f16_to_f32(km.w[c] >> 16), bias);
       }
       // the codes reach the scores as fp16 pairs (off + c) through v_fma_mix_f32 (the fp16
       // operand converts exactly), and sum off q' comes off the bias
@@ -488,8 +527,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
       for (int c = 0; c < E; ++c) bias = fmaf(BITS == 4 ? -int4_off(c) : -int2_off(c), qs[c], bias);
       float sc[8];  // slot s: the lane's K code word s, token g + 4 (s ^ (li >> 1)) (kslot)
       if constexpr (BITS == 4) {
+        // slots s and 7 - s one after the other: the transposed row sum's first step pairs them,
+        // so few scores are held at once
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int k = 0; k < 8; ++k) {
+          const int i = (k & 1) ? 7 - (k >> 1) : (k >> 1);
           uint32_t pr[4];
           int4_pairs_f16(i < 4 ? k0.w[i] : k1.w[i - 4], b64, b16, pr);
           float sv = bias;
@@ -519,22 +561,27 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
       // the row sums of the eight tokens, transposed: this lane keeps the score of its own
       // token g + 4 (li / 2) (base-2 units)
       xs = row_sum16_t8(sc) * p.scale_log2;
-      // Past the sequence (last page only): score -inf and V meta cleared, so that those
-      // tokens get zero weight against finite scales whatever the page holds there.
-      // (tested as "the last code page": the past-the-end tests below imply "the page ends
-      // past the history", so with that test the compiler dropped the branch and ran them on
-      // every page)
+      // Past the sequence (last page only): score -inf here, and far_head clears those
+      // tokens' V meta, so that they get zero weight against finite scales whatever the page
+      // holds there.  (Tested as "the last code page": the past-the-end test implies "the
+      // page ends past the history", so with that test the compiler dropped the branch and
+      // ran it on every page.)
       if (cp == n_cp - 1) {
         if (cp * kCodePage + g + 4 * (li >> 1) >= n_far) xs = -INFINITY;
+      }
+    };
+
+    // Value phase, first half: hot test against thr2 (base-2 units), online softmax (the
+    // accumulators are rescaled here), the loads of the V lo rows of hot tokens, and the V
+    // dequant folded into the weights, which leave as fp16 pairs wpk[j] for tokens 2 j and
+    // 2 j + 1 (nearest even); wacc sums the same rounded weights.
+    auto far_head = [&](int cp, rsrc_t rs, float xs, float thr2, Raw<32> vm, uint32_t* wpk,
+                        uint32_t* lo16, Raw<16>& vh) {
+      if (cp == n_cp - 1) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (cp * kCodePage + g + 4 * i >= n_far) vm.w[i] = 0u;
       }
-    };
-
-    // Value phase: hot test against thr2 (base-2 units), online softmax, V lo of hot tokens,
-    // V dequant folded into the weights, accumulation.
-    auto far_values = [&](int cp, const uint8_t* hb, float xs, float thr2, const Raw<16>& vh, const Raw<32>& vm) {
       // A finite threshold keeps tokens past the sequence (score -inf) cold under any rule,
       // and leaves every finite score hot when the rule's threshold is -inf.
       thr2 = fmaxf(thr2, -3.402823466e38f);  // -FLT_MAX
@@ -577,14 +624,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
 #pragma unroll
       for (int c = 0; c < E; ++c) o[c] *= alpha;
       zacc *= alpha;
-      // V lo rows of the hot tokens only (INT4 and shared cells; LoopKV page, Sec. 3.3)
-      uint32_t lo16[8];
-      const uint16_t* lo_row = reinterpret_cast<const uint16_t*>(hb + 28 * D + g * 32 + li * 2);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo16[i] = 0u;
-        if (masked && hot[i]) lo16[i] = lo_row[i * 64];  // token g + 4 i
-      }
+      wacc *= alpha;
       // V meta of the lane's group for its 8 tokens; fold scale and zero into the weights
       // (tokens past the sequence have p = 0 and cleared meta)
       float wgt[8];
@@ -596,37 +636,28 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
         zacc = fmaf(x[i], f16_to_f32(vm.w[i] >> 16), zacc);        // + p z
         if (masked) zacc = fmaf(1.5f, hot[i] ? 0.f : wgt[i], zacc);  // cold: bucket midpoint
       }
-      // V codes: INT4 hot 4 hi + lo, cold 4 hi (the bucket midpoint's 1.5 is in zacc)
-      if constexpr (BITS == 4) {
-        // the code word 4 hi + lo as fp16 pairs (off + c) through v_fma_mix_f32; wacc sums the
-        // weights, and off times it comes off each channel at the end
-        wacc *= alpha;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t hw = (vh.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-          uint32_t pr[4];
-          int4_pairs_f16(hi_nibbles(hw) | lo_nibbles(lo16[i]), b64, b16, pr);
+      for (int j = 0; j < 4; ++j) {
+        const f16x2_t wp = f16x2_t{(_Float16)wgt[2 * j], (_Float16)wgt[2 * j + 1]};
+        wacc = __builtin_amdgcn_fdot2(wp, f16x2_t{(_Float16)1.f, (_Float16)1.f}, wacc, false);
+        wpk[j] = __builtin_bit_cast(uint32_t, wp);
+      }
+      // The V meta is used up above, before the conditional lo loads: a wait for a load issued
+      // before loads that may or may not go out has to assume they did not, and so would wait
+      // for them too.  The lo loads take their lane offset through an empty statement that also
+      // takes the sums depending on every use of the V meta, so the compiler cannot sink those
+      // uses below the loads.
+      uint32_t lo_off = off_lo;
+      if constexpr (masked) asm("" : "+v"(lo_off) : "v"(wacc), "v"(zacc));
+      // INT4 and shared cells: the V hi plane goes out with the V lo rows of the hot tokens
+      // only (LoopKV page, Sec. 3.3), one memory round trip; the key phase does not need it
+      if constexpr (BITS == 4) buf_load<16, true, (int)(vcode_off - 4 * D)>(vh, rs, off_k);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            o[c] = fmaf(wgt[i], f16_lo_f32(pr[c]), o[c]);
-            o[c + 4] = fmaf(wgt[i], f16_hi_f32(pr[c]), o[c + 4]);
-          }
-          wacc += wgt[i];
-        }
-      } else {
-        // INT2: the weights of tokens 2 j and 2 j + 1 as an fp16 pair (nearest even) against
-        // each channel's pair (off + c), v_dot2c_f32_f16; wacc sums the same rounded weights,
-        // and off times it comes off each channel at the end
-        wacc *= alpha;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f16x2_t wp = f16x2_t{(_Float16)wgt[2 * j], (_Float16)wgt[2 * j + 1]};
-          wacc = __builtin_amdgcn_fdot2(wp, f16x2_t{(_Float16)1.f, (_Float16)1.f}, wacc, false);
-          uint32_t pr[E];
-          int2_pairs_f16(vh.w[j], b64, b16, b4, pr);
-#pragma unroll
-          for (int c = 0; c < E; ++c) o[c] = __builtin_amdgcn_fdot2(wp, __builtin_bit_cast(f16x2_t, pr[c]), o[c], false);
-        }
+      for (int i = 0; i < 8; ++i) {
+        lo16[i] = 0u;
+        // token g + 4 i: the token's part of the offset goes in the scalar offset, so that all
+        // eight loads share the lane's one offset register
+        if (masked && hot[i]) lo16[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, lo_off, 128 * i, 0);
       }
       if constexpr (TRACE) {
         const uint32_t word = or4(hotbits);
@@ -634,16 +665,73 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
       }
     };
 
+    // Value phase, second half: the V codes against the weight pairs, v_dot2c_f32_f16 (the
+    // bucket midpoint 1.5 of cold tokens is in zacc, the pairs' offsets come off at the end).
+    auto far_tail = [&](const Raw<16>& vh, const uint32_t* lo16, const uint32_t* wpk) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x2_t wp = __builtin_bit_cast(f16x2_t, wpk[j]);
+        if constexpr (BITS == 4) {
+          // tokens 2 j and 2 j + 1 (word j of V hi) together: codes 4 hi + lo as fp16 pairs (off
+          // + c of token 2 j, off + c of token 2 j + 1) per channel; a cold token's lo is 0.
+          // L = lo16[2 j] | lo16[2 j + 1] << 16 as one byte permute of both loads: an op on one
+          // conditional load alone would be moved into its branch, with a wait right after the load
+          const uint32_t H = vh.w[j], L = __builtin_amdgcn_perm(lo16[2 * j + 1], lo16[2 * j], 0x05040100u);
+          uint32_t pr[4];
+          int4_pairs_f16(vcodes_lo4(H, L), b64, b16, pr);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) o[c] = __builtin_amdgcn_fdot2(wp, __builtin_bit_cast(f16x2_t, pr[c]), o[c], false);
+          int4_pairs_f16(vcodes_hi4(H, L), b64, b16, pr);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            o[c + 4] = __builtin_amdgcn_fdot2(wp, __builtin_bit_cast(f16x2_t, pr[c]), o[c + 4], false);
+        } else {
+          // INT2: each channel's pair (off + c of token 2 j, off + c of token 2 j + 1)
+          uint32_t pr[E];
+          int2_pairs_f16(vh.w[j], b64, b16, b4, pr);
+#pragma unroll
+          for (int c = 0; c < E; ++c) o[c] = __builtin_amdgcn_fdot2(wp, __builtin_bit_cast(f16x2_t, pr[c]), o[c], false);
+        }
+      }
+    };
+
     if constexpr (!RUNNING || !masked) {
       // Fixed rule: hot iff s >= m0 - offset.
       const float thr2 = (m0 - p.thr_offset) * kLog2e;
-      for (int cp = c0 + w; cp < c1; cp += WAVES) {
-        const uint8_t* hb;
-        float xs;
-        Raw<16> vh;
-        Raw<32> vm;
-        far_keys(cp, hb, xs, vh, vm);
-        far_values(cp, hb, xs, thr2, vh, vm);
+      if constexpr (masked) {
+        // INT4 and shared cells: a page's lo rows need its scores, so the wave computes the
+        // next page's key phase while they are in flight (one memory round trip per page
+        // instead of two); the loop's last page leaves it, so no load sits in a branch.
+        int cp = c0 + w;
+        if (cp < c1) {
+          rsrc_t rs;
+          float xs;
+          Raw<16> vh;
+          Raw<32> vm;
+          uint32_t wpk[4], lo16[8];
+          far_keys(cp, rs, xs, vh, vm);
+          far_head(cp, rs, xs, thr2, vm, wpk, lo16, vh);
+          for (int nx = cp + WAVES; nx < c1; nx += WAVES) {
+            rsrc_t rs2;
+            float xs2;
+            Raw<32> vm2;
+            far_keys(nx, rs2, xs2, vh, vm2);  // (leaves vh alone: INT4 loads it in the head)
+            far_tail(vh, lo16, wpk);
+            far_head(nx, rs2, xs2, thr2, vm2, wpk, lo16, vh);
+          }
+          far_tail(vh, lo16, wpk);
+        }
+      } else {
+        for (int cp = c0 + w; cp < c1; cp += WAVES) {
+          rsrc_t rs;
+          float xs;
+          Raw<16> vh;
+          Raw<32> vm;
+          uint32_t wpk[4], lo16[8];
+          far_keys(cp, rs, xs, vh, vm);
+          far_head(cp, rs, xs, thr2, vm, wpk, lo16, vh);
+          far_tail(vh, lo16, wpk);
+        }
       }
     } else {
       // The LoopKV page's rule (App. E Algorithm 1): this far block walks its pages in order
@@ -658,13 +746,13 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
       for (int base = c0, round = 0; base < c1; base += WAVES, ++round) {
         const int cp = base + w;
         const bool active = cp < c1;  // uniform per wave
-        const uint8_t* hb = nullptr;
+        rsrc_t rs = slice_rsrc(p.codes, 0);  // set by far_keys on an active round
         float xs = -INFINITY;
         Raw<16> vh;
         Raw<32> vm;
         float pm = -INFINITY;
         if (active) {
-          far_keys(cp, hb, xs, vh, vm);
+          far_keys(cp, rs, xs, vh, vm);
           pm = fmaxf(xs, dpp<0x4E>(xs));  // -inf past the sequence
           pm = fmaxf(pm, dpp<0x141>(pm));
           pm = fmaxf(pm, dpp<0x140>(pm));
@@ -680,7 +768,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING ? 5 : 6)) void cel
           if (v <= w) m_page = fmaxf(m_page, pv);
           m_run = fmaxf(m_run, pv);
         }
-        if (active) far_values(cp, hb, xs, fmaxf(m_page, m0_2) - p.v_tau, vh, vm);
+        if (active) {
+          uint32_t wpk[4], lo16[8];
+          far_head(cp, rs, xs, fmaxf(m_page, m0_2) - p.v_tau, vm, wpk, lo16, vh);
+          far_tail(vh, lo16, wpk);
+        }
       }
     }
   }

@@ -777,20 +777,21 @@ int auto_splits(const lkv_cache* c, int n_seqs, int mode, int q_len, int max_pag
   return std::max(1, std::min(s, 64));
 }
 
-// Far splits of a quantised-cell call, at most one per code page and at most 64.  INT4 and
-// shared cells under the fixed rule run a software-pipelined far loop (a wave computes the
-// next page's scores while the current page's lo rows are in flight) at five waves per SIMD,
-// which pays off over long runs of pages: they take as many splits as keep the whole grid,
-// near blocks included, resident at once (five 4-wave workgroups per CU on the 256 CUs;
-// one split more and the last far blocks start a whole block late; measured on MI355X).
-// Other cells take enough (split, head, seq) workgroups to fill the chip several times.
+// Far splits of a quantised-cell call, at most one per code page and at most 64.  INT2 cells,
+// and INT4 and shared cells under the fixed rule, run a software-pipelined far loop at five
+// waves per SIMD (a wave keeps the next page's loads in flight while it computes the current
+// one; INT4: the next page's scores while the current page's lo rows are in flight), which
+// pays off over long runs of pages: they take as many splits as keep the whole grid, near
+// blocks included, resident at once (five 4-wave workgroups per CU on the 256 CUs; one split
+// more and the last far blocks start a whole block late; measured on MI355X).  The running
+// rule takes enough (split, head, seq) workgroups to fill the chip several times.
 constexpr int kCellPipelinedWgs = 5 * 256;
 
 int cell_splits(const lkv_cache* c, int n_seqs, int split_k, int max_code_pages, int bits, int rule) {
   const int rows = n_seqs * c->cfg.n_heads_q;
   int S;
   if (split_k > 0) S = split_k;
-  else if (bits == 4 && rule == LKV_VRULE_FIXED) S = std::max(1, std::min(64, kCellPipelinedWgs / rows - 1));
+  else if (bits == 2 || rule == LKV_VRULE_FIXED) S = std::max(1, std::min(64, kCellPipelinedWgs / rows - 1));
   else S = std::max(1, std::min(64, (kTargetWgs + rows - 1) / rows));
   return std::min(S, std::max(1, max_code_pages));
 }

@@ -385,11 +385,10 @@ __device__ __forceinline__ float f16_hi_f32(uint32_t w) { return (float)__builti
 // each lane takes one exponential, and the weights and hot bits reach the whole row
 // by lane broadcasts.
 template <int WAVES, bool TRACE, int BITS, bool RUNNING>
-// Five waves per SIMD (96 VGPRs) for INT4 and shared cells, whose fixed-rule loop holds one
-// page's value-phase state while it computes the next page's scores, and for the running rule
-// (a page's scores across a barrier); six (80 VGPRs) for INT2 cells.  The traced variants, for
-// tests, are left unconstrained.
-__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING || BITS == 4 ? 5 : 6)) void cell_kernel(const CellParams p) {
+// Five waves per SIMD (96 VGPRs): the fixed-rule loops hold one page's state while the next
+// page's loads are in flight (INT4: while its scores are computed), the running rule a page's
+// scores across a barrier.  The traced variants, for tests, are left unconstrained.
+__global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const CellParams p) {
   constexpr int D = 128, E = 8;
   constexpr uint64_t HEADB = (uint64_t)kPage * D * 2;  // bf16 (page, head) slice
   const int part = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -496,21 +495,39 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING || BITS == 4 ? 5 :
     // the lane's token g + 4 (li / 2) in base-2 units (xs; -inf past the sequence); the V
     // codes and V meta are loaded here too.  A score is bias + sum_c q'_c c_jc over the
     // lane's 8 channels for each of its 8 tokens, then the transposed 16-lane sum.
-    auto far_keys = [&](int cp, rsrc_t& rs, float& xs, Raw<16>& vh, Raw<32>& vm) {
-      rs = slice_rsrc(p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes, head_bytes);
-      // Issue the page's loads together: K meta of the lane's 8 channels, K codes, INT2 V
-      // codes, V meta (INT4 V hi goes out with the lo rows in the value phase).
+    struct KeyRegs {
       Raw<32> km;
-      buf_load<32, false>(km, rs, off_km);
       Raw<16> k0, k1;
-      buf_load<16, true>(k0, rs, off_k);
-      if constexpr (BITS == 4) buf_load<16, true, 1024>(k1, rs, off_k);
+    };
+    // The page's loads, issued together: K meta of the lane's 8 channels, K codes, INT2 V
+    // codes, V meta (INT4 V hi goes out with the lo rows in the value phase).
+    // (live = false: a resource of size 0, whose loads return zeros without touching memory)
+    auto far_rsrc = [&](int cp, bool live) {
+      return slice_rsrc(p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes,
+                        live ? (uint32_t)head_bytes : 0u);
+    };
+    auto far_load_k = [&](rsrc_t rs, KeyRegs& kr) {
+      buf_load<32, false>(kr.km, rs, off_km);
+      buf_load<16, true>(kr.k0, rs, off_k);
+      if constexpr (BITS == 4) buf_load<16, true, 1024>(kr.k1, rs, off_k);
+    };
+    auto far_load_v = [&](rsrc_t rs, Raw<16>& vh, Raw<32>& vm) {
       if constexpr (BITS == 2) buf_load<16, true, (int)(vcode_off - 4 * D)>(vh, rs, off_k);  // INT2 V codes
       buf_load<32, false>(vm, rs, off_vm);
+    };
+    auto far_load = [&](int cp, rsrc_t& rs, KeyRegs& kr, Raw<16>& vh, Raw<32>& vm) {
+      rs = far_rsrc(cp, true);
+      far_load_k(rs, kr);
+      far_load_v(rs, vh, vm);
       // In the pipelined loop the previous page's accumulation follows this key phase; keep
       // the scheduler from moving any of it above these loads, where it would wait for the
       // previous page's lo rows before the loads go out.
       if constexpr (masked && !RUNNING) __builtin_amdgcn_sched_barrier(0);
+    };
+    auto far_scores = [&](int cp, const KeyRegs& kr, float& xs) {
+      const Raw<32>& km = kr.km;
+      const Raw<16>& k0 = kr.k0;
+      const Raw<16>& k1 = kr.k1;
       // q' = q sigma and bias = q . z; fma with a zero addend so the fp16 operand folds into
       // v_fma_mix_f32 (q sigma is exact in fp32: bf16 x fp16)
       float qs[E], bias = 0.f;
@@ -569,6 +586,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING || BITS == 4 ? 5 :
       if (cp == n_cp - 1) {
         if (cp * kCodePage + g + 4 * (li >> 1) >= n_far) xs = -INFINITY;
       }
+    };
+    auto far_keys = [&](int cp, rsrc_t& rs, float& xs, Raw<16>& vh, Raw<32>& vm) {
+      KeyRegs kr;
+      far_load(cp, rs, kr, vh, vm);
+      far_scores(cp, kr, xs);
     };
 
     // Value phase, first half: hot test against thr2 (base-2 units), online softmax (the
@@ -722,15 +744,34 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : (RUNNING || BITS == 4 ? 5 :
           far_tail(vh, lo16, wpk);
         }
       } else {
-        for (int cp = c0 + w; cp < c1; cp += WAVES) {
+        // INT2 cells (no lo rows): the wave issues the next page's key loads as soon as the
+        // current page's key registers are free, so they are in flight during its value phase,
+        // and the next page's V loads once that phase is done (in flight during the next key
+        // phase); each load set reuses the registers of the set it replaces.  After the run's
+        // last page the loads go to an empty resource (zeros, no memory access): with no branch
+        // around the loads, the waits count them exactly.
+        int cp = c0 + w;
+        if (cp < c1) {
           rsrc_t rs;
-          float xs;
+          KeyRegs kr;
           Raw<16> vh;
           Raw<32> vm;
-          uint32_t wpk[4], lo16[8];
-          far_keys(cp, rs, xs, vh, vm);
-          far_head(cp, rs, xs, thr2, vm, wpk, lo16, vh);
-          far_tail(vh, lo16, wpk);
+          far_load(cp, rs, kr, vh, vm);
+          for (;;) {
+            float xs;
+            far_scores(cp, kr, xs);
+            const int nx = cp + WAVES;
+            const bool more = nx < c1;
+            const rsrc_t rs2 = far_rsrc(more ? nx : cp, more);
+            far_load_k(rs2, kr);
+            uint32_t wpk[4], lo16[8];
+            far_head(cp, rs, xs, thr2, vm, wpk, lo16, vh);
+            far_tail(vh, lo16, wpk);
+            far_load_v(rs2, vh, vm);
+            if (!more) break;
+            cp = nx;
+            rs = rs2;
+          }
         }
       }
     } else {

@@ -489,6 +489,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     const uint32_t off_km = (uint32_t)li * 32u, off_k = 4u * D + (uint32_t)lane * 16u;
     const uint32_t off_vm = (uint32_t)vmeta_off + (uint32_t)(g * 4 + (li >> 2)) * 32u;
     const uint32_t off_lo = 28u * D + (uint32_t)g * 32u + (uint32_t)li * 2u;  // V lo of token g
+    constexpr uint32_t kPastSlice = 1u << 30;  // any offset past a slice (plus at most 896)
 
     // Key phase of code page cp: loads, K dequant folded into q (LoopKV page, App. E: the
     // per-channel scale multiplies the query, the zero becomes a bias), and the score of
@@ -664,22 +665,18 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
         wacc = __builtin_amdgcn_fdot2(wp, f16x2_t{(_Float16)1.f, (_Float16)1.f}, wacc, false);
         wpk[j] = __builtin_bit_cast(uint32_t, wp);
       }
-      // The V meta is used up above, before the conditional lo loads: a wait for a load issued
-      // before loads that may or may not go out has to assume they did not, and so would wait
-      // for them too.  The lo loads take their lane offset through an empty statement that also
-      // takes the sums depending on every use of the V meta, so the compiler cannot sink those
-      // uses below the loads.
-      uint32_t lo_off = off_lo;
-      if constexpr (masked) asm("" : "+v"(lo_off) : "v"(wacc), "v"(zacc));
       // INT4 and shared cells: the V hi plane goes out with the V lo rows of the hot tokens
-      // only (LoopKV page, Sec. 3.3), one memory round trip; the key phase does not need it
+      // only (LoopKV page, Sec. 3.3), one memory round trip; the key phase does not need it.
+      // A cold token's load takes an offset past the slice, so it returns 0 without a memory
+      // access: the loads need no branch, and every wait counts them exactly.
       if constexpr (BITS == 4) buf_load<16, true, (int)(vcode_off - 4 * D)>(vh, rs, off_k);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         lo16[i] = 0u;
         // token g + 4 i: the token's part of the offset goes in the scalar offset, so that all
         // eight loads share the lane's one offset register
-        if (masked && hot[i]) lo16[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, lo_off, 128 * i, 0);
+        if constexpr (masked)
+          lo16[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, hot[i] ? off_lo : kPastSlice, 128 * i, 0);
       }
       if constexpr (TRACE) {
         const uint32_t word = or4(hotbits);
@@ -721,25 +718,44 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       // Fixed rule: hot iff s >= m0 - offset.
       const float thr2 = (m0 - p.thr_offset) * kLog2e;
       if constexpr (masked) {
-        // INT4 and shared cells: a page's lo rows need its scores, so the wave computes the
-        // next page's key phase while they are in flight (one memory round trip per page
-        // instead of two); the loop's last page leaves it, so no load sits in a branch.
+        // INT4 and shared cells: a page's lo rows need its scores, so the wave works on two
+        // pages at once.  One step: the scores of page n (its key loads went out one step
+        // earlier), the key loads of page n + 1 (into the key registers just freed), the
+        // accumulation of page n - 1 (its V hi and lo rows went out one step earlier), the value
+        // head of page n (V meta loaded one step earlier; V hi and lo rows go out), and the V
+        // meta load of page n + 1.  Every load has a whole phase of other work before its use,
+        // each load set reuses the registers of the set it replaces, and after the run's last
+        // page the loads go to an empty resource (zeros, no memory access), so no load sits in
+        // a branch and every wait counts the loads exactly.
         int cp = c0 + w;
         if (cp < c1) {
-          rsrc_t rs;
-          float xs;
+          KeyRegs kr;
           Raw<16> vh;
           Raw<32> vm;
           uint32_t wpk[4], lo16[8];
-          far_keys(cp, rs, xs, vh, vm);
+          float xs;
+          rsrc_t rs = far_rsrc(cp, true);
+          far_load_k(rs, kr);
+          far_load_v(rs, vh, vm);
+          far_scores(cp, kr, xs);
+          int nx = cp + WAVES;
+          bool more = nx < c1;
+          rsrc_t rs2 = far_rsrc(more ? nx : cp, more);
+          far_load_k(rs2, kr);
           far_head(cp, rs, xs, thr2, vm, wpk, lo16, vh);
-          for (int nx = cp + WAVES; nx < c1; nx += WAVES) {
-            rsrc_t rs2;
-            float xs2;
-            Raw<32> vm2;
-            far_keys(nx, rs2, xs2, vh, vm2);  // (leaves vh alone: INT4 loads it in the head)
+          far_load_v(rs2, vh, vm);  // (INT4: V meta only; V hi goes out in the head)
+          while (more) {
+            far_scores(nx, kr, xs);
+            const int nn = nx + WAVES;
+            const bool more2 = nn < c1;
+            const rsrc_t rs3 = far_rsrc(more2 ? nn : nx, more2);
+            far_load_k(rs3, kr);
             far_tail(vh, lo16, wpk);
-            far_head(nx, rs2, xs2, thr2, vm2, wpk, lo16, vh);
+            far_head(nx, rs2, xs, thr2, vm, wpk, lo16, vh);
+            far_load_v(rs3, vh, vm);
+            nx = nn;
+            more = more2;
+            rs2 = rs3;
           }
           far_tail(vh, lo16, wpk);
         }

@@ -288,7 +288,10 @@ lkv_status lkv_read_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop
                           int32_t n_pages, void* k_codes, void* k_meta, void* v_codes, void* v_meta,
                           void* stream);
 
-/* Workspace an attend call needs (0 when it runs unsplit). */
+/* Workspace an attend call needs (0 when it runs unsplit).  For a quantised cache the
+   size covers the call's (layer, loop) whatever its cell kind and V-precision rule
+   (the library's split choice depends on both), so one buffer serves every cell call
+   of that batch. */
 lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, size_t* bytes);
 
 /* Attention of n_seqs rows at (layer, loop), on `stream`: for query position t,

@@ -266,8 +266,9 @@ def test_plan_rules(lib):
 
 
 def test_quant_workspace_matches_the_cell_split_rule(lib):
-    """lkv_workspace_bytes sizes a quantised-cell call by the same split rule lkv_attend uses: far splits
-    min(64, ceil(2048 / (seqs * heads))), at most one per code page, plus the near part."""
+    """lkv_workspace_bytes sizes a quantised-cell call by the split rules lkv_attend uses, taking the most splits
+    over the cell kinds and V-precision rules: the running rule's min(64, ceil(2048 / (seqs * heads))) and the
+    pipelined loops' min(64, 1280 / (seqs * heads) - 1), at most one per code page, plus the near part."""
     cfg = vla.LoopCache.config(n_layers=1, n_loops=2, n_heads_q=4, n_heads_kv=4, head_dim=128,
                                kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=3, max_len=2000,
                                max_block=1, quant=1, sink=4, tail=128)
@@ -285,6 +286,20 @@ def test_quant_workspace_matches_the_cell_split_rule(lib):
     S = min(64, -(-2048 // rows), n_cp)
     assert c.lkv_workspace_bytes(0, 0, seqs) == rows * (S + 1) * 129 * 4
     assert c.lkv_workspace_bytes(0, 0, seqs[2:], split_k=5) == 4 * (1 + 1) * 129 * 4  # 1 code page caps the splits
+    # 256 rows: the pipelined loops take 1280 / 256 - 1 = 4 far splits, the running rule 2048 / 256 = 8; the
+    # workspace covers 8, so a running-rule call fits the buffer sized for the batch
+    cfg = vla.LoopCache.config(n_layers=1, n_loops=2, n_heads_q=16, n_heads_kv=16, head_dim=128,
+                               kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=16, max_len=1000,
+                               max_block=1, quant=1, sink=4, tail=128)
+    s = vla.LoopCache.sizes(cfg)
+    meta = np.zeros(max(256, s.meta_bytes), dtype=np.uint8)
+    ar = vla.lkv_arenas(base, 1024 * s.page_bytes, base + (1 << 38), 1024 * s.code4_page_bytes, base + (1 << 39),
+                        1024 * s.code2_page_bytes, meta.ctypes.data, s.meta_bytes)
+    c = vla.LoopCache(cfg, ar, 0)
+    seqs = [c.lkv_add_seq() for _ in range(16)]
+    for sq in seqs:
+        c.lkv_reserve(sq, 0, 0, 0, 1000)
+    assert c.lkv_workspace_bytes(0, 0, seqs) == 256 * (8 + 1) * 129 * 4
 
 
 @pytest.mark.parametrize("gamma,W", [(4, 8), (7, 7), (2, 40), (9, 4)])

@@ -810,10 +810,15 @@ lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, siz
     max_pages = std::max(max_pages, (L + kPage - 1) / kPage);
     max_cp = std::max(max_cp, (std::max(0, L - c->cfg.sink - c->cfg.tail) + kCodePage - 1) / kCodePage);
   }
-  // (quantised caches: the larger of the two cell rules, whatever the (layer, loop) cell is)
-  const int S = c->cfg.quant ? std::max(cell_splits(c, a->n_seqs, a->split_k, max_cp, 2, a->v_rule),
-                                        cell_splits(c, a->n_seqs, a->split_k, max_cp, 4, a->v_rule))
-                             : (a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, a->q_len, max_pages));
+  // (quantised caches: the most splits any cell kind and V-precision rule takes)
+  int S = 0;
+  if (c->cfg.quant) {
+    for (int bits : {2, 4})
+      for (int rule : {(int)LKV_VRULE_FIXED, (int)LKV_VRULE_RUNNING})
+        S = std::max(S, cell_splits(c, a->n_seqs, a->split_k, max_cp, bits, rule));
+  } else {
+    S = a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, a->q_len, max_pages);
+  }
   const int parts = c->cfg.quant ? S + 1 : S;
   if (parts <= 1) {
     *bytes = 0;

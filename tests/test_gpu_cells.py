@@ -180,9 +180,13 @@ def test_cells_running_rule(tau, split_k):
     bc.cache.close()
 
 
-def test_running_rule_infinite_tau_is_the_all_hot_reader_bitwise():
+def test_running_rule_infinite_tau_is_the_all_hot_reader():
     """LoopKV page, Sec. 3.3 and App. I: at tau = infinity the running rule keeps every far token hot, so the
-    cell equals the reader of both V planes (the fixed rule at offset +inf), bit for bit, masks included."""
+    cell equals the reader of both V planes (the fixed rule at offset +inf): masks bit for bit, outputs to
+    rounding.  The fixed rule lets the near block take a share of the far pages, the running rule keeps equal
+    runs per far split (whose running maxima define its hot sets), so the online softmax references and the
+    fp16 rounding of the value weights (relative 2^-12) differ: outputs within one bf16 step plus 1e-4 (the
+    weights' rounding, ~3e-5 on cancelling channels), lse within 1e-5."""
     w = _cells_wl(3)
     bc = harness.build_cells(w, lengths=[133, 640, 1000], layers=(0, 1), plan=PLAN)
     for layer in (0, 1):
@@ -190,7 +194,9 @@ def test_running_rule_infinite_tau_is_the_all_hot_reader_bitwise():
             for split_k in (1, 4):
                 a, la, ma = _attend_cells(bc, layer, loop, math.inf, split_k)
                 b, lb, mb = _attend_cells(bc, layer, loop, 4.0, split_k, v_rule=vla.VRULE_RUNNING, v_tau=math.inf)
-                assert np.array_equal(a, b) and np.array_equal(la, lb) and np.array_equal(ma, mb), (layer, loop)
+                assert np.array_equal(ma, mb), (layer, loop, split_k)
+                assert np.all(np.abs(a - b) <= np.maximum(np.abs(a), np.abs(b)) * 2.0 ** -7 + 1e-4), (layer, loop)
+                assert np.abs(la - lb).max() <= 1e-5, (layer, loop, split_k)
     bc.cache.close()
 
 

@@ -366,21 +366,22 @@ __device__ __forceinline__ float f16_lo_f32(uint32_t w) { return (float)__builti
 __device__ __forceinline__ float f16_hi_f32(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // One launch per cell: grid.x = n_splits far blocks + 1 near block.
-//   near block: exact bf16 attention over the sink [0, sink) and the tail
+//   near part (near block): exact bf16 attention over the sink [0, sink) and the tail
 //     [L - tail, L) of the cell's own loop (LoopKV page, Sec. 3.2: sink and window
 //     stay the cell's own and exact);
-//   far block c: its share of the code pages of the cell's source (own codes, or
-//     the final loop's for a shared cell).  Per page the K scale is folded into q
+//   far part (every block, the near block after its near part, so that no block idles
+//     once its near work is done): a share of the code pages of the cell's source (own
+//     codes, or the final loop's for a shared cell).  Per page the K scale is folded into q
 //     and q.z into a bias (LoopKV page, App. E), so a score is bias + sum q'_c c_jc.
-//     The seed m0 is the largest sink score, recomputed by every far block from
-//     the sink keys (no wait on another block).  Hot test of a far token: the fixed
+//     The seed m0 is the largest sink score, recomputed by every block from the
+//     sink keys (no wait on another block).  Hot test of a far token: the fixed
 //     rule s_j >= m0 - offset, or the page's own rule s_j >= max(m, m0) - tau ln 2
-//     with m the far block's running maximum over its pages so far (RUNNING).
+//     with m the block's running maximum over its far pages so far (RUNNING).
 //     V: hot tokens read both bit planes (4 hi + lo), cold tokens only hi and take
 //     the bucket midpoint 4 hi + 1.5; the per-token V scale and zero fold into the
 //     weight p_j (LoopKV page, Sec. 3.3, App. E Alg. 1).
 // Each DPP row keeps its own online softmax; partials go to the workspace and
-// the LSE merge kernel combines them.  In the far blocks a page's eight token scores
+// the LSE merge kernel combines them.  In the far part a page's eight token scores
 // of a row are summed transposed, so that lanes 2t and 2t + 1 hold token t's score:
 // each lane takes one exponential, and the weights and hot bits reach the whole row
 // by lane broadcasts.
@@ -418,10 +419,17 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
 #pragma unroll
   for (int e = 0; e < E; ++e) o[e] = 0.f;
   float zacc = 0.f;
-  float wacc = 0.f;  // far blocks: the running sum of the V weights (INT2: fp16-rounded), rescaled like o
+  float wacc = 0.f;  // far part: the running sum of the V weights (fp16-rounded), rescaled like o
 
-  if (part == p.n_splits) {
-    // ---------------- near block: sink and tail, bf16, own loop
+  // Row states of the block's waves for the final merge: far rows [0, 4 WAVES), and in the
+  // near block its near rows [4 WAVES, 8 WAVES).
+  __shared__ float sm_o[WAVES * 8][D];
+  __shared__ float sm_m[WAVES * 8], sm_l[WAVES * 8];
+  const int r = w * 4 + g;
+  const bool near_block = part == p.n_splits;
+
+  if (near_block) {
+    // ---------------- near part (the near block only): sink and tail, bf16, own loop
     const int np_sink = (p.sink + kPage - 1) / kPage;
     const int tp0 = max(np_sink, tail_lo / kPage), tp1 = (L - 1) / kPage;
     const int count = np_sink + (p.tail > 0 ? max(0, tp1 - tp0 + 1) : 0);
@@ -450,8 +458,21 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       softmax_step<E, 4>(st, o, x);
       accum_quad<bf16, D>(o, vr, x);
     }
-  } else {
-    // ---------------- far block
+    // park the near row states and start the far part from an empty state
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      sm_o[WAVES * 4 + r][vchan<bf16>(e, li)] = o[e];
+      o[e] = 0.f;
+    }
+    if (li == 0) {
+      sm_m[WAVES * 4 + r] = st.m;
+      sm_l[WAVES * 4 + r] = st.l;
+    }
+    st = Softmax{-INFINITY, 0.f};
+  }
+  {
+    // ---------------- far part (every block: n_splits far blocks and the near block split
+    // the code pages, the near block's share shorter by its near work)
     // seed m0: largest exact sink score (natural-log units)
     float m0 = -INFINITY;
     for (int sp = 0; sp * kPage < p.sink; ++sp) {  // sink pages (the page's own rule uses 32 sink keys)
@@ -471,17 +492,27 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     }
     m0 = fmaxf(m0, __shfl_xor(m0, 16));
     m0 = fmaxf(m0, __shfl_xor(m0, 32));
-    // the key codes of odd channels are converted as 16 times their value (one mask per
-    // nibble parity), so those channels' query entries carry 1/16: exact, and each product
-    // (q / 16) (16 c) equals q c bit for bit
     const uint32_t b64 = 0x54005400u, b16 = 0x4C004C00u, b4 = 0x44004400u;  // fp16 64, 16, 4 in both halves
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
-    const int n_cp = (n_far + kCodePage - 1) / kCodePage;
-    const int c0 = (int)((int64_t)part * n_cp / p.n_splits);
-    const int c1 = (int)((int64_t)(part + 1) * n_cp / p.n_splits);
     const int32_t* tab_code = p.tab_code + (int64_t)slot * p.code_ring;
     constexpr uint64_t head_bytes = (uint64_t)(BITS == 4 ? 40 : 24) * D;
+    // The n_splits + 1 blocks of a row take equal shares of the code pages plus the near
+    // work, counted as the code pages of the same bytes (sink + tail tokens of bf16 K and V);
+    // the near block's far share is its share less that.  Under the running rule the hot
+    // sets depend on how the pages are cut into runs (each far split keeps its own running
+    // maximum), so there the n_splits far blocks take equal shares and the near block none.
+    const int n_cp = (n_far + kCodePage - 1) / kCodePage;
+    int c0, c1;
+    if constexpr (RUNNING && masked) {
+      c0 = near_block ? n_cp : (int)((int64_t)part * n_cp / p.n_splits);
+      c1 = near_block ? n_cp : (int)((int64_t)(part + 1) * n_cp / p.n_splits);
+    } else {
+      const int64_t near_eq = ((int64_t)(p.sink + p.tail) * 4 * D + (int64_t)head_bytes - 1) / (int64_t)head_bytes;
+      const int64_t total = n_cp + near_eq;
+      c0 = (int)min((int64_t)n_cp, (int64_t)part * total / (p.n_splits + 1));
+      c1 = near_block ? n_cp : (int)min((int64_t)n_cp, (int64_t)(part + 1) * total / (p.n_splits + 1));
+    }
     constexpr uint64_t vcode_off = BITS == 4 ? 20 * D : 12 * D;
     constexpr uint64_t vmeta_off = BITS == 4 ? 36 * D : 20 * D;
     // the lane's byte offsets inside a page's head slice, 32-bit so that each load takes the
@@ -834,36 +865,29 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     }
   }
 
-  if (part != p.n_splits) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = fmaf(BITS == 4 ? -int4_off(e) : -int2_off(e), wacc, o[e]);  // the pairs' offsets
-    st.l = 0.5f * row_sum16(st.l);  // lanes 2t and 2t + 1 hold equal sums, so this is exact
-  }
+  for (int e = 0; e < E; ++e) o[e] = fmaf(BITS == 4 ? -int4_off(e) : -int2_off(e), wacc, o[e]);  // the pairs' offsets
+  st.l = 0.5f * row_sum16(st.l);  // lanes 2t and 2t + 1 hold equal sums, so this is exact
 
-  // merge the 4 * WAVES row states
-  __shared__ float sm_o[WAVES * 4][D];
-  __shared__ float sm_m[WAVES * 4], sm_l[WAVES * 4];
-  const int r = w * 4 + g;
+  // merge the block's row states (4 WAVES far rows, and in the near block 4 WAVES near rows)
 #pragma unroll
-  for (int e = 0; e < E; ++e) sm_o[r][part == p.n_splits ? vchan<bf16>(e, li) : li * E + e] = o[e] + zacc;
+  for (int e = 0; e < E; ++e) sm_o[r][li * E + e] = o[e] + zacc;
   if (li == 0) {
     sm_m[r] = st.m;
     sm_l[r] = st.l;
   }
   __syncthreads();
+  const int n_rows = near_block ? WAVES * 8 : WAVES * 4;
   float M = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < WAVES * 4; ++k) M = fmaxf(M, sm_m[k]);
+  for (int k = 0; k < n_rows; ++k) M = fmaxf(M, sm_m[k]);
   const float Mu = (M == -INFINITY) ? 0.f : M;
   float Lsum = 0.f;
-#pragma unroll
-  for (int k = 0; k < WAVES * 4; ++k) Lsum += sm_l[k] * fast_exp2(sm_m[k] - Mu);
+  for (int k = 0; k < n_rows; ++k) Lsum += sm_l[k] * fast_exp2(sm_m[k] - Mu);
   const int64_t row = (int64_t)b * p.hq + h;
   float* wsr = p.ws + (row * (p.n_splits + 1) + part) * (D + 1);
   for (int c = threadIdx.x; c < D; c += WAVES * 64) {
     float acc = 0.f;
-#pragma unroll
-    for (int k = 0; k < WAVES * 4; ++k) acc += sm_o[k][c] * fast_exp2(sm_m[k] - Mu);
+    for (int k = 0; k < n_rows; ++k) acc += sm_o[k][c] * fast_exp2(sm_m[k] - Mu);
     wsr[c] = Lsum > 0.f ? acc / Lsum : 0.f;
   }
   if (threadIdx.x == 0) wsr[D] = Lsum > 0.f ? M + fast_log2(Lsum) : -INFINITY;

@@ -522,18 +522,14 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     const uint32_t off_lo = 28u * D + (uint32_t)g * 32u + (uint32_t)li * 2u;  // V lo of token g
     constexpr uint32_t kPastSlice = 1u << 30;  // any offset past a slice (plus at most 896)
 
-    // Key phase of code page cp: loads, K dequant folded into q (LoopKV page, App. E: the
-    // per-channel scale multiplies the query, the zero becomes a bias), and the score of
-    // the lane's token g + 4 (li / 2) in base-2 units (xs; -inf past the sequence); the V
-    // codes and V meta are loaded here too.  A score is bias + sum_c q'_c c_jc over the
-    // lane's 8 channels for each of its 8 tokens, then the transposed 16-lane sum.
+    // A code page's loads: the head slice of page cp as a buffer resource (live = false: a
+    // resource of size 0, whose loads return zeros without touching memory); the key set (K
+    // meta of the lane's 8 channels, K codes) and the V set (INT2 V codes, V meta; INT4 V hi
+    // goes out with the lo rows in the value phase).
     struct KeyRegs {
       Raw<32> km;
       Raw<16> k0, k1;
     };
-    // The page's loads, issued together: K meta of the lane's 8 channels, K codes, INT2 V
-    // codes, V meta (INT4 V hi goes out with the lo rows in the value phase).
-    // (live = false: a resource of size 0, whose loads return zeros without touching memory)
     auto far_rsrc = [&](int cp, bool live) {
       return slice_rsrc(p.codes + (uint64_t)tab_code[cp] * p.code_page_bytes + (uint64_t)hk * head_bytes,
                         live ? (uint32_t)head_bytes : 0u);
@@ -551,11 +547,12 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       rs = far_rsrc(cp, true);
       far_load_k(rs, kr);
       far_load_v(rs, vh, vm);
-      // In the pipelined loop the previous page's accumulation follows this key phase; keep
-      // the scheduler from moving any of it above these loads, where it would wait for the
-      // previous page's lo rows before the loads go out.
-      if constexpr (masked && !RUNNING) __builtin_amdgcn_sched_barrier(0);
     };
+    // Key phase of code page cp: K dequant folded into q (LoopKV page, App. E: the
+    // per-channel scale multiplies the query, the zero becomes a bias), and the score of
+    // the lane's token g + 4 (li / 2) in base-2 units (xs; -inf past the sequence).  A
+    // score is bias + sum_c q'_c c_jc over the lane's 8 channels for each of its 8 tokens,
+    // then the transposed 16-lane sum.
     auto far_scores = [&](int cp, const KeyRegs& kr, float& xs) {
       const Raw<32>& km = kr.km;
       const Raw<16>& k0 = kr.k0;

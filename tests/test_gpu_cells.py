@@ -87,6 +87,36 @@ def test_cells_every_kind(offset):
     bc.cache.close()
 
 
+@pytest.mark.parametrize("split_k", [0, 2, 5, 16, 64])
+def test_cells_far_shares(split_k):
+    """How a row's far pages are shared: the far blocks and the near block take equal shares of the code pages
+    plus the near work, so with many splits most blocks get no page or one, and a wave's run of pages in the
+    pipelined loops is empty, one page, or a few (lengths 133: one far token; 164: exactly one code page; 229:
+    four pages, the last partial; 420; 1000), for every cell kind at the fixed rule (offset 4) and the
+    library's own split choice (0): outputs within 2e-2 of the oracle, hot masks bit-exact outside a 1e-4
+    band around the threshold."""
+    w = _cells_wl(5)
+    lengths = [133, 164, 229, 420, 1000]
+    bc = harness.build_cells(w, lengths=lengths, layers=(0, 1), plan=PLAN)
+    band_hits = 0
+    for layer in (0, 1):
+        for loop in range(4):
+            out, lse, mask = _attend_cells(bc, layer, loop, 4.0, split_k)
+            assert np.isfinite(out).all()
+            for b, L in enumerate(lengths):
+                n_far = L - w.sink - w.tail
+                for h in range(w.n_heads):
+                    want, want_lse, hot, s_far, thr = harness.cell_oracle_row(bc, b, layer, loop, h, 4.0)
+                    assert np.abs(out[b, 0, h] - want).max() <= TOL, (layer, loop, split_k, b, h)
+                    assert abs(lse[b, 0, h] - want_lse) <= 1e-2
+                    got = _bits(mask[b, h], n_far)
+                    near = np.abs(s_far - thr) <= BAND
+                    assert np.array_equal(got[~near], hot[~near]), (layer, loop, split_k, b, h)
+                    band_hits += int(near.sum())
+    assert band_hits < 5
+    bc.cache.close()
+
+
 def test_all_hot_cell_reads_full_int4_codes_bitwise_equal_to_negative_infinite_threshold():
     """LoopKV page, App. I: with the threshold at -inf (every token hot) the reader equals the plain reader
     of both V planes; the same kernel with any offset >= the whole score range gives the same bits."""

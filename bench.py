@@ -73,6 +73,7 @@ def parse():
                     choices=["huginn_ripe", "ouro_splitk", "huginn_verify", "huginn_draft", "loopkv_cells",
                              "raven_ripe", "dory_lastloop", "tiny"])
     ap.add_argument("--split-k", type=int, default=-1, help="splits per row (-1: the workload's, 0: library's)")
+    ap.add_argument("--waves", type=int, default=0, help="waves per workgroup (0: the library's choice)")
     ap.add_argument("--policy", choices=["default", "full", "ripe"], default="default",
                     help="cache policy of a plain workload (default: the workload's own; the verify configuration "
                          "names both the full-depth cache and the RIPE window)")
@@ -349,6 +350,8 @@ def run_workload(args, workload: str, prober, with_cpu: bool) -> dict:
         extra = {"v_thresh_offset": args.v_offset}
         if args.v_rule == "running":
             extra = {"v_rule": vla.VRULE_RUNNING, "v_tau": args.v_tau}
+    if args.waves > 0:
+        extra["waves"] = args.waves
 
     # Algorithmic bytes of each call.  Quantised cells skip the V lo plane of cold tokens, so one untimed
     # pass with the hot-mask trace counts them first.
@@ -422,7 +425,7 @@ def run_workload(args, workload: str, prober, with_cpu: bool) -> dict:
     khash = kernel_hash(workload)
     # the counters were taken on the workload as defined: its batch, splits and resident layers and, for
     # cells, the fixed rule at m0 - 4.0
-    as_profiled = (args.batch <= 0 and args.split_k < 0 and args.layers <= 0 and
+    as_profiled = (args.batch <= 0 and args.split_k < 0 and args.layers <= 0 and args.waves <= 0 and
                    (not w.quant or (args.v_rule == "fixed" and args.v_offset == 4.0)))
     policy_tag = "" if w.policy == synth.WORKLOADS[workload].policy else "_" + w.policy
     traffic = read_traffic(workload + policy_tag, khash) if as_profiled else None
@@ -465,6 +468,8 @@ def run_workload(args, workload: str, prober, with_cpu: bool) -> dict:
            "head_dim": w.head_dim, "context": w.length, "q_len": q_len, "policy": w.policy, "window": w.window,
            "page_tokens": 32 if w.quant else 16, "split_k": split, "calls_per_step": len(calls),
            "layers_resident": len(layers), "setup_s": round(setup_s, 1)}
+    if args.waves > 0:
+        cfg["waves"] = args.waves
     if draft:
         cfg.update(draft_passes=passes, draft_loops=d_loops, draft_window=w.extra["draft_window"],
                    draft_block="1..%d tokens from scratch" % passes)

@@ -424,11 +424,14 @@ def run_workload(args, workload: str, prober, with_cpu: bool) -> dict:
     achieved = float(sum(call_bytes[n] for (_, n) in sampled)) / (kern.sum() / 1e3) / 1e9
     khash = kernel_hash(workload)
     # the counters were taken on the workload as defined: its batch, splits and resident layers and, for
-    # cells, the fixed rule at m0 - 4.0
+    # cells, the fixed rule at m0 - 4.0 (profiles/traffic_loopkv_cells.txt) or the page's running rule at
+    # tau 14 (traffic_loopkv_cells_running.txt)
     as_profiled = (args.batch <= 0 and args.split_k < 0 and args.layers <= 0 and args.waves <= 0 and
-                   (not w.quant or (args.v_rule == "fixed" and args.v_offset == 4.0)))
+                   (not w.quant or (args.v_rule == "fixed" and args.v_offset == 4.0) or
+                    (args.v_rule == "running" and args.v_tau == 14.0)))
     policy_tag = "" if w.policy == synth.WORKLOADS[workload].policy else "_" + w.policy
-    traffic = read_traffic(workload + policy_tag, khash) if as_profiled else None
+    rule_tag = "_running" if w.quant and args.v_rule == "running" else ""
+    traffic = read_traffic(workload + policy_tag + rule_tag, khash) if as_profiled else None
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -289,9 +289,9 @@ lkv_status lkv_read_coded(lkv_cache* c, int32_t seq, int32_t layer, int32_t loop
                           void* stream);
 
 /* Workspace an attend call needs (0 when it runs unsplit).  For a quantised cache the
-   size covers the call's (layer, loop) whatever its cell kind and V-precision rule
-   (the library's split choice depends on both), so one buffer serves every cell call
-   of that batch. */
+   library's split choice depends only on the batch (sequences, heads, far lengths), so
+   the size covers the call's (layer, loop) whatever its cell kind and V-precision rule,
+   and one buffer serves every cell call of that batch. */
 lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, size_t* bytes);
 
 /* Attention of n_seqs rows at (layer, loop), on `stream`: for query position t,

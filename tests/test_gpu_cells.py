@@ -135,7 +135,7 @@ def test_loopkv_full_shape_sampled(layer):
     16 heads x 128, the seeded plan's cells of one layer's four loops (layer 0: four INT4 cells; layer 14: INT2,
     shared, shared, INT4); sampled rows and their masks with the hot-mask trace on (the traced kernel
     instance), and sampled rows in the launch configuration the benchmark times (untraced kernel, the
-    library's split choice)."""
+    library's split choice), under the fixed rule and under the page's running rule."""
     w = synth.WORKLOADS["loopkv_cells"]
     plan = synth.cell_plan(w.seed, w.n_layers, w.n_loops)
     bc = harness.build_cells(w, layers=(layer,), plan=plan)
@@ -151,11 +151,23 @@ def test_loopkv_full_shape_sampled(layer):
         torch.cuda.synchronize()
         plain = harness.out_f64(plain)
         assert np.isfinite(plain).all()
+        # the page's running rule (tau 14) in the same launch configuration: untraced, the library's split
+        # count, read back from the workspace size ([rows][S + 1][d + 1] fp32)
+        S = bc.cache.lkv_workspace_bytes(layer, loop, bc.seqs) // (w.batch * w.n_heads * (w.head_dim + 1) * 4) - 1
+        run = torch.empty_like(q)
+        bc.cache.lkv_attend(layer, loop, bc.seqs, q, run, workspace=ws, v_rule=vla.VRULE_RUNNING, v_tau=14.0)
+        torch.cuda.synchronize()
+        run = harness.out_f64(run)
+        assert np.isfinite(run).all()
         for _ in range(4):
             b, h = int(rng.integers(w.batch)), int(rng.integers(w.n_heads))
             want, want_lse, hot, s_far, thr = harness.cell_oracle_row(bc, b, layer, loop, h, 4.0)
             assert np.abs(out[b, 0, h] - want).max() <= TOL
             assert np.abs(plain[b, 0, h] - want).max() <= TOL
+            a = harness.cell_inputs(bc, b, layer, loop, h)
+            want_run = oracle.cell_row_running(a["q"], a["k_near"], a["v_near"], a["kc"], a["ks"], a["kz"], a["vc"],
+                                               a["vs"], a["vz"], a["sink"], a["tail"], a["kind"], 14.0, S)[0]
+            assert np.abs(run[b, 0, h] - want_run).max() <= TOL, (layer, loop, S, b, h)
             got = _bits(mask[b, h], n_far)
             near = np.abs(s_far - thr) <= BAND
             assert np.array_equal(got[~near], hot[~near])
@@ -163,12 +175,12 @@ def test_loopkv_full_shape_sampled(layer):
 
 
 @pytest.mark.parametrize("tau", [14.0, 2.0, 0.5])
-@pytest.mark.parametrize("split_k", [1, 3, 7])
+@pytest.mark.parametrize("split_k", [0, 1, 3, 7])
 def test_cells_running_rule(tau, split_k):
     """The LoopKV page's own V-precision rule (Sec. 3.3, App. E Algorithm 1): each far split walks its pages in
     order with a running maximum m; a token is hot iff s >= max(m, m0) - tau ln 2.  Outputs vs the oracle's rule
     with the same page partition (max-abs 2e-2) and hot masks bit-exact outside a 1e-4 band around each token's
-    threshold; INT2 cells read their whole codes."""
+    threshold; INT2 cells read their whole codes.  split_k 0: the library's split count."""
     w = _cells_wl()
     lengths = [133, 300, 1000]
     bc = harness.build_cells(w, lengths=lengths, layers=(0, 1), plan=PLAN)
@@ -180,8 +192,8 @@ def test_cells_running_rule(tau, split_k):
             out = torch.empty_like(q)
             words = (max(lengths) - w.sink - w.tail + 31) // 32
             mask = torch.empty((n, w.n_heads, words), dtype=torch.int32, device="cuda")
-            ws = torch.empty(bc.cache.lkv_workspace_bytes(layer, loop, bc.seqs, split_k=split_k) + 4,
-                             dtype=torch.uint8, device="cuda")
+            ws_bytes = bc.cache.lkv_workspace_bytes(layer, loop, bc.seqs, split_k=split_k)
+            ws = torch.empty(ws_bytes + 4, dtype=torch.uint8, device="cuda")
             bc.cache.lkv_attend(layer, loop, bc.seqs, q, out, split_k=split_k, workspace=ws, mask_trace=mask,
                                 v_rule=vla.VRULE_RUNNING, v_tau=tau)
             torch.cuda.synchronize()
@@ -189,6 +201,8 @@ def test_cells_running_rule(tau, split_k):
             m = mask.cpu().numpy().view(np.uint32)
             # the call's far splits: split_k, at most the longest row's code pages (shorter rows leave splits empty)
             S = min(split_k, max((L - w.sink - w.tail + 31) // 32 for L in lengths))
+            if split_k == 0:  # the library's choice, read back from the workspace size [rows][S + 1][d + 1] fp32
+                S = ws_bytes // (n * w.n_heads * (w.head_dim + 1) * 4) - 1
             for b, L in enumerate(lengths):
                 n_far = L - w.sink - w.tail
                 for h in range(w.n_heads):

@@ -266,9 +266,9 @@ def test_plan_rules(lib):
 
 
 def test_quant_workspace_matches_the_cell_split_rule(lib):
-    """lkv_workspace_bytes sizes a quantised-cell call by the split rules lkv_attend uses, taking the most splits
-    over the cell kinds and V-precision rules: the running rule's min(64, ceil(2048 / (seqs * heads))) and the
-    pipelined loops' min(64, 1280 / (seqs * heads) - 1), at most one per code page, plus the near part."""
+    """lkv_workspace_bytes sizes a quantised-cell call by the split rule lkv_attend uses for every cell kind and
+    V-precision rule: min(64, 1280 / (seqs * heads) - 1) far splits (at least 1), at most one per code page, plus
+    the near part."""
     cfg = vla.LoopCache.config(n_layers=1, n_loops=2, n_heads_q=4, n_heads_kv=4, head_dim=128,
                                kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=3, max_len=2000,
                                max_block=1, quant=1, sink=4, tail=128)
@@ -283,11 +283,10 @@ def test_quant_workspace_matches_the_cell_split_rule(lib):
         c.lkv_reserve(sq, 0, 0, 0, L)
     rows = 3 * 4
     n_cp = (2000 - 132 + 31) // 32
-    S = min(64, -(-2048 // rows), n_cp)
+    S = min(64, max(1, 1280 // rows - 1), n_cp)
     assert c.lkv_workspace_bytes(0, 0, seqs) == rows * (S + 1) * 129 * 4
     assert c.lkv_workspace_bytes(0, 0, seqs[2:], split_k=5) == 4 * (1 + 1) * 129 * 4  # 1 code page caps the splits
-    # 256 rows: the pipelined loops take 1280 / 256 - 1 = 4 far splits, the running rule 2048 / 256 = 8; the
-    # workspace covers 8, so a running-rule call fits the buffer sized for the batch
+    # 256 rows: 1280 / 256 - 1 = 4 far splits (five workgroups per row, one resident generation)
     cfg = vla.LoopCache.config(n_layers=1, n_loops=2, n_heads_q=16, n_heads_kv=16, head_dim=128,
                                kv_dtype=vla.DTYPE_BF16, policy=vla.POLICY_FULL, window=0, max_seqs=16, max_len=1000,
                                max_block=1, quant=1, sink=4, tail=128)
@@ -299,7 +298,7 @@ def test_quant_workspace_matches_the_cell_split_rule(lib):
     seqs = [c.lkv_add_seq() for _ in range(16)]
     for sq in seqs:
         c.lkv_reserve(sq, 0, 0, 0, 1000)
-    assert c.lkv_workspace_bytes(0, 0, seqs) == 256 * (8 + 1) * 129 * 4
+    assert c.lkv_workspace_bytes(0, 0, seqs) == 256 * (4 + 1) * 129 * 4
 
 
 @pytest.mark.parametrize("gamma,W", [(4, 8), (7, 7), (2, 40), (9, 4)])

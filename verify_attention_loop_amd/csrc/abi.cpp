@@ -777,22 +777,19 @@ int auto_splits(const lkv_cache* c, int n_seqs, int mode, int q_len, int max_pag
   return std::max(1, std::min(s, 64));
 }
 
-// Far splits of a quantised-cell call, at most one per code page and at most 64.  INT2 cells,
-// and INT4 and shared cells under the fixed rule, run a software-pipelined far loop at five
-// waves per SIMD (a wave keeps the next page's loads in flight while it computes the current
-// one; INT4: the next page's scores while the current page's lo rows are in flight), which
-// pays off over long runs of pages: they take as many splits as keep the whole grid, near
-// blocks included, resident at once (five 4-wave workgroups per CU on the 256 CUs; one split
-// more and the last far blocks start a whole block late; measured on MI355X).  The running
-// rule takes enough (split, head, seq) workgroups to fill the chip several times.
+// Far splits of a quantised-cell call, at most one per code page and at most 64.  The far
+// loops are software-pipelined at five waves per SIMD (a wave keeps the next page's loads in
+// flight while it computes the current one; INT4: the next page's scores while the current
+// page's lo rows are in flight), which pays off over long runs of pages: a call takes as many
+// splits as keep the whole grid, near blocks included, resident at once (five 4-wave
+// workgroups per CU on the 256 CUs; one split more and the last far blocks start a whole
+// block late; measured on MI355X, for the running rule too, whose far blocks meet at a
+// barrier once per round of pages).
 constexpr int kCellPipelinedWgs = 5 * 256;
 
-int cell_splits(const lkv_cache* c, int n_seqs, int split_k, int max_code_pages, int bits, int rule) {
+int cell_splits(const lkv_cache* c, int n_seqs, int split_k, int max_code_pages) {
   const int rows = n_seqs * c->cfg.n_heads_q;
-  int S;
-  if (split_k > 0) S = split_k;
-  else if (bits == 2 || rule == LKV_VRULE_FIXED) S = std::max(1, std::min(64, kCellPipelinedWgs / rows - 1));
-  else S = std::max(1, std::min(64, (kTargetWgs + rows - 1) / rows));
+  const int S = split_k > 0 ? split_k : std::max(1, std::min(64, kCellPipelinedWgs / rows - 1));
   return std::min(S, std::max(1, max_code_pages));
 }
 
@@ -810,15 +807,8 @@ lkv_status lkv_workspace_bytes(const lkv_cache* c, const lkv_attend_args* a, siz
     max_pages = std::max(max_pages, (L + kPage - 1) / kPage);
     max_cp = std::max(max_cp, (std::max(0, L - c->cfg.sink - c->cfg.tail) + kCodePage - 1) / kCodePage);
   }
-  // (quantised caches: the most splits any cell kind and V-precision rule takes)
-  int S = 0;
-  if (c->cfg.quant) {
-    for (int bits : {2, 4})
-      for (int rule : {(int)LKV_VRULE_FIXED, (int)LKV_VRULE_RUNNING})
-        S = std::max(S, cell_splits(c, a->n_seqs, a->split_k, max_cp, bits, rule));
-  } else {
-    S = a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, a->q_len, max_pages);
-  }
+  const int S = c->cfg.quant ? cell_splits(c, a->n_seqs, a->split_k, max_cp)
+                             : (a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, a->q_len, max_pages));
   const int parts = c->cfg.quant ? S + 1 : S;
   if (parts <= 1) {
     *bytes = 0;
@@ -1000,7 +990,7 @@ static lkv_status attend_cell(lkv_cache* c, const lkv_attend_args* a, hipStream_
   }
   const int D = cfg.head_dim, hq = cfg.n_heads_q;
   const int max_cp = (max_far + kCodePage - 1) / kCodePage;
-  const int S = cell_splits(c, a->n_seqs, a->split_k, max_cp, bits, a->v_rule);
+  const int S = cell_splits(c, a->n_seqs, a->split_k, max_cp);
   const size_t ws_need = (size_t)a->n_seqs * hq * (S + 1) * (D + 1) * 4;
   if (!a->workspace || a->workspace_bytes < ws_need)
     return c->fail(LKV_ENOMEM, "workspace of %zu bytes needed", ws_need);

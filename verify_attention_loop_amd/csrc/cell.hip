@@ -495,7 +495,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     const uint32_t b64 = 0x54005400u, b16 = 0x4C004C00u, b4 = 0x44004400u;  // fp16 64, 16, 4 in both halves
     constexpr float kLog2e = 1.4426950408889634f;
     constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
-    const int32_t* tab_code = p.tab_code + (int64_t)slot * p.code_ring;
+    // The code-page table in the constant address space: the kernel never writes it, so its
+    // entries stay scalar loads also after a barrier (which a plain global pointer's loads do
+    // not: any barrier could order another workgroup's write before them)
+    typedef const int32_t __attribute__((address_space(4)))* const_tab_t;
+    const const_tab_t tab_code = (const_tab_t)(p.tab_code + (int64_t)slot * p.code_ring);
     constexpr uint64_t head_bytes = (uint64_t)(BITS == 4 ? 40 : 24) * D;
     // The n_splits + 1 blocks of a row take equal shares of the code pages plus the near
     // work, counted as the code pages of the same bytes (sink + tail tokens of bf16 K and V);
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     // dequant folded into the weights, which leave as fp16 pairs wpk[j] for tokens 2 j and
     // 2 j + 1 (nearest even); wacc sums the same rounded weights.
     auto far_head = [&](int cp, rsrc_t rs, float xs, float thr2, Raw<32> vm, uint32_t* wpk,
-                        uint32_t* lo16, Raw<16>& vh) {
+                        uint32_t* lo16, Raw<16>& vh, bool live = true) {
       if (cp == n_cp - 1) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -708,7 +712,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       }
       if constexpr (TRACE) {
         const uint32_t word = or4(hotbits);
-        if (lane == 0 && p.mask_trace) p.mask_trace[((int64_t)b * p.hq + h) * p.mask_words + cp] = word;
+        if (lane == 0 && live && p.mask_trace) p.mask_trace[((int64_t)b * p.hq + h) * p.mask_words + cp] = word;
       }
     };
 
@@ -824,40 +828,70 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       // s >= max(m, m0) - tau ln 2, i.e. x2 >= max(m2, m0 log2 e) - tau in base-2 units.
       // The waves take the block's pages in rounds (page c0 + WAVES r + w) and trade page
       // maxima through LDS once per round, so the rule is the sequential one whatever the
-      // schedule.  Every wave runs every round, with or without a page, to meet the barrier.
+      // schedule.  Every wave runs every round, with or without a page, to meet the barrier;
+      // a wave without a page in a round (the last one) works on an empty resource with
+      // score -inf, which leaves its state unchanged.  The steps overlap as in the fixed-rule
+      // loop: a round's key loads go out one round early, its V hi and lo rows are
+      // accumulated one round late, and the accumulation of the previous round's page covers
+      // the wait at the barrier.
       __shared__ float sm_pm[2][WAVES];
-      const float m0_2 = m0 * kLog2e;
+      // m0 and the running maximum are uniform over the wave: kept in scalar registers
+      const float m0_2 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(m0 * kLog2e)));
       float m_run = -INFINITY;
-      for (int base = c0, round = 0; base < c1; base += WAVES, ++round) {
-        const int cp = base + w;
-        const bool active = cp < c1;  // uniform per wave
-        rsrc_t rs = slice_rsrc(p.codes, 0);  // set by far_keys on an active round
-        float xs = -INFINITY;
+      const int n_rounds = (c1 - c0 + WAVES - 1) / WAVES;  // uniform per block
+      if (n_rounds > 0) {
+        int cp = c0 + w;
+        bool live = cp < c1;
+        KeyRegs kr;
         Raw<16> vh;
         Raw<32> vm;
-        float pm = -INFINITY;
-        if (active) {
-          far_keys(cp, rs, xs, vh, vm);
-          pm = fmaxf(xs, dpp<0x4E>(xs));  // -inf past the sequence
+        uint32_t wpk[4], lo16[8];
+        rsrc_t rs = far_rsrc(live ? cp : c0, live);
+        far_load_k(rs, kr);
+        far_load_v(rs, vh, vm);
+        // One round: the scores of page cp (key loads issued a round earlier), its maximum to
+        // LDS, the key loads of the next round's page, the accumulation of the previous round's
+        // page (acc), the barrier, the threshold and the value head of page cp (V hi and lo rows
+        // go out), and the V meta load of the next round's page.  The first round is its own
+        // copy, so that the loop is entered with the loads in flight that its back edge carries.
+        auto round_step = [&](int round, bool acc) {
+          float xs;
+          far_scores(cp, kr, xs);
+          if (!live) xs = -INFINITY;
+          // the page maximum: over each row (lanes 2t and 2t + 1 hold one token), then the four
+          // rows' values read into scalar registers
+          float pm = fmaxf(xs, dpp<0x4E>(xs));  // -inf past the sequence
           pm = fmaxf(pm, dpp<0x141>(pm));
           pm = fmaxf(pm, dpp<0x140>(pm));
-          pm = fmaxf(pm, __shfl_xor(pm, 16));
-          pm = fmaxf(pm, __shfl_xor(pm, 32));
-        }
-        if (lane == 0) sm_pm[round & 1][w] = pm;
-        __syncthreads();
-        float m_page = m_run;
+          const uint32_t pmi = __float_as_uint(pm);
+          pm = fmaxf(fmaxf(__uint_as_float(__builtin_amdgcn_readlane(pmi, 0)),
+                           __uint_as_float(__builtin_amdgcn_readlane(pmi, 16))),
+                     fmaxf(__uint_as_float(__builtin_amdgcn_readlane(pmi, 32)),
+                           __uint_as_float(__builtin_amdgcn_readlane(pmi, 48))));
+          if (lane == 0) sm_pm[round & 1][w] = pm;
+          const int nx = cp + WAVES;
+          const bool live2 = nx < c1;
+          const rsrc_t rs2 = far_rsrc(live2 ? nx : c0, live2);
+          far_load_k(rs2, kr);
+          if (acc) far_tail(vh, lo16, wpk);
+          __syncthreads();
+          float m_page = m_run;
 #pragma unroll
-        for (int v = 0; v < WAVES; ++v) {
-          const float pv = sm_pm[round & 1][v];
-          if (v <= w) m_page = fmaxf(m_page, pv);
-          m_run = fmaxf(m_run, pv);
-        }
-        if (active) {
-          uint32_t wpk[4], lo16[8];
-          far_head(cp, rs, xs, fmaxf(m_page, m0_2) - p.v_tau, vm, wpk, lo16, vh);
-          far_tail(vh, lo16, wpk);
-        }
+          for (int v = 0; v < WAVES; ++v) {
+            const float pv = sm_pm[round & 1][v];
+            if (v <= w) m_page = fmaxf(m_page, pv);
+            m_run = fmaxf(m_run, pv);
+          }
+          m_run = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(m_run)));
+          far_head(cp, rs, xs, fmaxf(m_page, m0_2) - p.v_tau, vm, wpk, lo16, vh, live);
+          far_load_v(rs2, vh, vm);
+          cp = nx;
+          live = live2;
+          rs = rs2;
+        };
+        round_step(0, false);
+        for (int round = 1; round < n_rounds; ++round) round_step(round, true);
+        far_tail(vh, lo16, wpk);
       }
     }
   }

@@ -58,6 +58,7 @@ struct PageRegs {
   Raw<DecodeTile<T, D>::VB> v;
   int phys_own, phys_deep;
   bool own_tok;  // plane of the lane's K row token (for the trace)
+  bool edge;     // the page straddles the RIPE window edge (uniform over the wave)
 };
 
 }  // namespace
@@ -106,6 +107,15 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kerne
   const uint64_t koff = (uint64_t)hk * HEAD + (uint64_t)krow * D * ES + 16 * g;
   const uint64_t voff = (uint64_t)p.hkv * HEAD + (uint64_t)hk * HEAD + (uint64_t)g * (kQuad * D * ES) + 16 * n;
 
+  // K goes through LDS on a page of one plane (every page but the one at the RIPE window
+  // edge): the wave reads the page's K slice of its KV head (HEAD bytes, contiguous) with
+  // whole-line streaming loads, lane l taking bytes 16 l + 1024 s, and then reads its MFMA
+  // operand pieces (row krow, 16-byte channel pieces 64 bytes apart) from LDS.  On the edge
+  // page each lane reads its operand pieces straight from its token's plane.
+  static_assert(HEAD == NB * 64 * 16, "one 16-byte piece per lane and load");
+  __shared__ __attribute__((aligned(16))) uint8_t sm_k[WAVES][HEAD];
+  const int kl = (int)(koff - (uint64_t)hk * HEAD);  // the lane's operand offset inside the slice
+
   // Issue the loads of page pg (no waits: the page's per-token plane choice for V waits
   // until compute_page).
   auto load_page = [&](int pg, PR& r) {
@@ -118,9 +128,11 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kerne
     const uint8_t* base_deep = p.pool + (uint64_t)r.phys_deep * p.page_bytes;
     const int jk = pos + krow;
     r.own_tok = jk < L ? jk >= own_lo : any_own;
-    const uint8_t* kb = (r.own_tok ? base_own : base_deep) + koff;
+    r.edge = any_own && any_deep;
+    const uint8_t* kb = (r.own_tok ? base_own : base_deep) + koff;                                    // edge page
+    const uint8_t* ks = (any_own ? base_own : base_deep) + (uint64_t)hk * HEAD + (uint64_t)lane * 16;  // slice
 #pragma unroll
-    for (int s = 0; s < NB; ++s) load_raw<16>(r.k[s], kb + 64 * s);
+    for (int s = 0; s < NB; ++s) load_stream<16>(r.k[s], r.edge ? kb + 64 * s : ks + 1024 * s);
     load_vquad<T, D>(r.v, (any_own ? base_own : base_deep) + voff);
   };
 
@@ -147,16 +159,42 @@ __global__ __launch_bounds__(WAVES * 64, D == 256 ? 2 : 1) void gqa_decode_kerne
         blend_quad<T, D>(v, vd, take_deep, zero);
       }
     }
+    // the K operand: staged through the wave's LDS slice, or (edge page) as loaded
+    Raw<16> kop[NB];
+#pragma unroll
+    for (int s = 0; s < NB; ++s) kop[s] = r.k[s];
+    if (!r.edge) {
+      // the slice is shared by the lanes of one wave: other lanes' reads of the previous
+      // page must be done before it is overwritten, and its stores visible before it is
+      // read (wavefront-scope fences around a wave barrier)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int s = 0; s < NB; ++s)
+        *reinterpret_cast<u32x4_t*>(&sm_k[w][(s * 64 + lane) * 16]) = u32x4_t{r.k[s].w[0], r.k[s].w[1], r.k[s].w[2], r.k[s].w[3]};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int s = 0; s < NB; ++s) {
+        const u32x4_t v4 = *reinterpret_cast<const u32x4_t*>(&sm_k[w][kl + 64 * s]);
+        kop[s].w[0] = v4.x;
+        kop[s].w[1] = v4.y;
+        kop[s].w[2] = v4.z;
+        kop[s].w[3] = v4.w;
+      }
+    }
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NB; ++s) {
       if constexpr (F32) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(r.k[s].w[e]), __uint_as_float(qb[s][e]), sc, 0,
+          sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kop[s].w[e]), __uint_as_float(qb[s][e]), sc, 0,
                                                     0, 0);
       } else {
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[s].w),
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kop[s].w),
                                                      __builtin_bit_cast(bf16x8_t, qb[s]), sc, 0, 0, 0);
       }
     }

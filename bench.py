@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--v-tau", type=float, default=14.0, help="tau of the running-maximum rule")
     ap.add_argument("--v-offset", type=float, default=4.0,
                     help="fixed rule's offset: a far token is hot iff its score >= m0 - offset (the workload: 4.0)")
+    ap.add_argument("--ripen", choices=["workload", "paper"], default="workload",
+                    help="ripening planes (Huginn-shaped workloads): the workload's noise 0.88^(R-1-r) on plane r, or "
+                         "0.88^(r+1), the RIPE page's direction (values only: no byte count or plane read changes)")
     ap.add_argument("--also", default="auto",
                     help="workloads timed after the first one in the same run, reported under 'secondary' "
                          "(comma-separated; 'auto': huginn_ripe when no --workload is given, else none; 'none')")
@@ -308,6 +311,8 @@ def run_workload(args, workload: str, prober, with_cpu: bool) -> dict:
         w = dataclasses.replace(w, batch=args.batch)
     if args.policy != "default" and not w.quant and args.policy != w.policy:
         w = dataclasses.replace(w, policy=args.policy, window=w.window if args.policy == "ripe" else 0)
+    if args.ripen == "paper" and w.mode == synth.MODE_RIPEN:
+        w = dataclasses.replace(w, mode=synth.MODE_RIPEN_PAPER)
     t_setup = time.perf_counter()
     R, B, q_len = w.n_loops, w.batch, w.q_len
     split = w.split_k if args.split_k < 0 else args.split_k
@@ -464,8 +469,9 @@ def run_workload(args, workload: str, prober, with_cpu: bool) -> dict:
         data = "synthetic (seeded counter-hash generator: binomial codes, fp16 metadata, seeded cell plan)"
     else:
         dtype = "bf16" if w.dtype == synth.DT_BF16 else "f32"
-        data = ("synthetic (seeded counter-hash generator; Huginn-shaped ripening planes)"
-                if w.mode == synth.MODE_RIPEN else "synthetic (seeded counter-hash generator)")
+        data = ("synthetic (seeded counter-hash generator; Huginn-shaped ripening planes)" if w.mode == synth.MODE_RIPEN
+                else "synthetic (seeded counter-hash generator; ripening planes in the RIPE page's direction)"
+                if w.mode == synth.MODE_RIPEN_PAPER else "synthetic (seeded counter-hash generator)")
     cfg = {"workload": w.name, "batch": B, "core_layers": w.n_layers, "loops": R, "heads": w.n_heads,
            "kv_heads": w.hkv,
            "head_dim": w.head_dim, "context": w.length, "q_len": q_len, "policy": w.policy, "window": w.window,

@@ -15,7 +15,10 @@ Definitions (identical in ``synth.h`` for the GPU fill kernels):
   so the value is exact in fp32; bf16/fp16 by explicit round-to-nearest-even;
 * ripening planes (the Huginn-shaped workload): plane r < R-1 equals the
   deepest plane plus ``0.88^(R-1-r)`` times an independent normal, summed in
-  fp64 (the product is exact) and rounded once to bf16;
+  fp64 (the product is exact) and rounded once to bf16 (``MODE_RIPEN``, the
+  workload's literal recipe); ``MODE_RIPEN_PAPER`` takes ``0.88^(r+1)`` instead,
+  the direction of the RIPE page's ripening fit (the difference to the deepest
+  plane shrinks geometrically as the loop index grows, Sec. 3.2);
 * codes: Binomial(2^b - 1, 1/2) via the popcount of 2^b - 1 hashed bits;
   scales ``base * (1 + u/2^21)`` and zeros ``-mid * scale + n/8`` in fp16.
 """
@@ -38,7 +41,7 @@ T_KCODE, T_VCODE, T_KSCALE, T_KZERO, T_VSCALE, T_VZERO = 6, 7, 8, 9, 10, 11
 T_DRAFTK, T_DRAFTV, T_PLAN, T_PERM = 12, 13, 14, 15
 
 DT_F32, DT_BF16 = 0, 1
-MODE_PLAIN, MODE_RIPEN = 0, 1
+MODE_PLAIN, MODE_RIPEN, MODE_RIPEN_PAPER = 0, 1, 2
 CELL_BF16, CELL_INT4, CELL_INT2, CELL_SHARED = 0, 1, 2, 3
 
 
@@ -165,7 +168,7 @@ def kv(dtype: int, seed: int, tensor: int, seq: int, layer: int, plane: int, n_h
     """
     heads = list(range(n_heads)) if heads is None else list(heads)
     deepest = n_loops - 1
-    ripen = mode == MODE_RIPEN and plane != deepest
+    ripen = mode in (MODE_RIPEN, MODE_RIPEN_PAPER) and plane != deepest
     pos = np.arange(pos0, pos0 + n_pos, dtype=np.uint64)
     elem = (pos[:, None] * np.uint64(d) + np.arange(d, dtype=np.uint64)[None, :])
     sc = np.float32(scale)
@@ -175,7 +178,7 @@ def kv(dtype: int, seed: int, tensor: int, seq: int, layer: int, plane: int, n_h
         base = (normal_f32(stream_key(seed, tensor, seq, layer, base_plane, h), elem) * sc).astype(np.float32)
         if ripen:
             noise = (normal_f32(stream_key(seed, tensor + 3, seq, layer, plane, h), elem) * sc).astype(np.float32)
-            coef = np.float64(ripen_coef(deepest - plane))
+            coef = np.float64(ripen_coef(deepest - plane if mode == MODE_RIPEN else plane + 1))
         if dtype == DT_F32:
             if ripen:
                 out[:, hi, :] = (base.astype(np.float64) + coef * noise.astype(np.float64)).astype(np.float32)

@@ -34,14 +34,16 @@ __global__ void fill_kv_kernel(void* dst, int dtype, uint64_t seed, uint32_t ten
     const int h = (int)((idx / d) % n_heads);
     const int p = (int)(idx / ((int64_t)d * n_heads));
     const uint64_t elem = (uint64_t)(pos0 + p) * (uint64_t)d + (uint64_t)c;
-    const bool ripen = (mode == 1) && (plane != deepest);
+    // mode 1: noise 0.88^(R-1-r) (the workload's recipe); mode 2: 0.88^(r+1) (the page's direction)
+    const bool ripen = (mode == 1 || mode == 2) && (plane != deepest);
+    const int coef_k = mode == 1 ? (int)(deepest - plane) : (int)plane + 1;
     const uint32_t base_plane = ripen ? deepest : plane;
     const float base = normal_f32(stream_key(seed, tensor, seq, layer, base_plane, h), elem) * scale;
     if (dtype == 0) {
       float out = base;
       if (ripen) {
         const float noise = normal_f32(stream_key(seed, tensor + 3u, seq, layer, plane, h), elem) * scale;
-        const float coef = ripen_coef((int)(deepest - plane));
+        const float coef = ripen_coef(coef_k);
         out = (float)__dadd_rn((double)base, __dmul_rn((double)coef, (double)noise));
       }
       ((float*)dst)[idx] = out;
@@ -49,7 +51,7 @@ __global__ void fill_kv_kernel(void* dst, int dtype, uint64_t seed, uint32_t ten
       uint16_t out = bf16_from_f32(base);
       if (ripen) {
         const float noise = normal_f32(stream_key(seed, tensor + 3u, seq, layer, plane, h), elem) * scale;
-        const float coef = ripen_coef((int)(deepest - plane));
+        const float coef = ripen_coef(coef_k);
         const double sum = __dadd_rn((double)f32_from_bf16(out), __dmul_rn((double)coef, (double)noise));
         out = bf16_from_f64(sum);
       }

@@ -93,6 +93,28 @@ def test_ragged_lengths_bf16(D, policy):
     built.cache.close()
 
 
+@pytest.mark.parametrize("policy", [vla.POLICY_FULL, vla.POLICY_RIPE])
+def test_ripening_planes_in_the_page_direction(policy):
+    """Planes ripening in the RIPE page's direction (MODE_RIPEN_PAPER: plane r = plane R + 0.88^(r+1) noise,
+    shrinking with r, Sec. 3.2): the GPU fill kernel writes the planes the numpy generator gives the oracle, and
+    the path matches the oracle as under the workload's recipe (ragged lengths, loops 0 / 2 / deepest, splits 1
+    and 2)."""
+    w = _ragged(96, synth.MODE_RIPEN_PAPER)
+    lengths = [1, 17, 100, 257]
+    built = harness.build_plain(w, lengths=lengths, layers=(1,), policy=policy, window=20, shuffle=True,
+                                poison=True)
+    rows = [(b, 0, h) for b in range(len(lengths)) for h in range(w.n_heads)]
+    for loop in (0, 2, w.n_loops - 1):
+        want, want_lse = harness.oracle_rows(w, rows, 1, loop, lengths, 1, policy, 20)
+        q = harness.gpu_queries(built, 1, loop, 1)
+        for split_k in (1, 2):
+            out, lse, _ = _attend(built, 1, loop, q, split_k)
+            got = harness.out_f64(out)[:, 0]
+            assert np.abs(got.reshape(-1, w.head_dim) - want).max() <= TOL_BF16, (loop, split_k)
+            assert np.abs(lse.cpu().numpy()[:, 0].reshape(-1) - want_lse).max() <= 1e-3
+    built.cache.close()
+
+
 def test_shuffled_tables_are_bitwise_identical_to_identity_tables():
     """Paging changes addresses, not values: identical outputs for shuffled and in-order page tables."""
     w = _ragged(96)

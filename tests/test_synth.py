@@ -78,6 +78,21 @@ def test_ripening_noise_grows_with_the_loop_index():
         assert abs(sd / 0.88 ** (R - 1 - r) - 1.0) < 0.05, (r, sd)
 
 
+def test_ripening_noise_in_the_page_direction_shrinks_with_the_loop_index():
+    """MODE_RIPEN_PAPER, the RIPE page's direction (Sec. 3.2: the difference to the deepest plane shrinks
+    geometrically as the loop index grows): plane r - plane R has standard deviation 0.88^(r+1) (0.88 at r = 0,
+    0.019 at r = R - 2), and the deepest plane is the same as under the workload's recipe."""
+    R = 32
+    deep = synth.kv(synth.DT_BF16, 0, synth.T_K, 0, 0, R - 1, 2, 96, 0, 512, synth.MODE_RIPEN_PAPER, R)
+    assert np.array_equal(deep, synth.kv(synth.DT_BF16, 0, synth.T_K, 0, 0, R - 1, 2, 96, 0, 512, synth.MODE_RIPEN, R))
+    deep = synth.f32_from_bf16(deep).astype(np.float64)
+    for r in (0, 16, 30):
+        pr = synth.f32_from_bf16(synth.kv(synth.DT_BF16, 0, synth.T_K, 0, 0, r, 2, 96, 0, 512,
+                                          synth.MODE_RIPEN_PAPER, R)).astype(np.float64)
+        sd = (pr - deep).std()
+        assert abs(sd / 0.88 ** (r + 1) - 1.0) < 0.05, (r, sd)
+
+
 def test_codes_and_metadata_ranges():
     c4 = synth.codes(0, synth.T_KCODE, 0, 0, 0, 2, 32, 0, 500, 4)
     c2 = synth.codes(0, synth.T_KCODE, 0, 0, 0, 2, 32, 0, 500, 2)

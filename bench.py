@@ -263,10 +263,16 @@ def read_traffic(workload: str, khash: str):
     return int(float(kv["bytes_per_launch"]))
 
 
-def cpu_baseline_cells(bc, seconds: float):
+def cpu_baseline_cells(bc, seconds: float, v_rule: str = "fixed", v_offset: float = 4.0, v_tau: float = 14.0,
+                       n_splits: int = 1):
     """The fp64 oracle's cell routine, as it stands, on a bounded sample of the quantised-cell workload:
     rows (seq, layer 0, loop, head) of every loop with inputs regenerated on the host (not timed), repeated
-    until `seconds` of oracle time accumulate."""
+    until `seconds` of wall time pass, under the timed V-precision rule (the fixed rule at m0 - v_offset, or
+    the page's running rule at v_tau over the call's n_splits far splits).  The routine computes one row per
+    call, so the rows go to as many host threads as the oracle's plain row loop uses (each call releases the
+    interpreter lock); the same rows on one thread, for about a fifth of the time, give the one-core rate."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import harness
@@ -278,19 +284,45 @@ def cpu_baseline_cells(bc, seconds: float):
     for i in range(8):
         b, h, r = int(rng.integers(w.batch)), int(rng.integers(w.n_heads)), i % w.n_loops
         rows.append(harness.cell_inputs(bc, b, 0, r, h))
-    done, elapsed = 0, 0.0
-    while elapsed < seconds:
-        for a in rows:
-            t1 = time.perf_counter()
-            oracle.cell_row(a["q"], a["k_near"], a["v_near"], a["kc"], a["ks"], a["kz"], a["vc"], a["vs"], a["vz"],
-                            a["sink"], a["tail"], a["kind"], 4.0)
-            elapsed += time.perf_counter() - t1
-            done += 1
+
+    def row(a):
+        args = (a["q"], a["k_near"], a["v_near"], a["kc"], a["ks"], a["kz"], a["vc"], a["vs"], a["vz"], a["sink"],
+                a["tail"], a["kind"])
+        if v_rule == "running":
+            oracle.cell_row_running(*args, v_tau, n_splits)
+        else:
+            oracle.cell_row(*args, v_offset)
+
+    done1, elapsed1 = 0, 0.0
+    while elapsed1 < seconds / 5:
+        t1 = time.perf_counter()
+        row(rows[done1 % len(rows)])
+        elapsed1 += time.perf_counter() - t1
+        done1 += 1
+    cores = oracle.threads()
+    t_start = time.perf_counter()
+    t_end = t_start + seconds
+
+    def worker(k):
+        n = 0
+        while n == 0 or time.perf_counter() < t_end:
+            row(rows[(k + n) % len(rows)])
+            n += 1
+        return n
+
+    with ThreadPoolExecutor(cores) as ex:
+        done = sum(ex.map(worker, range(cores)))
+    elapsed = time.perf_counter() - t_start
     rows_per_token = w.n_layers * w.n_heads
-    return {"value": done / elapsed / rows_per_token, "unit": "loop-query tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": done / elapsed / rows_per_token, "unit": "loop-query tokens/s", "cores": cores, "kind": "oracle",
             "host": host_info(),
+            "one_core": {"value": done1 / elapsed1 / rows_per_token, "seconds": round(elapsed1, 1),
+                         "row_ms": round(1e3 * elapsed1 / done1, 3)},
             "sample": f"{done} cell rows ({len(rows)} distinct (seq, layer 0, loop, head) rows of the {w.name} "
-                      f"workload, L={w.length}, repeated) in {elapsed:.1f} s of fp64 oracle time on one thread; "
+                      f"workload, L={w.length}, repeated, "
+                      + (f"running rule at tau {v_tau} over {n_splits} far splits" if v_rule == "running"
+                         else f"fixed rule at m0 - {v_offset}")
+                      + f") in {elapsed:.1f} s of fp64 oracle time on {cores} threads; "
                       f"{rows_per_token} rows = 1 loop-query token"}
 
 
@@ -462,7 +494,13 @@ def run_workload(args, workload: str, prober, with_cpu: bool) -> dict:
 
     cpu = None
     if with_cpu and not args.no_cpu_baseline:
-        cpu = cpu_baseline_cells(built, args.cpu_seconds) if w.quant else cpu_baseline(w, args.cpu_seconds)
+        if w.quant:
+            # the call's far splits (the running rule's runs), read back from the workspace size
+            # [rows][S + 1][d + 1] fp32
+            n_far_splits = ws_bytes // (B * w.n_heads * (w.head_dim + 1) * 4) - 1
+            cpu = cpu_baseline_cells(built, args.cpu_seconds, args.v_rule, args.v_offset, args.v_tau, n_far_splits)
+        else:
+            cpu = cpu_baseline(w, args.cpu_seconds)
 
     if w.quant:
         dtype = "int4/int2 codes + bf16 near, fp32 accumulate"

@@ -1,7 +1,8 @@
 """Calls with more sequences than one launch takes (64 per launch): the library issues such a call as several
 launches over consecutive groups of 64 sequences, each with its own offsets into the queries, outputs, lse,
-split workspace and traces.  Decode (unsplit and with split partials), verify (q = k, causal inside the block;
-RIPE page, Algorithm 1 and Eq. (9)), grouped-query decode and quantised cells (LoopKV page, Sec. 3.1-3.4) over
+split workspace, draft scratch and traces.  Decode (unsplit and with split partials), verify (q = k, causal
+inside the block; RIPE page, Algorithm 1 and Eq. (9)), the draft step, grouped-query decode and quantised cells
+(LoopKV page, Sec. 3.1-3.4) over
 70 / 66 ragged sequences, against the fp64 oracle on every row of every launch; the index and mask traces of the
 later launch land on their own rows; the entry point that allocates nothing gives the same bits."""
 import numpy as np
@@ -85,6 +86,47 @@ def test_decode_and_verify_past_one_launch(hq, hkv):
             got, lse, _ = _call(built, loop, qk, vla.MODE_VERIFY, split_k)
             assert np.abs(got.reshape(-1, w.head_dim) - want).max() <= TOL, (loop, split_k)
             assert np.abs(lse.reshape(-1) - want_lse).max() <= 1e-2, (loop, split_k)
+    built.cache.close()
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2)])
+def test_draft_step_past_one_launch(hq, hkv):
+    """The draft step (RIPE page, Algorithm 1: cached positions through the policy at W = 0, the block's own keys
+    and values from caller scratch, whose rows take the same per-launch offsets) over 70 ragged sequences with a
+    3-token draft block, unsplit and with 2 splits: every row within 2e-2 of the oracle."""
+    dl = 3
+    w = synth.Workload("chunks", N_SEQS, 1, 3, hq, 64, 48, synth.DT_BF16, "ripe", 0, 1, 16, synth.MODE_RIPEN, 1.0,
+                       n_kv_heads=hkv)
+    n_cached = _lengths(N_SEQS, 17, 29)
+    built = harness.build_plain(w, lengths=n_cached, layers=(0,), policy=vla.POLICY_RIPE, window=0, q_len=1,
+                                shuffle=True, poison=True, max_block=8)
+    R, D, group = w.n_loops, w.head_dim, hq // hkv
+    for loop in (0, 1):
+        dk, dv = harness.gpu_draft_kv(w, built.rows, 0, loop, n_cached, dl)
+        q = harness.gpu_queries(built, 0, loop, 1, t0s=[n + dl - 1 for n in n_cached])
+        want = []
+        for b, n in enumerate(n_cached):
+            L = n + dl
+            for h in range(hq):
+                hk = h // group
+                ko = harness.cpu_values(w, synth.T_K, b, 0, loop, hk, L)
+                vo = harness.cpu_values(w, synth.T_V, b, 0, loop, hk, L)
+                kd = harness.cpu_values(w, synth.T_K, b, 0, R - 1, hk, L)
+                vd = harness.cpu_values(w, synth.T_V, b, 0, R - 1, hk, L)
+                ko[n:] = harness.cpu_draft_values(w, synth.T_DRAFTK, b, 0, loop, hk, n, dl)
+                vo[n:] = harness.cpu_draft_values(w, synth.T_DRAFTV, b, 0, loop, hk, n, dl)
+                qq = harness.cpu_query(w, b, 0, loop, h, L - 1)
+                want.append(oracle.attend_row(qq, ko, vo, kd, vd, L - 1, n, oracle.RIPE, loop, R, 0)[0])
+        want = np.array(want)
+        for split_k in (1, 2):
+            out = torch.full_like(q, float("nan"))
+            wsb = built.cache.lkv_workspace_bytes(0, loop, built.seqs, mode=vla.MODE_DRAFT, split_k=split_k)
+            ws = torch.empty(max(4, wsb), dtype=torch.uint8, device="cuda")
+            built.cache.lkv_attend(0, loop, built.seqs, q, out, mode=vla.MODE_DRAFT, window=0, split_k=split_k,
+                                   workspace=ws, draft_k=dk, draft_v=dv, draft_len=dl)
+            torch.cuda.synchronize()
+            got = harness.out_f64(out)[:, 0].reshape(-1, D)
+            assert np.abs(got - want).max() <= TOL, (loop, split_k)
     built.cache.close()
 
 

@@ -3,8 +3,11 @@
 Builds a ``LoopCache`` for a ``synth.Workload`` by generating each plane on the
 GPU with the seeded fill kernels and appending it through the C-ABI, exactly as
 a serving engine would append the planes its loops produce.  It also assembles
-the CPU-side inputs of sampled rows (same generator, same bits) for the oracle.
-This module does no attention arithmetic.
+the CPU-side inputs of sampled rows (same generator, same bits) for the oracle;
+the functions that reach the oracle (``oracle_rows``, ``cell_inputs``,
+``cell_oracle_row``) import it on call and serve only the tests, ``smoke()`` and
+``bench.py``'s ``cpu_baseline`` leg, never a timed or product path.  This module
+does no attention arithmetic.
 """
 from __future__ import annotations
 

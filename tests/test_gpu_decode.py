@@ -93,6 +93,33 @@ def test_ragged_lengths_bf16(D, policy):
     built.cache.close()
 
 
+@pytest.mark.parametrize("D", [96, 128])
+@pytest.mark.parametrize("waves", [2, 4, 8])
+def test_waves_per_workgroup(D, waves):
+    """The multi-head decode kernel at 2, 4 and 8 waves per workgroup (the library picks 2 for grids of 768-1024
+    workgroups, else 8): ragged lengths 1-257, RIPE W = 20, loops 0 / 2 / deepest, splits 1 and 3, every row
+    against the oracle."""
+    w = _ragged(D)
+    lengths = [1, 15, 16, 17, 100, 257]
+    built = harness.build_plain(w, lengths=lengths, layers=(1,), policy=vla.POLICY_RIPE, window=20, shuffle=True,
+                                poison=True)
+    rows = [(b, 0, h) for b in range(len(lengths)) for h in range(w.n_heads)]
+    for loop in (0, 2, w.n_loops - 1):
+        want, want_lse = harness.oracle_rows(w, rows, 1, loop, lengths, 1, vla.POLICY_RIPE, 20)
+        q = harness.gpu_queries(built, 1, loop, 1)
+        for split_k in (1, 3):
+            out = torch.empty_like(q)
+            lse = torch.empty((len(lengths), 1, w.n_heads), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(4, built.cache.lkv_workspace_bytes(1, loop, built.seqs, split_k=split_k)),
+                             dtype=torch.uint8, device="cuda")
+            built.cache.lkv_attend(1, loop, built.seqs, q, out, split_k=split_k, lse=lse, workspace=ws, waves=waves)
+            torch.cuda.synchronize()
+            got = harness.out_f64(out)[:, 0].reshape(-1, D)
+            assert np.abs(got - want).max() <= TOL_BF16, (loop, split_k)
+            assert np.abs(lse.cpu().numpy()[:, 0].reshape(-1) - want_lse).max() <= 1e-3, (loop, split_k)
+    built.cache.close()
+
+
 @pytest.mark.parametrize("policy", [vla.POLICY_FULL, vla.POLICY_RIPE])
 def test_ripening_planes_in_the_page_direction(policy):
     """Planes ripening in the RIPE page's direction (MODE_RIPEN_PAPER: plane r = plane R + 0.88^(r+1) noise,

@@ -854,17 +854,6 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
   const int group = cfg.n_heads_q / cfg.n_heads_kv;
   const bool gqa = a->mode == LKV_MODE_DECODE && (group == 2 || group == 4 || group == 8) &&
                    a->kernel == LKV_KERNEL_AUTO;
-  // Waves per workgroup (defaults measured best on MI355X at the workloads' shapes): 8 for
-  // multi-head q = 1 rows, 4 for grouped-query rows (and the grouped VALU kernel, whose
-  // registers grow with G), 2 for verify tiles.
-  const int waves = a->waves > 0 ? a->waves
-                    : a->mode == LKV_MODE_VERIFY ? 2
-                    : gqa                        ? 4
-                                                 : (group == 1 ? 8 : 4);
-  const bool waves_ok = a->mode == LKV_MODE_VERIFY ? (waves == 1 || waves == 2 || waves == 4)
-                        : gqa                      ? (waves == 1 || waves == 2 || waves == 4)
-                                                   : (waves == 2 || waves == 4 || waves == 8);
-  if (!waves_ok) return c->fail(LKV_EINVAL, "waves %d is not built for this kernel", waves);
   const int window = a->window < 0 ? cfg.window : a->window;
   const int R = cfg.n_loops;
   const bool ripe = cfg.policy == LKV_POLICY_RIPE && a->loop != R - 1;
@@ -874,6 +863,24 @@ lkv_status lkv_attend(lkv_cache* c, const lkv_attend_args* a, void* stream) {
   int max_pages = 0;
   for (const auto& r : rows) max_pages = std::max(max_pages, (r.n_cached + kPage - 1) / kPage);
   const int S = a->split_k > 0 ? a->split_k : auto_splits(c, a->n_seqs, a->mode, a->q_len, max_pages);
+  // Waves per workgroup (defaults measured best on MI355X): 2 for verify tiles, 4 for
+  // grouped-query rows (and the grouped VALU kernel, whose registers grow with G), and for
+  // multi-head q = 1 rows 8, except 2 when the grid has 768-1024 workgroups: there the 8-wave
+  // grid is about one generation of resident waves (seven per SIMD) and 2-wave workgroups, at
+  // 1.5-2 waves per SIMD with twice the pages per wave, measured 1-8% faster (Huginn shape at
+  // 14, 16 and 18 sequences: 52.4 -> 48.1, 57.4 -> 54.8, 61.8 -> 61.0 us); below that band
+  // they leave SIMDs idle (12 sequences: 44.3 -> 45.1 us), above it 8 waves stay ahead.
+  const int64_t wgs = (int64_t)a->n_seqs * cfg.n_heads_kv * S;
+  const int waves = a->waves > 0 ? a->waves
+                    : a->mode == LKV_MODE_VERIFY ? 2
+                    : gqa                        ? 4
+                    : group != 1                 ? 4
+                    : (wgs >= 768 && wgs <= 1024) ? 2
+                                                  : 8;
+  const bool waves_ok = a->mode == LKV_MODE_VERIFY ? (waves == 1 || waves == 2 || waves == 4)
+                        : gqa                      ? (waves == 1 || waves == 2 || waves == 4)
+                                                   : (waves == 2 || waves == 4 || waves == 8);
+  if (!waves_ok) return c->fail(LKV_EINVAL, "waves %d is not built for this kernel", waves);
   const int D = cfg.head_dim, hq = cfg.n_heads_q, es = elem_bytes(cfg);
   const size_t ws_need = S > 1 ? (size_t)a->n_seqs * a->q_len * hq * S * (D + 1) * 4 : 0;
   if (ws_need > 0 && (!a->workspace || a->workspace_bytes < ws_need))

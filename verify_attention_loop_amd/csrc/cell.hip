@@ -494,6 +494,10 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     m0 = fmaxf(m0, __shfl_xor(m0, 32));
     const uint32_t b64 = 0x54005400u, b16 = 0x4C004C00u, b4 = 0x44004400u;  // fp16 64, 16, 4 in both halves
     constexpr float kLog2e = 1.4426950408889634f;
+    // headroom of a row's far reference over the page maximum that set it (base-2 units):
+    // the largest weight of that page is 2^-2, and later pages rescale only on a new
+    // maximum more than that above it
+    constexpr float kFarHeadroom = 2.f;
     constexpr bool masked = BITS == 4;  // INT4 and shared cells carry the hi / lo bit planes
     // The code-page table in the constant address space: the kernel never writes it, so its
     // entries stay scalar loads also after a barrier (which a plain global pointer's loads do
@@ -519,6 +523,33 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     }
     constexpr uint64_t vcode_off = BITS == 4 ? 20 * D : 12 * D;
     constexpr uint64_t vmeta_off = BITS == 4 ? 36 * D : 20 * D;
+    // INT2 cells: the query for the far keys as an fp16 pair per channel c, (-off_c q_c 2^s,
+    // q_c 2^s), where off_c is the offset of the channel's code pairs and 2^s puts the row's
+    // largest |q_c| in [512, 1024).  Both elements are exact fp16 values (a bf16 query has 8
+    // significant bits, and 64 x 1024 stays below the fp16 maximum); only channels more than
+    // 2^23 below the largest fall to fp16 subnormals, where their products are under the fp32
+    // rounding of the score.  One v_dot2 of the pair with the page's (sigma_c, z_c) metadata
+    // adds both q_c z_c and the code offset's share to a page's bias, and the scores, 2^s too
+    // large, come back through the scale.  (INT4 cells keep the query as 4 bf16 pair
+    // registers: their loops have no room for 8.)
+    uint32_t qp[E] = {};
+    float scale2 = p.scale_log2;
+    if constexpr (BITS == 2) {
+      float qa = 0.f;
+#pragma unroll
+      for (int x = 0; x < E / 2; ++x) qa = fmaxf(qa, fmaxf(fabsf(bf_lo(qw[x])), fabsf(bf_hi(qw[x]))));
+      qa = row_max16(qa);  // the 16 lanes of a DPP row hold the head's D channels
+      int qe = 0;
+      (void)frexpf(qa, &qe);  // qa in [2^(qe - 1), 2^qe)
+      const int s = qa > 0.f ? min(10 - qe, 100) : 0;
+      const float up = ldexpf(1.f, s);
+#pragma unroll
+      for (int c = 0; c < E; ++c) {
+        const float qt = ((c & 1) ? bf_hi(qw[c >> 1]) : bf_lo(qw[c >> 1])) * up;
+        qp[c] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)(-int2_off(c) * qt), (_Float16)qt});
+      }
+      scale2 = p.scale_log2 * ldexpf(1.f, -s);
+    }
     // the lane's byte offsets inside a page's head slice, 32-bit so that each load takes the
     // page's address in scalar registers plus one lane offset (lane = 16 g + li)
     const uint32_t off_km = (uint32_t)li * 32u, off_k = 4u * D + (uint32_t)lane * 16u;
@@ -561,20 +592,29 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       const Raw<32>& km = kr.km;
       const Raw<16>& k0 = kr.k0;
       const Raw<16>& k1 = kr.k1;
-      // q' = q sigma and bias = q . z; fma with a zero addend so the fp16 operand folds into
-      // v_fma_mix_f32 (q sigma is exact in fp32: bf16 x fp16)
+      // q' = q sigma (2^s too large): fp16 x fp16, exact in fp32, as one v_fma_mix_f32 with a
+      // zero addend; the codes reach the scores as fp16 pairs (off + c) through v_fma_mix_f32
+      // (the fp16 operand converts exactly), and the bias q . z - sum_c off_c q'_c takes one
+      // v_dot2 of the channel's query pair with its (sigma, z) metadata
       float qs[E], bias = 0.f;
+      if constexpr (BITS == 2) {
 #pragma unroll
-      for (int c = 0; c < E; ++c) {
-        // q_c from the bf16 pairs per page (4 registers across the loop instead of 8)
-        const float qc = (c & 1) ? bf_hi(qw[c >> 1]) : bf_lo(qw[c >> 1]);
-        qs[c] = fmaf(qc, f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
-        bias = fmaf(qc, f16_to_f32(km.w[c] >> 16), bias);
+        for (int c = 0; c < E; ++c) {
+          qs[c] = fmaf(f16_hi_f32(qp[c]), f16_to_f32(km.w[c] & 0xFFFFu), 0.f);  // both fp16: exact
+          bias = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, qp[c]), __builtin_bit_cast(f16x2_t, km.w[c]),
+                                        bias, false);
+        }
+      } else {
+        // (INT4: q_c from the bf16 pairs per page; bf16 x fp16 is exact in fp32 too)
+#pragma unroll
+        for (int c = 0; c < E; ++c) {
+          const float qc = (c & 1) ? bf_hi(qw[c >> 1]) : bf_lo(qw[c >> 1]);
+          qs[c] = fmaf(qc, f16_to_f32(km.w[c] & 0xFFFFu), 0.f);
+          bias = fmaf(qc, f16_to_f32(km.w[c] >> 16), bias);
+        }
+#pragma unroll
+        for (int c = 0; c < E; ++c) bias = fmaf(-int4_off(c), qs[c], bias);
       }
-      // the codes reach the scores as fp16 pairs (off + c) through v_fma_mix_f32 (the fp16
-      // operand converts exactly), and sum off q' comes off the bias
-#pragma unroll
-      for (int c = 0; c < E; ++c) bias = fmaf(BITS == 4 ? -int4_off(c) : -int2_off(c), qs[c], bias);
       float sc[8];  // slot s: the lane's K code word s, token g + 4 (s ^ (li >> 1)) (kslot)
       if constexpr (BITS == 4) {
         // slots s and 7 - s one after the other: the transposed row sum's first step pairs them,
@@ -610,7 +650,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       }
       // the row sums of the eight tokens, transposed: this lane keeps the score of its own
       // token g + 4 (li / 2) (base-2 units)
-      xs = row_sum16_t8(sc) * p.scale_log2;
+      xs = row_sum16_t8(sc) * scale2;
       // Past the sequence (last page only): score -inf here, and far_head clears those
       // tokens' V meta, so that they get zero weight against finite scales whatever the page
       // holds there.  (Tested as "the last code page": the past-the-end test implies "the
@@ -643,16 +683,27 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       const bool hot_own = masked ? xs >= thr2 : xs > -INFINITY;
       // online softmax of this row, one token per lane pair: the page maximum over the row,
       // the lane's own weight, and st.l summing the lane's own weights (the row's sum is
-      // half the sum over its lanes)
-      float mx = fmaxf(xs, dpp<0x4E>(xs));  // lanes 2t and 2t + 1 hold the same token
-      mx = fmaxf(mx, dpp<0x141>(mx));
-      mx = fmaxf(mx, dpp<0x140>(mx));
-      const float mn = fmaxf(st.m, mx);
-      const float mu = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(st.m - mu);
+      // half the sum over its lanes).  The reference st.m moves only when the page's maximum
+      // passes it, and then to that maximum plus kFarHeadroom, so weights stay at most 1 (the
+      // fp16 weight pairs cannot overflow) and a wave skips the rescale of its accumulators
+      // on every page where none of its rows passes its reference.
+      float mx = dpp_max<0x4E>(xs);  // lanes 2t and 2t + 1 hold the same token
+      mx = dpp_max<0x141>(mx);
+      mx = dpp_max<0x140>(mx);
+      const bool grow = mx > st.m;
+      if (lazy_any(grow)) {
+        const float mn = grow ? mx + kFarHeadroom : st.m;
+        const float alpha = grow ? fast_exp2(st.m - mn) : 1.f;  // 0 from an empty state
+        st.l *= alpha;
+#pragma unroll
+        for (int c = 0; c < E; ++c) o[c] *= alpha;
+        zacc *= alpha;
+        wacc *= alpha;
+        st.m = mn;
+      }
+      const float mu = (st.m == -INFINITY) ? 0.f : st.m;
       const float p_own = fast_exp2(xs - mu);
-      st.l = fmaf(st.l, alpha, p_own);
-      st.m = mn;
+      st.l += p_own;
       // every lane needs the eight weights and hot bits: broadcast from lane 2i of the row,
       // the hot bit riding in the sign (a cold or absent token, p = 0 included, has it set)
       const float ps = hot_own ? p_own : -p_own;
@@ -676,10 +727,6 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
           if (TRACE && hot[i]) hotbits |= 1u << (g + 4 * i);
         }
       }
-#pragma unroll
-      for (int c = 0; c < E; ++c) o[c] *= alpha;
-      zacc *= alpha;
-      wacc *= alpha;
       // V meta of the lane's group for its 8 tokens; fold scale and zero into the weights
       // (tokens past the sequence have p = 0 and cleared meta)
       float wgt[8];
@@ -860,9 +907,9 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
           if (!live) xs = -INFINITY;
           // the page maximum: over each row (lanes 2t and 2t + 1 hold one token), then the four
           // rows' values read into scalar registers
-          float pm = fmaxf(xs, dpp<0x4E>(xs));  // -inf past the sequence
-          pm = fmaxf(pm, dpp<0x141>(pm));
-          pm = fmaxf(pm, dpp<0x140>(pm));
+          float pm = dpp_max<0x4E>(xs);  // -inf past the sequence
+          pm = dpp_max<0x141>(pm);
+          pm = dpp_max<0x140>(pm);
           const uint32_t pmi = __float_as_uint(pm);
           pm = fmaxf(fmaxf(__uint_as_float(__builtin_amdgcn_readlane(pmi, 0)),
                            __uint_as_float(__builtin_amdgcn_readlane(pmi, 16))),

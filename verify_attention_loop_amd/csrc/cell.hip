@@ -260,6 +260,17 @@ hipError_t launch_pack_codes(const PackParams& p, int head_dim, hipStream_t s) {
   return hipGetLastError();
 }
 
+// max(x, its DPP partner) as v_med3_f32(x, y, +inf): for the non-NaN scores it sees this is
+// the larger one, and unlike fmaxf it does not quiet its DPP-moved input first (one VALU
+// instruction fewer per step).  The +inf comes through an empty asm so that the compiler
+// does not turn the median back into a max.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+  float inf = __builtin_inff();
+  asm("" : "+s"(inf));
+  return __builtin_amdgcn_fmed3f(x, dpp<CTRL>(x), inf);
+}
+
 __device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }

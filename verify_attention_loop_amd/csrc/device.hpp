@@ -72,17 +72,6 @@ __device__ __forceinline__ float row_bcast(float x) {
   return dpp<0x150 + N>(x);
 }
 
-// max(x, its DPP partner) as v_med3_f32(x, y, +inf): for the non-NaN scores it sees this is
-// the larger one, and unlike fmaxf it does not quiet its DPP-moved input first (one VALU
-// instruction fewer per step).  The +inf comes through an empty asm so that the compiler
-// does not turn the median back into a max.
-template <int CTRL>
-__device__ __forceinline__ float dpp_max(float x) {
-  float inf = __builtin_inff();
-  asm("" : "+s"(inf));
-  return __builtin_amdgcn_fmed3f(x, dpp<CTRL>(x), inf);
-}
-
 __device__ __forceinline__ float row_max16(float x) {
   x = fmaxf(x, dpp<0xB1>(x));
   x = fmaxf(x, dpp<0x4E>(x));

@@ -201,11 +201,12 @@ def test_growing_far_scores_running_rule(built, tau, split_k):
     assert band < 3
 
 
-@pytest.mark.parametrize("qmul", [2.0 ** -12, 700.0, 2.0 ** 12])
+@pytest.mark.parametrize("qmul", [0.0, 2.0 ** -12, 700.0, 2.0 ** 12])
 def test_int2_query_magnitudes(built, qmul):
     """The INT2 far loop carries the query as exact fp16 pairs under a power-of-two row scale that puts its
     largest element in [512, 1024): queries 2^-12, 700 and 2^12 times as large (700: a scale that is no power of
-    two, rounded to bf16 on both sides) give every row within 2e-2 of the oracle, lse within 2e-2 of |lse| / 64."""
+    two, rounded to bf16 on both sides) give every row within 2e-2 of the oracle, lse within 2e-2 of |lse| / 64;
+    an all-zero query (no scale to take: every score 0, the mean of the row's values) the same."""
     o, lse, _, _ = _attend(built, 0, 0, traced=False, qmul=qmul, v_thresh_offset=1.0)
     for b, L in enumerate(LENGTHS):
         for h in range(H):

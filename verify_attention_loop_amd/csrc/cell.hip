@@ -541,8 +541,8 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
     // 2^23 below the largest fall to fp16 subnormals, where their products are under the fp32
     // rounding of the score.  One v_dot2 of the pair with the page's (sigma_c, z_c) metadata
     // adds both q_c z_c and the code offset's share to a page's bias, and the scores, 2^s too
-    // large, come back through the scale.  (INT4 cells keep the query as 4 bf16 pair
-    // registers: their loops have no room for 8.)
+    // large, come back through the scale.  (INT4 cells keep the bf16 query: their loops hold
+    // 96 VGPRs, and with the pairs they spilled.)
     uint32_t qp[E] = {};
     float scale2 = p.scale_log2;
     if constexpr (BITS == 2) {
@@ -603,10 +603,11 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
       const Raw<32>& km = kr.km;
       const Raw<16>& k0 = kr.k0;
       const Raw<16>& k1 = kr.k1;
-      // q' = q sigma (2^s too large): fp16 x fp16, exact in fp32, as one v_fma_mix_f32 with a
-      // zero addend; the codes reach the scores as fp16 pairs (off + c) through v_fma_mix_f32
-      // (the fp16 operand converts exactly), and the bias q . z - sum_c off_c q'_c takes one
-      // v_dot2 of the channel's query pair with its (sigma, z) metadata
+      // q' = q sigma as one v_fma_mix_f32 with a zero addend (exact in fp32); the codes reach
+      // the scores as fp16 pairs (off + c) through v_fma_mix_f32 (the fp16 operand converts
+      // exactly), and sum_c off_c q'_c comes off the bias q . z.  INT2: q' from the query
+      // pair's fp16 q_c 2^s (2^s too large), and the bias takes one v_dot2 of the pair with
+      // the channel's (sigma, z) metadata.
       float qs[E], bias = 0.f;
       if constexpr (BITS == 2) {
 #pragma unroll
@@ -616,7 +617,7 @@ __global__ __launch_bounds__(WAVES * 64, TRACE ? 1 : 5) void cell_kernel(const C
                                         bias, false);
         }
       } else {
-        // (INT4: q_c from the bf16 pairs per page; bf16 x fp16 is exact in fp32 too)
+        // INT4: q_c from the bf16 query, one fma per channel for q_c z_c and one for the offset
 #pragma unroll
         for (int c = 0; c < E; ++c) {
           const float qc = (c & 1) ? bf_hi(qw[c >> 1]) : bf_lo(qw[c >> 1]);
